@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle against closed forms, exact arithmetic, brute force and the
+figures of ExactMoE's Table 1 -- none of them re-types the oracle's own formula."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from oracle import layout as L
+from oracle.quant import bf16_bits_to_f64, f64_to_bf16_bits, quantize_group128
+from synthetic import SyntheticLayer, TINY, LayerShape, f32_to_bf16_bits, bf16_bits_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def _frac_to_bf16_bits(v: Fraction) -> int:
+    """Exact rational -> bf16 bits, round to nearest even, by integer arithmetic."""
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    qe = max(e - 7, -133)
+    m = a / Fraction(2) ** qe            # want round-half-even(m)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = Fraction(fl) * Fraction(2) ** qe
+    bits = int(np.array(float(val), dtype=np.float32).view(np.uint32)) >> 16
+    return sign | bits
+
+
+def test_f64_to_bf16_ties_and_no_double_rounding():
+    one = 0x3F80
+    assert f64_to_bf16_bits(np.array([1.0 + 2.0 ** -8]))[0] == one           # tie -> even
+    assert f64_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8]))[0] == one + 2   # tie -> even (up)
+    # fp32 would round 1 + 2^-8 + 2^-30 to the exact tie and then to 1.0; one rounding gives 1 + 2^-7
+    assert f64_to_bf16_bits(np.array([1.0 + 2.0 ** -8 + 2.0 ** -30]))[0] == one + 1
+    assert f64_to_bf16_bits(np.array([-2.5]))[0] == 0xC020
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000)
+    got = f64_to_bf16_bits(v)
+    exp = [_frac_to_bf16_bits(Fraction(float(x))) for x in v]
+    assert np.array_equal(got, np.array(exp, dtype=np.uint16))
+
+
+# ---------------------------------------------------------------- quantization
+def _weights(seed, n=48, k=512, sigma=0.02):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * sigma).astype(np.float32)
+    w[3, 128:256] *= 50.0            # a group with a large absmax
+    w[5, 0:128] = 0.0                # an all-zero group
+    w[7, 256:384] = 1e-30            # tiny constant group (bf16 subnormal-free scale range)
+    return w
+
+
+def test_quant_hand_worked_group():
+    # absmax 0.7 -> fp32 0.7/7 = 0x3DCCCCCD -> bf16 0x3DCD = 0.10009765625
+    w = np.zeros((1, 128), np.float32)
+    w[0, :4] = [0.7, -0.35, 0.1, -0.05]
+    q, s = quantize_group128(w)
+    assert s[0, 0] == 0x3DCD
+    assert list(q[0, :4]) == [7, -3, 1, 0]          # 6.993 -> 7; -3.4966 -> -3; 0.999 -> 1; -0.4995 -> -0
+    assert not q[0, 4:].any()
+
+
+def test_quant_roundtrip_bound_and_range():
+    w = _weights(0)
+    q, s = quantize_group128(w)
+    sv = np.repeat(bf16_bits_to_f64(s), 128, axis=1)
+    deq = q.astype(np.float64) * sv
+    assert q.min() >= -7 and q.max() <= 7               # -8 is never needed with absmax/7
+    assert np.all(np.abs(w.astype(np.float64) - deq) <= sv / 2)
+
+
+def test_quant_matches_bruteforce_argmin():
+    w = _weights(1, n=16, k=256)
+    q, s = quantize_group128(w)
+    sv = np.repeat(bf16_bits_to_f64(s), 128, axis=1)
+    for n in range(w.shape[0]):
+        for kk in range(w.shape[1]):
+            sc = sv[n, kk]
+            if sc == 0.0:
+                assert q[n, kk] == 0
+                continue
+            best, bestd = None, None
+            for cand in range(-8, 8):
+                d = abs(float(w[n, kk]) - cand * sc)
+                if bestd is None or d < bestd or (d == bestd and cand % 2 == 0):
+                    best, bestd = cand, d
+            assert q[n, kk] == best, (n, kk)
+
+
+def test_quant_scale_is_bf16_of_absmax_over_7():
+    w = _weights(2)
+    q, s = quantize_group128(w)
+    absmax = np.abs(w.astype(np.float64)).reshape(w.shape[0], -1, 128).max(axis=2)
+    sv = bf16_bits_to_f64(s)
+    # bf16 keeps 8 significant bits: relative error of one rounding <= 2^-8 (plus fp32's 2^-24)
+    nz = absmax > 0
+    assert np.all(np.abs(sv[nz] - absmax[nz] / 7) <= (2.0 ** -8 + 2.0 ** -23) * absmax[nz] / 7)
+    assert np.all(sv[~nz] == 0)
+    # the absmax element of each group gets code +-7
+    g = np.abs(w).reshape(w.shape[0], -1, 128).argmax(axis=2)
+    qq = q.reshape(w.shape[0], -1, 128)
+    for n in range(w.shape[0]):
+        for gi in range(g.shape[1]):
+            if nz[n, gi]:
+                assert abs(int(qq[n, gi, g[n, gi]])) == 7
+
+
+def test_quant_idempotent_and_zero_group():
+    w = _weights(3)
+    q, s = quantize_group128(w)
+    deq = (q.astype(np.float64) * np.repeat(bf16_bits_to_f64(s), 128, axis=1)).astype(np.float32)
+    q2, s2 = quantize_group128(deq)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert s[5, 0] == 0 and not q[5, :128].any()
+
+
+# ---------------------------------------------------------------- packed layout
+def test_packed_size_formula():
+    for H, I in [(256, 256), (2048, 1024), (4096, 14336), (128, 384)]:
+        assert L.packed_expert_bytes(H, I) == 3 * H * I // 2 + 3 * H * I // 64
+    assert L.packed_expert_bytes(2048, 1024) == 3_244_032
+    assert L.packed_expert_bytes(256, 256) == 101_376
+    assert L.packed_expert_bytes(4096, 14336) == 90_832_896
+
+
+def test_packed_size_matches_table1_transfer_volume():
+    """Table 1: H2D GiB per 128-token request / implied misses ~= one packed OLMoE expert.
+    int4 without scales, or with fp32 scales, would be >= 3% off."""
+    with open(os.path.join(GOLDEN, "table1_slot_cache.json")) as f:
+        t1 = json.load(f)
+    size = L.packed_expert_bytes(2048, 1024)
+    for row in t1["rows"]:
+        if row["hit_rate_pct"] is None:
+            assert row["h2d_gib"] == 0.0          # fully resident: no transfers
+            continue
+        for steps in (127, 128):
+            misses = (1 - row["hit_rate_pct"] / 100) * steps * 16 * 8
+            per_miss = row["h2d_gib"] * 2 ** 30 / misses
+            assert abs(per_miss / size - 1) < 0.012, (row, steps, per_miss)
+    assert abs((3 * 2048 * 1024 // 2) / (30.04 * 2 ** 30 / ((1 - 0.388) * 127 * 128)) - 1) > 0.025
+
+
+def test_pack_hand_worked_nibble():
+    H = I = 128
+    qg = np.zeros((I, H), np.int8); qu = np.zeros((I, H), np.int8); qd = np.zeros((H, I), np.int8)
+    sg = np.zeros((I, 1), np.uint16); su = np.zeros((I, 1), np.uint16); sd = np.zeros((H, 1), np.uint16)
+    qu[17, 45] = 7
+    su[17, 0] = 0x1234
+    blob = L.pack_expert(qg, sg, qu, su, qd, sd, H, I)
+    # row 17 -> block 1, tile row 1; up -> tile 2*1+1 = 3; input 45 -> word 1, lane 16+1, j = 5
+    # j = 5 sits at bits 16 + 4*2 = 24.  All other nibbles hold u = 8.
+    off = 1024 * 3 + 16 * 17 + 4 * 1
+    assert int.from_bytes(blob[off:off + 4], "little") == 0x8F888888
+    assert blob[:off].count(b"\x88") == off and set(blob[off + 4:1024 * 24]) == {0x88}
+    n_tiles = 24
+    so = 1024 * n_tiles + 32 * 3 + 2 * 1
+    assert int.from_bytes(blob[so:so + 2], "little") == 0x1234
+
+
+def test_pack_fast_equals_loop_and_roundtrip():
+    rng = np.random.default_rng(7)
+    H, I = 256, 384
+    qg = rng.integers(-8, 8, (I, H)).astype(np.int8); qu = rng.integers(-8, 8, (I, H)).astype(np.int8)
+    qd = rng.integers(-8, 8, (H, I)).astype(np.int8)
+    sg = rng.integers(0, 65535, (I, H // 128)).astype(np.uint16); su = rng.integers(0, 65535, (I, H // 128)).astype(np.uint16)
+    sd = rng.integers(0, 65535, (H, I // 128)).astype(np.uint16)
+    a = L.pack_expert(qg, sg, qu, su, qd, sd, H, I, fast=True)
+    b = L.pack_expert(qg, sg, qu, su, qd, sd, H, I, fast=False)
+    assert a == b and len(a) == L.packed_expert_bytes(H, I)
+    out = L.unpack_expert(a, H, I)
+    for x, y in zip(out, (qg, sg, qu, su, qd, sd)):
+        assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- router
+def test_logits_equal_exact_rational_sum_tiny_layer():
+    lay = SyntheticLayer(TINY, seed=0)
+    x = lay.x(16)
+    wr = lay.router()
+    bias = np.linspace(-1, 1, TINY.E).astype(np.float32)
+    got = oracle.router_logits(x, wr, bias)
+    xf = bf16_bits_to_f32(x); wf = bf16_bits_to_f32(wr)
+    for t in range(16):
+        for e in range(TINY.E):
+            acc = Fraction(float(bias[e]))
+            for h in range(TINY.H):
+                acc += Fraction(float(xf[t, h])) * Fraction(float(wf[e, h]))
+            assert got[t, e] == _frac_to_bf16_bits(acc), (t, e)
+
+
+def test_topk_equals_full_stable_sort_bruteforce():
+    rng = np.random.default_rng(3)
+    logits = f32_to_bf16_bits(rng.standard_normal((200, 64)).astype(np.float32) * 0.9)
+    logits[:, 10] = logits[:, 3]          # forced ties
+    logits[0, :] = 0x8000                 # all -0
+    logits[0, 5] = 0x0000                 # one +0: ties with -0
+    for k in (1, 2, 8, 64):
+        ids = oracle.topk_ids(logits, k)
+        lf = bf16_bits_to_f32(logits)
+        for t in range(logits.shape[0]):
+            order = sorted(range(64), key=lambda e: (-float(lf[t, e]), e))
+            assert list(ids[t]) == order[:k]
+            assert len(set(ids[t])) == k
+    assert list(oracle.topk_ids(logits, 3)[0]) == [0, 1, 2]
+
+
+def test_weights_closed_forms():
+    rng = np.random.default_rng(4)
+    logits = f32_to_bf16_bits(rng.standard_normal((50, 16)).astype(np.float32))
+    lf = bf16_bits_to_f32(logits).astype(np.float64)
+    full = scipy.special.softmax(lf, axis=1)
+    for k in (1, 4, 16):
+        ids = oracle.topk_ids(logits, k)
+        w = oracle.topk_weights(logits, ids, renormalize=True).astype(np.float64)
+        p = np.take_along_axis(full, ids.astype(np.int64), axis=1)
+        assert np.allclose(w, p / p.sum(axis=1, keepdims=True), rtol=1e-6, atol=1e-7)
+        assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+        wr = oracle.topk_weights(logits, ids, renormalize=False).astype(np.float64)
+        assert np.allclose(wr, p, rtol=1e-6, atol=1e-8)
+    ids = oracle.topk_ids(logits, 16)
+    w = oracle.topk_weights(logits, ids)
+    assert np.allclose(np.take_along_axis(full, ids.astype(np.int64), axis=1), w, rtol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)     # slots ordered by logit
+
+
+# ---------------------------------------------------------------- grouping
+def test_group_is_stable_bucket_permutation():
+    rng = np.random.default_rng(8)
+    E, T, k = 16, 37, 3
+    ids = np.stack([rng.choice(np.arange(1, E, 2), k, replace=False) for _ in range(T)]).astype(np.int32)
+    off, sf, fs = oracle.group_tokens(ids, E)
+    buckets = [[] for _ in range(E)]
+    for f, e in enumerate(ids.reshape(-1)):
+        buckets[e].append(f)
+    assert off[0] == 0 and off[-1] == T * k
+    for e in range(E):
+        assert list(sf[off[e]:off[e + 1]]) == buckets[e]
+        if e % 2 == 0:
+            assert off[e] == off[e + 1]          # never-selected experts get empty segments
+    assert sorted(sf) == list(range(T * k))
+    assert np.array_equal(sf[fs], np.arange(T * k)) and np.array_equal(fs[sf], np.arange(T * k))
+
+
+# ---------------------------------------------------------------- expert MLP + combine
+def _tiny_layer(H=128, I=128, E=3, T=3, k=2, seed=11):
+    shape = LayerShape(H=H, I=I, E=E, k=k)
+    lay = SyntheticLayer(shape, seed=seed)
+    experts = [oracle.quantize_expert(*lay.expert(e)) for e in range(E)]
+    x = lay.x(T)
+    wr = lay.router()
+    return shape, lay, experts, x, wr
+
+
+def test_mlp_bruteforce_python_loops():
+    shape, lay, experts, x, wr = _tiny_layer()
+    res = oracle.moe_layer(x, wr, experts, shape.k)
+    xf = bf16_bits_to_f32(x)
+    for t in range(x.shape[0]):
+        y = [0.0] * shape.H
+        for j in range(shape.k):
+            e = int(res["ids"][t, j])
+            qe = experts[e]
+            sg = bf16_bits_to_f32(qe.sg); su = bf16_bits_to_f32(qe.su); sd = bf16_bits_to_f32(qe.sd)
+            a = []
+            for n in range(shape.I):
+                gn = sum(float(xf[t, kk]) * int(qe.qg[n, kk]) * float(sg[n, kk // 128]) for kk in range(shape.H))
+                un = sum(float(xf[t, kk]) * int(qe.qu[n, kk]) * float(su[n, kk // 128]) for kk in range(shape.H))
+                a.append(gn / (1 + math.exp(-gn)) * un)
+            wj = float(res["weights"][t, j])
+            for m in range(shape.H):
+                om = sum(a[n] * int(qe.qd[m, n]) * float(sd[m, n // 128]) for n in range(shape.I))
+                y[m] += wj * om
+        assert np.allclose(res["y"][t], y, rtol=1e-9, atol=1e-12)
+
+
+def test_grouped_equals_per_token():
+    shape, lay, experts, x, wr = _tiny_layer(H=256, I=256, E=8, T=16, k=2, seed=0)
+    res = oracle.moe_layer(x, wr, experts, shape.k)
+    xf = bf16_bits_to_f64(x)
+    yg = oracle.forward_grouped(xf, res["ids"], res["weights"], experts, res["offsets"], res["sorted_flat"], rowwise=True)
+    assert np.array_equal(yg, res["y"])                  # identical per-row arithmetic: bit-exact
+    yb = oracle.forward_grouped(xf, res["ids"], res["weights"], experts, res["offsets"], res["sorted_flat"])
+    assert np.allclose(yb, res["y"], rtol=1e-12, atol=1e-15)
+
+
+def test_mlp_special_cases():
+    shape, lay, experts, x, wr = _tiny_layer(E=4, T=5, k=2)
+    res = oracle.moe_layer(x, wr, experts, shape.k)
+    # x = 0 -> y = 0
+    z = oracle.moe_layer(np.zeros_like(x), wr, experts, shape.k)
+    assert not np.any(z["y"])
+    # W_down = 0 -> y = 0
+    import copy
+    ex0 = [copy.copy(e) for e in experts]
+    for e in ex0:
+        e.qd = np.zeros_like(e.qd); e._deq = {}
+    assert not np.any(oracle.moe_layer(x, wr, ex0, shape.k)["y"])
+    # doubling every down scale (exact in bf16) doubles y exactly
+    ex2 = [copy.copy(e) for e in experts]
+    for e in ex2:
+        e.sd = (e.sd.astype(np.uint32) + (1 << 7)).astype(np.uint16); e._deq = {}    # exponent + 1
+    assert np.array_equal(oracle.moe_layer(x, wr, ex2, shape.k)["y"], 2 * res["y"])
+    # relabelling experts consistently (router rows and expert list) leaves y unchanged
+    perm = np.array([2, 0, 3, 1])
+    exp_perm = [experts[perm[i]] for i in range(4)]
+    wr_perm = wr[perm]
+    r2 = oracle.moe_layer(x, wr_perm, exp_perm, shape.k)
+    assert np.allclose(r2["y"], res["y"], rtol=1e-14, atol=1e-16)
+    # k = 1 with weight 1: y equals the single routed expert's MLP
+    r1 = oracle.moe_layer(x, wr, experts, 1)
+    assert np.allclose(r1["weights"], 1.0)
+    for t in range(x.shape[0]):
+        o = oracle.expert_mlp(experts[int(r1["ids"][t, 0])], bf16_bits_to_f64(x[t:t + 1]))[0]
+        assert np.array_equal(r1["y"][t], o)
+
+
+def test_knockout_every_routed_expert_runs():
+    shape, lay, experts, x, wr = _tiny_layer(E=4, T=12, k=2, seed=5)
+    res = oracle.moe_layer(x, wr, experts, shape.k)
+    other = SyntheticLayer(shape, seed=99)
+    for e in range(4):
+        ex = list(experts)
+        ex[e] = oracle.quantize_expert(*other.expert(e))
+        y2 = oracle.moe_layer(x, wr, ex, shape.k)["y"]
+        changed = np.nonzero(np.any(y2 != res["y"], axis=1))[0]
+        assert np.array_equal(changed, oracle.knockout_rows(res["ids"], e))
+
+
+# ---------------------------------------------------------------- LRU slot cache
+def _lru_reference(trace, E, S, nbytes):
+    """Independent formulation: a recency list per layer, free slots taken lowest first."""
+    layers = trace.shape[1]
+    rec = [[] for _ in range(layers)]       # least recent first
+    slots = [dict() for _ in range(layers)]
+    c = dict(lookups=0, hits=0, misses=0, evictions=0, bytes=0)
+    for step in trace:
+        for l in range(layers):
+            A = sorted(set(int(e) for e in step[l]))
+            for e in A:
+                c["lookups"] += 1
+                if e in rec[l]:
+                    c["hits"] += 1
+                    rec[l].remove(e)
+                else:
+                    c["misses"] += 1; c["bytes"] += nbytes
+                    used = set(slots[l].values())
+                    if len(rec[l]) < S:
+                        slots[l][e] = min(set(range(S)) - used)
+                    else:
+                        victim = next(x for x in rec[l] if x not in A)
+                        rec[l].remove(victim)
+                        slots[l][e] = slots[l].pop(victim)
+                        c["evictions"] += 1
+                rec[l].append(e)
+    return c, slots
+
+
+def test_lru_matches_independent_reference():
+    from synthetic import slot_cache_trace
+    for S in (1, 2, 3, 5, 8):
+        k = min(S, 3)
+        trace = slot_cache_trace(E=8, k=k, layers=2, steps=60, seed=S)
+        sim = oracle.LRUSlotCacheSim(layers=2, E=8, slots=S, expert_bytes=10) if S < 8 else None
+        if sim is None:
+            continue
+        for step in trace:
+            for l in range(2):
+                table = sim.acquire(l, step[l])
+        ref, slots = _lru_reference(trace, 8, S, 10)
+        assert (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes) == \
+            (ref["lookups"], ref["hits"], ref["misses"], ref["evictions"], ref["bytes"])
+        for l in range(2):
+            assert sim.slot_of[l] == slots[l]
+
+
+def test_lru_closed_forms():
+    # enough slots: only compulsory misses
+    tr = np.array([[[0, 1]], [[1, 2]], [[0, 2]], [[3, 1]]], dtype=np.int32)
+    sim = oracle.LRUSlotCacheSim(layers=1, E=6, slots=4, expert_bytes=7)
+    for st in tr:
+        sim.acquire(0, st[0])
+    assert sim.misses == 4 and sim.evictions == 0 and sim.h2d_bytes == 28 and sim.lookups == 8
+    # one slot, k = 1: a miss on every change of expert
+    seq = [0, 0, 1, 1, 1, 0, 2, 2, 0]
+    sim = oracle.LRUSlotCacheSim(layers=1, E=3, slots=1, expert_bytes=1)
+    for e in seq:
+        sim.acquire(0, [e])
+    assert sim.misses == 1 + sum(a != b for a, b in zip(seq, seq[1:]))
+    # resident: counters bypassed
+    sim = oracle.LRUSlotCacheSim(layers=1, E=3, slots=3, expert_bytes=1)
+    assert list(sim.acquire(0, [2, 0])) == [0, 1, 2] and sim.lookups == 0
+    with pytest.raises(ValueError):
+        oracle.LRUSlotCacheSim(layers=1, E=4, slots=2, expert_bytes=1).acquire(0, [0, 1, 2])
