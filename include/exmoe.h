@@ -1,0 +1,235 @@
+/*
+ * exmoe.h -- C ABI of libexmoe, a fused grouped W4A16 mixture-of-experts expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes follows "Every Expert Counts: ExactMoE for Memory-Efficient
+ * W4A16 Inference": routed experts carry symmetric group-128 int4 weights packed once
+ * into a kernel-native form (abstract; Fig. 1 caption), the BF16 router and its top-k
+ * procedure are unchanged (abstract; Fig. 1), tokens are grouped by selected expert and
+ * every selected expert runs (Fig. 1), and packed experts live in a pinned host pool
+ * behind a configurable GPU slot cache (abstract; Fig. 1; Tab. 1).
+ *
+ * Conventions shared by every entry point
+ *  - Return value: EXMOE_OK (0) or a negative exmoe_status. exmoe_last_error() returns a
+ *    thread-local message for the last failing call on the calling thread. Nothing throws
+ *    or aborts across this boundary.
+ *  - Validation happens before anything is enqueued: on an error no work is launched and
+ *    outputs are untouched. Faults of already-enqueued device work surface as
+ *    EXMOE_ERR_HIP on a later synchronizing call.
+ *  - Ownership: the caller owns every buffer passed in. The library owns only slot-cache
+ *    handles (pinned pool, device slots, copy stream, events).
+ *  - Device calls are asynchronous on the caller's stream unless stated otherwise.
+ *  - bf16 values travel as raw uint16_t bit patterns; indices are int32; routing weights
+ *    are fp32. Device buffers must be 16-byte aligned.
+ *  - Shapes: H % 128 == 0, I % 128 == 0, group size 128, 1 <= k <= E <= 256. T == 0 is a
+ *    valid no-op.
+ *  - Integer outputs are deterministic; y is bitwise reproducible for fixed inputs and
+ *    path (no floating-point atomics).
+ */
+#ifndef EXMOE_H
+#define EXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXMOE_ABI_VERSION 1
+
+typedef uint16_t exmoe_bf16;
+
+typedef enum exmoe_status {
+  EXMOE_OK = 0,
+  EXMOE_ERR_INVALID_ARGUMENT = -1, /* bad pointer, shape, alignment or flag */
+  EXMOE_ERR_UNSUPPORTED = -2,      /* valid request this build does not implement */
+  EXMOE_ERR_WORKSPACE = -3,        /* workspace missing or smaller than the query says */
+  EXMOE_ERR_HIP = -4,              /* a HIP runtime call failed */
+  EXMOE_ERR_OUT_OF_MEMORY = -5,    /* a library-owned allocation failed */
+  EXMOE_ERR_CACHE = -6             /* slot-cache misuse: too many active experts, bad layer */
+} exmoe_status;
+
+const char* exmoe_status_string(int status);
+/* Thread-local message of the calling thread's last failing call ("" if none). */
+const char* exmoe_last_error(void);
+int exmoe_abi_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * Offline quantize + pack (host memory, synchronous, runs on the CPU).
+ * Abstract and Fig. 1: routed expert projections are quantized (symmetric, group 128,
+ * four bits) and packed once into the form the expert kernels consume.
+ *
+ * Quantization per output row n and input group g (inputs 128g..128g+127):
+ *   s = bf16_round_nearest_even(fp32(absmax / 7)), 0 for an all-zero group;
+ *   q = clamp(round_half_even(w / s), -8, 7) with the quotient formed in fp64; q = 0 if s = 0.
+ * Packed blob of one expert (exmoe_packed_expert_bytes(H, I) = 3HI/2 + 3HI/64 bytes):
+ *   [n_tiles x 1024 B int4 tiles][n_tiles x 32 B bf16 scales],
+ *   n_tiles = 2(I/16)(H/128) + (H/16)(I/128).
+ *   Tile order: for row block b < I/16: gate tiles g < H/128, then up tiles g < H/128;
+ *   then for row block b < H/16: down tiles g < I/128. A tile holds rows 16b..16b+15 and
+ *   inputs 128g..128g+127 of its matrix. Byte 16l+4s of a tile (lane l < 64, word s < 4)
+ *   starts a little-endian word with row 16b + l%16, inputs 128g + 32s + 8(l/16) + j
+ *   (j < 8) as nibbles u = q + 8; input j sits at bit 4(j/2) for even j and 16 + 4(j/2)
+ *   for odd j. The 16 scales of tile t (its rows in order) start at byte
+ *   1024 n_tiles + 32 t.
+ * ---------------------------------------------------------------------------------- */
+size_t exmoe_packed_expert_bytes(int H, int I);
+
+/* w_gate, w_up: fp32 [I, H] row-major; w_down: fp32 [H, I]; group_size must be 128.
+ * packed: host buffer of packed_bytes >= exmoe_packed_expert_bytes(H, I).
+ * Non-finite weights are EXMOE_ERR_INVALID_ARGUMENT. */
+int exmoe_quantize_pack(const float* w_gate, const float* w_up, const float* w_down, int H, int I,
+                        int group_size, void* packed, size_t packed_bytes);
+
+/* Inverse of the packing (not of the rounding): codes q int8 ([I,H], [I,H], [H,I]) and
+ * scales bf16 ([I,H/128], [I,H/128], [H,I/128]). Any output pointer may be NULL. */
+int exmoe_unpack_expert(const void* packed, size_t packed_bytes, int H, int I, int8_t* q_gate,
+                        int8_t* q_up, int8_t* q_down, exmoe_bf16* s_gate, exmoe_bf16* s_up,
+                        exmoe_bf16* s_down);
+
+/* ------------------------------------------------------------------------------------
+ * Routing (device, asynchronous). Abstract and Fig. 1: the original BF16 router selects
+ * the experts and the top-k procedure is unchanged.
+ *   logits[t,e] = bf16_round_nearest_even(sum_h x[t,h] * w_router[e,h] + bias[e]), the
+ *     exact bf16 products summed in fp64 (order-insensitive in practice), rounded once;
+ *   topk_ids[t, 0..k-1]: experts ordered by (logit descending, expert id ascending),
+ *     -0 and +0 equal;
+ *   topk_weights[t,j]: renormalize != 0 -> softmax over the k selected logits;
+ *     renormalize == 0 -> full-softmax probability of the selected expert (fp32 expf).
+ * x bf16 [T,H]; w_router bf16 [E,H]; logit_bias fp32 [E] or NULL; logits bf16 [T,E] or
+ * NULL (not written); topk_ids int32 [T,k]; topk_weights fp32 [T,k]. All device memory.
+ * ---------------------------------------------------------------------------------- */
+int exmoe_route_topk(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
+                     int T, int H, int E, int k, int renormalize, exmoe_bf16* logits,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* Top-k and weights from given bf16 logits [T,E] (same rules as exmoe_route_topk). */
+int exmoe_topk_from_logits(const exmoe_bf16* logits, int T, int E, int k, int renormalize,
+                           int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* Weights for externally chosen experts (a routing trace): topk_ids int32 [T,k] holds k
+ * distinct ids per token; weights follow the renormalize rule above over those ids. */
+int exmoe_route_weights(const exmoe_bf16* logits, const int32_t* topk_ids, int T, int E, int k,
+                        int renormalize, float* topk_weights, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Grouping (device, asynchronous). Fig. 1: tokens are grouped by selected expert.
+ * Flat index f = t*k + j. expert_offsets int32 [E+1] is the exclusive prefix sum of the
+ * per-expert counts (offsets[E] = T*k, unpadded); sorted_flat int32 [T*k] lists, expert by
+ * expert ascending and within an expert in ascending f, every f routed there;
+ * flat_to_sorted int32 [T*k] is its inverse. Ids outside [0, E) are a caller error: they
+ * are counted nowhere and the outputs are then unspecified (no memory is touched out of
+ * range). The workspace may be NULL when exmoe_group_workspace_bytes returns 0.
+ * ---------------------------------------------------------------------------------- */
+size_t exmoe_group_workspace_bytes(int T, int k, int E);
+int exmoe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                       int32_t* sorted_flat, int32_t* flat_to_sorted, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Reactive-cache step (synchronizes `stream`): copies offsets to the host and lists the
+ * experts with a non-empty segment in ascending order. ids_host must hold E ints. */
+int exmoe_active_experts(const int32_t* expert_offsets, int E, int32_t* ids_host, int* n_host,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Expert layer (device, asynchronous). Abstract and Fig. 1: every selected expert runs,
+ * grouped, with int4 weights dequantized on the fly (no 16-bit copy of an expert).
+ * For every routed pair (t, j) with e = topk_ids[t,j]:
+ *   g = W_gate x_t, u = W_up x_t, a = silu(g) * u (stored as bf16), o = W_down a,
+ * with W = q*s from expert e's blob, products of bf16 operands accumulated in fp32; then
+ *   y[t] = bf16(sum_{j=0..k-1} w[t,j] * o_{t,j}) summed in that slot order.
+ * The expert MLP form (SwiGLU) is not on the pages; it is this layer's stated workload.
+ *
+ * bank: expert e's blob is at base + stride * slot(e), slot(e) = expert_to_slot[e] when
+ * expert_to_slot (device int32 [E]) is given, else e. Every routed expert must map to a
+ * valid slot (a -1 slot for a routed expert is a caller error; the kernels then skip it
+ * and count it in the debug word). x bf16 [T,H]; y bf16 [T,H]; routing buffers as
+ * produced by exmoe_route_topk / exmoe_group_tokens for the same T, k, E.
+ * ---------------------------------------------------------------------------------- */
+typedef struct exmoe_expert_bank {
+  const void* base;
+  size_t stride;                 /* bytes between slots, >= packed expert bytes, % 16 == 0 */
+  const int32_t* expert_to_slot; /* device int32 [E] or NULL for identity */
+} exmoe_expert_bank;
+
+enum {
+  EXMOE_PATH_AUTO = 0,       /* choose by rows per active expert */
+  EXMOE_PATH_DECODE = 1,     /* split-K GEMV-style kernels, 16-token MFMA tiles */
+  EXMOE_PATH_PREFILL = 2,    /* grouped GEMM kernels, large token tiles */
+  EXMOE_PATH_SEQUENTIAL = 3, /* per-expert launches in ascending expert order (reference
+                                W4 path; synchronizes once to read the offsets) */
+  EXMOE_PATH_MASK = 0xff
+};
+
+size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, int flags);
+
+int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
+                      const int32_t* expert_offsets, const int32_t* sorted_flat,
+                      const int32_t* flat_to_sorted, const exmoe_expert_bank* bank, int T, int H,
+                      int I, int E, int k, int flags, exmoe_bf16* y, void* workspace,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer in one call: route (exmoe_route_topk), group (exmoe_group_tokens) and the
+ * expert layer (exmoe_moe_forward), with the routing results written to caller buffers
+ * (logits may be NULL). Same arguments and rules as those three calls. */
+size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags);
+int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
+                    const exmoe_expert_bank* bank, int T, int H, int I, int E, int k,
+                    int renormalize, int flags, exmoe_bf16* logits, int32_t* topk_ids,
+                    float* topk_weights, int32_t* expert_offsets, int32_t* sorted_flat,
+                    int32_t* flat_to_sorted, exmoe_bf16* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Slot cache (host policy + asynchronous host-to-device copies). Abstract, Fig. 1, Fig. 2
+ * and Tab. 1: a pinned host pool keeps every packed expert; a GPU cache of a configurable
+ * number of slots per layer holds the ones in use; misses copy packed weights and scales.
+ * Policy (the pages name none): least-recently-used per layer. A layer-step looks up its
+ * distinct active experts in ascending id; a hit refreshes the expert's stamp; a miss
+ * takes the lowest free slot, else evicts the resident expert with the oldest stamp that
+ * is not in the current active set, and copies the blob on the cache's copy stream.
+ * slots_per_layer == E is full residency: exmoe_slot_cache_preload copies everything and
+ * lookups are bypassed (counters stay 0, stats.resident = 1).
+ * ---------------------------------------------------------------------------------- */
+typedef struct exmoe_slot_cache exmoe_slot_cache;
+
+typedef struct exmoe_cache_stats {
+  uint64_t lookups, hits, misses, evictions;
+  uint64_t h2d_bytes, h2d_copies;
+  uint64_t device_bytes;       /* device slot memory held */
+  uint64_t pinned_host_bytes;  /* pinned pool held */
+  int resident;                /* 1 when slots_per_layer == E */
+} exmoe_cache_stats;
+
+enum { EXMOE_CACHE_DRY_RUN = 1 }; /* policy and counters only: no allocation, no copies */
+
+/* Allocates the pinned pool (layers*E*expert_stride bytes), the device slots
+ * (layers*slots*expert_stride), a copy stream and the device expert->slot tables;
+ * synchronous. expert_bytes is the packed size; the stride rounds it up to 256 B. */
+int exmoe_slot_cache_create(int layers, int E, int slots_per_layer, size_t expert_bytes, int flags,
+                            exmoe_slot_cache** out);
+/* Host pointer of (layer, expert)'s pinned blob, for the caller to fill once (e.g. with
+ * exmoe_quantize_pack). Not available in dry-run mode. */
+int exmoe_slot_cache_host_slot(exmoe_slot_cache* cache, int layer, int expert, void** pinned_ptr);
+/* Full residency only: copies every blob to its slot and waits. */
+int exmoe_slot_cache_preload(exmoe_slot_cache* cache, hipStream_t stream);
+/* One layer-step: looks up the active experts (host ids, any order, duplicates ignored),
+ * enqueues the copies for the misses on the copy stream, uploads the layer's
+ * expert->slot table, and makes compute_stream wait for both; bank_out then describes the
+ * layer's slots. More distinct active experts than slots -> EXMOE_ERR_CACHE, state kept.
+ * In dry-run mode only the policy and counters run and bank_out is zeroed. */
+int exmoe_slot_cache_acquire(exmoe_slot_cache* cache, int layer, const int32_t* active_ids_host,
+                             int n_active, hipStream_t compute_stream, exmoe_expert_bank* bank_out);
+/* Host copy of the layer's expert->slot table (-1 = not resident), int32 [E]. */
+int exmoe_slot_cache_table(const exmoe_slot_cache* cache, int layer, int32_t* table_host);
+int exmoe_slot_cache_stats(const exmoe_slot_cache* cache, exmoe_cache_stats* out);
+int exmoe_slot_cache_reset_stats(exmoe_slot_cache* cache);
+/* Waits for outstanding copies, frees everything. NULL is a no-op. */
+int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EXMOE_H */

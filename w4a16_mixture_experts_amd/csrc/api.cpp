@@ -1,0 +1,481 @@
+// libexmoe C ABI: argument validation, error reporting, the offline int4 packer, workspace
+// layout and kernel dispatch. Every device entry point validates everything before it
+// enqueues anything.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+#include "exmoe.h"
+
+namespace exmoe {
+
+static thread_local char g_last_error[512] = "";
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(e == hipErrorOutOfMemory ? EXMOE_ERR_OUT_OF_MEMORY : EXMOE_ERR_HIP, "%s: %s", what,
+                   hipGetErrorString(e));
+}
+
+static int check_shape(int T, int H, int I, int E, int k) {
+  if (T < 0) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %d)", T);
+  if (H <= 0 || H % kGroup) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (got %d)", H);
+  if (I <= 0 || I % kGroup) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "I must be a positive multiple of 128 (got %d)", I);
+  if (E < 1 || E > kMaxExperts) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "E must be in [1, 256] (got %d)", E);
+  if (k < 1 || k > E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "k must be in [1, E] (got k=%d, E=%d)", k, E);
+  if (k > 64) return set_error(EXMOE_ERR_UNSUPPORTED, "k > 64 is not supported (got %d)", k);
+  if ((long long)T * k > (1LL << 30)) return set_error(EXMOE_ERR_UNSUPPORTED, "T*k too large");
+  return EXMOE_OK;
+}
+
+#define CHECK_PTR(p)                                                                           \
+  do {                                                                                         \
+    if (!(p)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", #p);          \
+    if (!aligned16(p)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", #p); \
+  } while (0)
+
+#define CHECK_PTR4(p)                                                                          \
+  do {                                                                                         \
+    if (!(p)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", #p);          \
+    if (((uintptr_t)(p)) & 3u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "%s must be 4-byte aligned", #p); \
+  } while (0)
+
+// ------------------------------------------------------------------------------------
+// Offline quantize + pack (host)
+// ------------------------------------------------------------------------------------
+static inline uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+static inline float host_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// One tile: rows 16b.., inputs 128g.. of a row-major [N, K] matrix.
+static void pack_tile(const float* W, int K, int b, int g, uint8_t* tile_out, uint8_t* scale_out) {
+  int8_t q[kTileRows][kGroup];
+  for (int r = 0; r < kTileRows; r++) {
+    const float* row = W + (size_t)(kTileRows * b + r) * K + (size_t)kGroup * g;
+    float amax = 0.f;
+    for (int c = 0; c < kGroup; c++) amax = std::max(amax, std::fabs(row[c]));
+    const uint16_t sb = host_f32_to_bf16(amax / 7.0f);
+    const double s = (double)host_bf16_to_f32(sb);
+    for (int c = 0; c < kGroup; c++) {
+      double v = s == 0.0 ? 0.0 : std::nearbyint((double)row[c] / s);   // ties to even
+      v = std::min(7.0, std::max(-8.0, v));
+      q[r][c] = (int8_t)v;
+    }
+    scale_out[2 * r] = (uint8_t)(sb & 0xFF);
+    scale_out[2 * r + 1] = (uint8_t)(sb >> 8);
+  }
+  for (int l = 0; l < 64; l++) {
+    const int r = l % 16, kq = 8 * (l / 16);
+    for (int s = 0; s < 4; s++) {
+      uint32_t w = 0;
+      for (int j = 0; j < 8; j++) {
+        const uint32_t u = (uint32_t)(q[r][32 * s + kq + j] + 8);
+        const int sh = (j % 2 == 0) ? 4 * (j / 2) : 16 + 4 * (j / 2);
+        w |= u << sh;
+      }
+      uint8_t* p = tile_out + 16 * l + 4 * s;
+      p[0] = (uint8_t)w;
+      p[1] = (uint8_t)(w >> 8);
+      p[2] = (uint8_t)(w >> 16);
+      p[3] = (uint8_t)(w >> 24);
+    }
+  }
+}
+
+static bool all_finite(const float* p, size_t n) {
+  for (size_t i = 0; i < n; i++)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+}  // namespace exmoe
+
+using namespace exmoe;
+
+extern "C" {
+
+const char* exmoe_status_string(int status) {
+  switch (status) {
+    case EXMOE_OK: return "ok";
+    case EXMOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case EXMOE_ERR_UNSUPPORTED: return "unsupported";
+    case EXMOE_ERR_WORKSPACE: return "workspace too small";
+    case EXMOE_ERR_HIP: return "HIP runtime error";
+    case EXMOE_ERR_OUT_OF_MEMORY: return "out of memory";
+    case EXMOE_ERR_CACHE: return "slot cache error";
+    default: return "unknown status";
+  }
+}
+
+const char* exmoe_last_error(void) { return g_last_error; }
+int exmoe_abi_version(void) { return EXMOE_ABI_VERSION; }
+
+size_t exmoe_packed_expert_bytes(int H, int I) {
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return 0;
+  return packed_bytes(H, I);
+}
+
+int exmoe_quantize_pack(const float* w_gate, const float* w_up, const float* w_down, int H, int I,
+                        int group_size, void* packed, size_t packed_bytes_given) {
+  if (!w_gate || !w_up || !w_down || !packed)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "weights and packed buffer must not be NULL");
+  if (group_size != kGroup) return set_error(EXMOE_ERR_UNSUPPORTED, "group_size must be 128 (got %d)", group_size);
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "H and I must be positive multiples of 128");
+  const size_t need = packed_bytes(H, I);
+  if (packed_bytes_given < need)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "packed buffer too small: %zu < %zu", packed_bytes_given, need);
+  const size_t nw = (size_t)H * I;
+  if (!all_finite(w_gate, nw) || !all_finite(w_up, nw) || !all_finite(w_down, nw))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "weights must be finite");
+  const int G = H / kGroup, GD = I / kGroup;
+  const size_t n_gu = 2 * (size_t)(I / kTileRows) * G;
+  const size_t nt = n_tiles(H, I);
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  uint8_t* scales = out + nt * kTileBytes;
+  auto work = [&](size_t t0, size_t t1) {
+    for (size_t t = t0; t < t1; t++) {
+      if (t < n_gu) {
+        const int b = (int)(t / (2 * G)), rem = (int)(t % (2 * G));
+        const float* W = rem < G ? w_gate : w_up;
+        pack_tile(W, H, b, rem % G, out + t * kTileBytes, scales + t * kScaleBytes);
+      } else {
+        const size_t u = t - n_gu;
+        pack_tile(w_down, I, (int)(u / GD), (int)(u % GD), out + t * kTileBytes, scales + t * kScaleBytes);
+      }
+    }
+  };
+  unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (nt < 256) nth = 1;
+  std::vector<std::thread> pool;
+  const size_t chunk = (nt + nth - 1) / nth;
+  for (unsigned i = 0; i < nth; i++) {
+    const size_t a = i * chunk, b = std::min(nt, a + chunk);
+    if (a < b) pool.emplace_back(work, a, b);
+  }
+  for (auto& th : pool) th.join();
+  return EXMOE_OK;
+}
+
+int exmoe_unpack_expert(const void* packed, size_t packed_bytes_given, int H, int I, int8_t* q_gate,
+                        int8_t* q_up, int8_t* q_down, exmoe_bf16* s_gate, exmoe_bf16* s_up,
+                        exmoe_bf16* s_down) {
+  if (!packed) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "packed must not be NULL");
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "H and I must be positive multiples of 128");
+  if (packed_bytes_given < packed_bytes(H, I))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "packed buffer too small");
+  const uint8_t* in = static_cast<const uint8_t*>(packed);
+  const int G = H / kGroup, GD = I / kGroup;
+  const size_t n_gu = 2 * (size_t)(I / kTileRows) * G;
+  const size_t nt = n_tiles(H, I);
+  const uint8_t* scales = in + nt * kTileBytes;
+  for (size_t t = 0; t < nt; t++) {
+    int8_t* Q;
+    exmoe_bf16* S;
+    int K, b, g, SG;
+    if (t < n_gu) {
+      b = (int)(t / (2 * G));
+      const int rem = (int)(t % (2 * G));
+      g = rem % G;
+      Q = rem < G ? q_gate : q_up;
+      S = rem < G ? s_gate : s_up;
+      K = H;
+      SG = G;
+    } else {
+      const size_t u = t - n_gu;
+      b = (int)(u / GD);
+      g = (int)(u % GD);
+      Q = q_down;
+      S = s_down;
+      K = I;
+      SG = GD;
+    }
+    const uint8_t* tp = in + t * kTileBytes;
+    for (int l = 0; l < 64; l++)
+      for (int s = 0; s < 4; s++) {
+        const uint8_t* p = tp + 16 * l + 4 * s;
+        const uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+        for (int j = 0; j < 8; j++) {
+          const int sh = (j % 2 == 0) ? 4 * (j / 2) : 16 + 4 * (j / 2);
+          const int qv = (int)((w >> sh) & 0xF) - 8;
+          const int row = kTileRows * b + l % 16, col = kGroup * g + 32 * s + 8 * (l / 16) + j;
+          if (Q) Q[(size_t)row * K + col] = (int8_t)qv;
+        }
+      }
+    if (S)
+      for (int r = 0; r < kTileRows; r++) {
+        const uint8_t* p = scales + t * kScaleBytes + 2 * r;
+        S[(size_t)(kTileRows * b + r) * SG + g] = (exmoe_bf16)(p[0] | (p[1] << 8));
+      }
+  }
+  return EXMOE_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// Routing and grouping
+// ------------------------------------------------------------------------------------
+int exmoe_route_topk(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias, int T, int H,
+                     int E, int k, int renormalize, exmoe_bf16* logits, int32_t* topk_ids,
+                     float* topk_weights, hipStream_t stream) {
+  int st = check_shape(T, H, kGroup, E, k);
+  if (st) return st;
+  if (T == 0) return EXMOE_OK;
+  CHECK_PTR(x);
+  CHECK_PTR(w_router);
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  if (logit_bias && ((uintptr_t)logit_bias & 3u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logit_bias must be 4-byte aligned");
+  if (logits && ((uintptr_t)logits & 1u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logits must be 2-byte aligned");
+  // Logits go to the caller buffer or, when none is given, to the front of the weights
+  // buffer is not possible (different sizes): require a logits buffer internally.
+  uint16_t* lg = logits;
+  void* tmp = nullptr;
+  if (!lg) {
+    EXMOE_HIP(hipMallocAsync(&tmp, (size_t)T * E * 2, stream));
+    lg = static_cast<uint16_t*>(tmp);
+  }
+  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, lg, stream));
+  EXMOE_HIP(launch_topk(lg, nullptr, T, E, k, renormalize, topk_ids, topk_weights, stream));
+  if (tmp) EXMOE_HIP(hipFreeAsync(tmp, stream));
+  return EXMOE_OK;
+}
+
+int exmoe_topk_from_logits(const exmoe_bf16* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                           float* topk_weights, hipStream_t stream) {
+  int st = check_shape(T, kGroup, kGroup, E, k);
+  if (st) return st;
+  if (T == 0) return EXMOE_OK;
+  if (!logits || ((uintptr_t)logits & 1u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logits must be non-NULL and 2-byte aligned");
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  EXMOE_HIP(launch_topk(logits, nullptr, T, E, k, renormalize, topk_ids, topk_weights, stream));
+  return EXMOE_OK;
+}
+
+int exmoe_route_weights(const exmoe_bf16* logits, const int32_t* topk_ids, int T, int E, int k, int renormalize,
+                        float* topk_weights, hipStream_t stream) {
+  int st = check_shape(T, kGroup, kGroup, E, k);
+  if (st) return st;
+  if (T == 0) return EXMOE_OK;
+  if (!logits || ((uintptr_t)logits & 1u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logits must be non-NULL and 2-byte aligned");
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  EXMOE_HIP(launch_topk(logits, topk_ids, T, E, k, renormalize, nullptr, topk_weights, stream));
+  return EXMOE_OK;
+}
+
+size_t exmoe_group_workspace_bytes(int T, int k, int E) {
+  (void)T; (void)k; (void)E;
+  return 0;
+}
+
+int exmoe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets, int32_t* sorted_flat,
+                       int32_t* flat_to_sorted, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  (void)workspace; (void)ws_bytes;
+  int st = check_shape(T, kGroup, kGroup, E, k);
+  if (st) return st;
+  CHECK_PTR4(expert_offsets);
+  if (T > 0) {
+    CHECK_PTR4(topk_ids);
+    CHECK_PTR4(sorted_flat);
+    CHECK_PTR4(flat_to_sorted);
+  }
+  EXMOE_HIP(launch_group(topk_ids, T, k, E, expert_offsets, sorted_flat, flat_to_sorted, stream));
+  return EXMOE_OK;
+}
+
+int exmoe_active_experts(const int32_t* expert_offsets, int E, int32_t* ids_host, int* n_host, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "E must be in [1, 256]");
+  CHECK_PTR4(expert_offsets);
+  if (!ids_host || !n_host) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "ids_host and n_host must not be NULL");
+  int32_t off[kMaxExperts + 1];
+  EXMOE_HIP(hipMemcpyAsync(off, expert_offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, stream));
+  EXMOE_HIP(hipStreamSynchronize(stream));
+  int n = 0;
+  for (int e = 0; e < E; e++)
+    if (off[e + 1] > off[e]) ids_host[n++] = e;
+  *n_host = n;
+  return EXMOE_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------
+// Expert layer
+// ------------------------------------------------------------------------------------
+static int choose_path(int T, int E, int k, int flags) {
+  const int p = flags & EXMOE_PATH_MASK;
+  if (p != EXMOE_PATH_AUTO) return p;
+  const long long rows = (long long)T * k;
+  const long long act = std::min<long long>(E, rows);
+  if (T <= 16 || rows < 64 * act) return EXMOE_PATH_DECODE;
+  return EXMOE_PATH_PREFILL;
+}
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+namespace exmoe {
+size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws) {
+  (void)E; (void)path;
+  const size_t rows = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_h = take(rows * I * 2);
+  const size_t o_yp = take(rows * H * 4);
+  const size_t o_gs = take(rows * (I / kGroup) * 4);
+  const size_t o_xs = take((size_t)T * (H / kGroup) * 4);
+  const size_t o_ct = take((size_t)(H / 32 + 1) * 4);
+  const size_t o_db = take(16);
+  if (a && ws) {
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    a->h = reinterpret_cast<uint16_t*>(b + o_h);
+    a->y_perm = reinterpret_cast<float*>(b + o_yp);
+    a->gsum = reinterpret_cast<float*>(b + o_gs);
+    a->xsum = reinterpret_cast<float*>(b + o_xs);
+    a->counters = reinterpret_cast<uint32_t*>(b + o_ct);
+    a->debug = reinterpret_cast<uint32_t*>(b + o_db);
+  }
+  return off;
+}
+}  // namespace exmoe
+
+extern "C" size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, int flags) {
+  if (check_shape(T, H, I, E, k)) return 0;
+  return moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+}
+
+static int validate_bank(const exmoe_expert_bank* bank, int H, int I) {
+  if (!bank) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank must not be NULL");
+  if (!bank->base || !aligned16(bank->base)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->base must be non-NULL and 16-byte aligned");
+  if (bank->stride % 16) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->stride must be a multiple of 16");
+  if (bank->stride < packed_bytes(H, I))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->stride %zu smaller than the packed expert size %zu", bank->stride, packed_bytes(H, I));
+  if (bank->expert_to_slot && ((uintptr_t)bank->expert_to_slot & 3u))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->expert_to_slot must be 4-byte aligned");
+  return EXMOE_OK;
+}
+
+static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
+                            const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
+                            const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int flags, exmoe_bf16* y,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const int path = choose_path(T, E, k, flags);
+  MoeArgs a{};
+  a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
+  a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
+  a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
+  moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
+  if (path == EXMOE_PATH_DECODE) {
+    EXMOE_HIP(launch_moe_decode(a, stream));
+  } else if (path == EXMOE_PATH_PREFILL) {
+    EXMOE_HIP(launch_moe_prefill(a, stream));
+  } else {
+    // Sequential W4 reference: experts one after another in ascending id, each with its
+    // own launches over its gathered rows; one host read of the offsets drives the loop.
+    int32_t off[kMaxExperts + 1];
+    EXMOE_HIP(hipMemcpyAsync(off, expert_offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, stream));
+    EXMOE_HIP(hipStreamSynchronize(stream));
+    for (int e = 0; e < E; e++) {
+      const int cnt = off[e + 1] - off[e];
+      if (cnt <= 0) continue;
+      EXMOE_HIP(launch_moe_expert_range(a, e, cnt, stream));
+    }
+    EXMOE_HIP(launch_combine(a, stream));
+  }
+  return EXMOE_OK;
+}
+
+extern "C" {
+
+int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
+                      const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
+                      const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int flags, exmoe_bf16* y,
+                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(T, H, I, E, k);
+  if (st) return st;
+  const int path = flags & EXMOE_PATH_MASK;
+  if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if ((st = validate_bank(bank, H, I))) return st;
+  if (T == 0) return EXMOE_OK;
+  CHECK_PTR(x);
+  CHECK_PTR(y);
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  CHECK_PTR4(expert_offsets);
+  CHECK_PTR4(sorted_flat);
+  CHECK_PTR4(flat_to_sorted);
+  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+  if (!workspace || ws_bytes < need)
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
+                          k, flags, y, workspace, ws_bytes, stream);
+}
+
+size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags) {
+  return exmoe_moe_workspace_bytes(T, H, I, E, k, flags);
+}
+
+int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
+                    const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int renormalize, int flags,
+                    exmoe_bf16* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                    int32_t* sorted_flat, int32_t* flat_to_sorted, exmoe_bf16* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_shape(T, H, I, E, k);
+  if (st) return st;
+  const int path = flags & EXMOE_PATH_MASK;
+  if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if ((st = validate_bank(bank, H, I))) return st;
+  CHECK_PTR4(expert_offsets);
+  if (T == 0) return exmoe_group_tokens(topk_ids, 0, k, E, expert_offsets, sorted_flat, flat_to_sorted, nullptr, 0, stream);
+  CHECK_PTR(x);
+  CHECK_PTR(w_router);
+  CHECK_PTR(y);
+  if (!logits || ((uintptr_t)logits & 1u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logits must be non-NULL and 2-byte aligned");
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  CHECK_PTR4(sorted_flat);
+  CHECK_PTR4(flat_to_sorted);
+  if (logit_bias && ((uintptr_t)logit_bias & 3u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logit_bias must be 4-byte aligned");
+  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+  if (!workspace || ws_bytes < need)
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
+  EXMOE_HIP(launch_topk(logits, nullptr, T, E, k, renormalize, topk_ids, topk_weights, stream));
+  EXMOE_HIP(launch_group(topk_ids, T, k, E, expert_offsets, sorted_flat, flat_to_sorted, stream));
+  return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
+                          k, flags, y, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers for the gfx950 kernels: MFMA operand types, int4 dequantization into
+// bf16 MFMA operands, bf16 conversions and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace exmoe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// v_mfma_f32_16x16x32_bf16: A 16x32 (lane l: row l%16, k = 8(l/16)+0..7), B 32x16 (lane l:
+// column l%16, same k), C 16x16 (lane l: column l%16, rows 4(l/16)+0..3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One packed word (8 nibbles u = q + 8, input j at bit 4(j/2) for even j, 16 + 4(j/2) for
+// odd j) -> 8 bf16 operand values 128 + u, exact. Register p holds inputs 2p (low half)
+// and 2p+1 (high half). The "+128 + 8" offset is removed by the correction chain below.
+__device__ __forceinline__ bf16x8 dequant_word(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, magic = 0x43004300u;   // bf16 128.0 in both halves
+  i32x4 r;
+  r[0] = (int)((w & m) | magic);
+  r[1] = (int)(((w >> 4) & m) | magic);
+  r[2] = (int)(((w >> 8) & m) | magic);
+  r[3] = (int)(((w >> 12) & m) | magic);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Operand of -136.0 in every element: an MFMA chain of it against the activation
+// fragments yields -136 * (sum of the activations of the group), which turns the
+// 128 + u operand values into the signed codes q = u - 8.
+__device__ __forceinline__ bf16x8 neg136_operand() {
+  i32x4 r;
+  r[0] = r[1] = r[2] = r[3] = (int)0xC308C308u;          // bf16 -136.0
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// acc[i] += scale(row i) * c[i]; sc holds the 4 bf16 scales of the lane's rows 4(l/16)+0..3.
+__device__ __forceinline__ void scale_accum(f32x4& acc, const f32x4& c, uint2 sc) {
+  acc[0] += __uint_as_float(sc.x << 16) * c[0];
+  acc[1] += __uint_as_float(sc.x & 0xFFFF0000u) * c[1];
+  acc[2] += __uint_as_float(sc.y << 16) * c[2];
+  acc[3] += __uint_as_float(sc.y & 0xFFFF0000u) * c[3];
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 with a single rounding (nearest even), no detour through fp32.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  if (v == 0.0) return __double_as_longlong(v) < 0 ? 0x8000 : 0;
+  int e;
+  (void)frexp(v, &e);                      // v = m 2^e, 0.5 <= |m| < 1
+  int qe = e - 1 - 7;
+  if (qe < -133) qe = -133;
+  double r = ldexp(rint(ldexp(v, -qe)), qe);
+  return (uint16_t)(__float_as_uint((float)r) >> 16);
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    T o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// The a-th (0-based) expert with a non-empty segment, or -1; also returns the count of
+// non-empty segments. Called by a whole wave; E <= 256.
+__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets, int E, int a,
+                                                 int* n_active) {
+  int lane = (int)lane_id();
+  int found = -1, base = 0;
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    int e = c0 + lane;
+    bool act = e < E && offsets[e + 1] > offsets[e];
+    uint64_t m = __ballot(act);
+    int rank = base + __popcll(m & ((1ull << lane) - 1ull));
+    uint64_t hit = __ballot(act && rank == a);
+    if (hit) found = c0 + (int)__ffsll((long long)hit) - 1;
+    base += __popcll(m);
+  }
+  *n_active = base;
+  return found;
+}
+
+}  // namespace exmoe
