@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused grouped W4A16 MoE expert layer on one MI355X.
+
+One step = one whole MoE layer call through the C ABI (router logits, top-k, grouping,
+gate/up + SiLU*up, down + routing weight, combine) on one batch of synthetic tokens,
+with the packed experts resident in HBM. Default workload: the OLMoE-shaped decode layer
+(hidden 2048, 64 experts, top-8, intermediate 1024, int4 group-128) at 16 tokens per
+call; 8 copies of the layer's expert bank at distinct addresses (1.66 GB) and 64 token
+batches are rotated so consecutive calls neither hit the 256 MB Infinity Cache nor reuse
+a routing. Steps are captured in one HIP graph and replayed.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline figure (algorithmic bytes
+per launch over its average launch time, timed with HIP events around each launch on
+its stream) and the CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/s on 1 MI355X; % HBM BW (decode) / % bf16 MFMA (prefill)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--tokens", type=int, default=16, help="tokens per decode call (1, 4 or 16)")
+    ap.add_argument("--rotate", type=int, default=8, help="expert-bank copies rotated across calls")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["decode", "prefill", "large"], default=None,
+                    help="run a single workload (for profiling)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- workloads
+class Workload:
+    def __init__(self, name, shape, T, layer, banks, xs, bias=None):
+        self.name, self.shape, self.T, self.layer, self.banks, self.xs, self.bias = name, shape, T, layer, banks, xs, bias
+
+
+def build_olmoe(exm, torch, rotate):
+    from synthetic import SyntheticLayer, OLMOE
+    lay = SyntheticLayer(OLMOE, seed=0)
+    t0 = time.time()
+    blobs = [None] * OLMOE.E
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(e):
+        return e, exm.quantize_pack(*lay.expert(e))
+
+    with ThreadPoolExecutor(8) as ex:
+        for e, b in ex.map(one, range(OLMOE.E)):
+            blobs[e] = b
+    bank0 = exm.bank_from_blobs(blobs)
+    banks = [bank0] + [exm.ExpertBank(base=bank0.base.clone(), stride=bank0.stride) for _ in range(rotate - 1)]
+    torch.cuda.synchronize()
+    log(f"built OLMoE-shaped layer: {rotate} bank copies of {bank0.base.numel() / 1e6:.1f} MB in {time.time() - t0:.1f}s")
+    return lay, banks
+
+
+def bytes_per_call(exm, torch, lay_syn, shape, wr, xs_dev, T, bias=None):
+    """Distinct experts of each x batch (from a routing pass) -> algorithmic HBM bytes."""
+    D = []
+    for x in xs_dev:
+        _, ids, _ = exm.route_topk(x, wr, shape.k, bias=bias)
+        D.append(len(np.unique(ids.cpu().numpy())))
+    return np.array(D)
+
+
+def time_layer(exm, torch, wl, steps, warmup, use_graph):
+    shape = wl.shape
+    bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k)
+    wr = wl.layer["wr"]
+
+    def step(i):
+        exm.moe_layer(wl.xs[i % len(wl.xs)], wr, wl.banks[i % len(wl.banks)], shape.I, shape.k, bias=wl.bias,
+                      buffers=bufs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        graph.replay()          # warm replay
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    return ms / steps
+
+
+def kernel_times(exm, torch, wl, steps, names):
+    """Average launch time of each named kernel: HIP events around every launch."""
+    shape = wl.shape
+    bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k)
+    wr = wl.layer["wr"]
+    exm.profile_reset()
+    exm.profile_enable(True)
+    for i in range(steps):
+        exm.moe_layer(wl.xs[i % len(wl.xs)], wr, wl.banks[i % len(wl.banks)], shape.I, shape.k, bias=wl.bias,
+                      buffers=bufs)
+    torch.cuda.synchronize()
+    out = {}
+    for n in names:
+        ms, cnt = exm.profile_read(n)
+        if cnt:
+            out[n] = (ms / cnt, cnt)
+    exm.profile_enable(False)
+    exm.profile_reset()
+    return out
+
+
+def cpu_baseline(lay_syn, shape, T, seconds, n_batches=64):
+    """The CPU oracle as it stands, on successive fresh batches of the same workload, until
+    `seconds` of CPU work have run (dequantization of the used experts included)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    wr = lay_syn.router()
+    t0 = time.time()
+    qexp = [oracle.quantize_expert(*lay_syn.expert(e)) for e in range(shape.E)]
+    tq = time.time() - t0
+    tokens = 0
+    batches = 0
+    t0 = time.time()
+    while True:
+        for q in qexp:
+            q.drop_cache()
+        x = lay_syn.x(T, stream=1000 + batches)
+        oracle.moe_layer(x, wr, qexp, shape.k)
+        tokens += T
+        batches += 1
+        el = time.time() - t0
+        if el >= seconds or batches >= n_batches:
+            break
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{batches} fresh {T}-token batches of the OLMoE-shaped decode layer through the fp64 "
+                      f"oracle (per-token expert MLPs, dequantization of the routed experts included; "
+                      f"{el:.1f}s; quantization {tq:.1f}s not counted)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the layer is not sharded across GPUs "
+                                   "(see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import w4a16_mixture_experts_amd as exm
+    from synthetic import OLMOE, LARGE, SyntheticLayer
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    H, I, E, k = OLMOE.H, OLMOE.I, OLMOE.E, OLMOE.k
+    expert_bytes = exm.packed_expert_bytes(H, I)
+    gu_bytes = 2 * (I // 16) * (H // 128) * 1056
+    down_bytes = (H // 16) * (I // 128) * 1056
+    result = {}
+    secondary = {}
+    use_graph = not args.no_graph
+
+    olmoe_syn = banks = None
+    if args.only in (None, "decode", "prefill"):
+        olmoe_syn, banks = build_olmoe(exm, torch, args.rotate)
+        wr = to_dev_bf16(olmoe_syn.router())
+
+    # ------------------------------------------------------------------ decode (headline)
+    def run_decode(T, steps, warmup, want_kernels):
+        xs = [to_dev_bf16(olmoe_syn.x(T, stream=s)) for s in range(64)]
+        wl = Workload(f"olmoe_decode_T{T}", OLMOE, T, {"wr": wr}, banks, xs)
+        D = bytes_per_call(exm, torch, olmoe_syn, OLMOE, wr, xs, T)
+        ms = time_layer(exm, torch, wl, steps, warmup, use_graph)
+        layer_bytes = D.mean() * expert_bytes + E * H * 2 + 2 * T * H * 2 + T * k * 8
+        rec = {"T": T, "tokens_per_s": T / (ms * 1e-3), "us_per_layer": ms * 1e3,
+               "distinct_experts_mean": float(D.mean()),
+               "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+               "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if want_kernels:
+            kt = kernel_times(exm, torch, wl, min(steps, 256),
+                              ["route_logits", "topk", "group", "decode_gateup", "decode_down"])
+            rec["kernel_us"] = {n: v[0] * 1e3 for n, v in kt.items()}
+            ms_gu = kt["decode_gateup"][0]
+            gu_alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2
+            rec["roofline"] = {"bound": "hbm", "achieved": gu_alg / (ms_gu * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": gu_alg / (ms_gu * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "traffic": None, "kernel": "decode_gateup_kernel",
+                               "algorithmic_bytes_per_launch": gu_alg, "avg_launch_us": ms_gu * 1e3}
+            if "decode_down" in kt:
+                ms_d = kt["decode_down"][0]
+                d_alg = D.mean() * down_bytes + T * k * I * 2 + 2 * T * k * H * 4 + T * H * 2
+                rec["down_kernel"] = {"achieved_gbs": d_alg / (ms_d * 1e-3) / 1e9, "avg_launch_us": ms_d * 1e3,
+                                      "algorithmic_bytes_per_launch": d_alg}
+        log(f"decode T={T}: {rec['tokens_per_s']:.0f} tok/s, {rec['us_per_layer']:.2f} us/layer, "
+            f"layer {rec['layer_hbm_gbs']:.0f} GB/s ({rec['layer_hbm_frac'] * 100:.1f}% of HBM)")
+        return rec
+
+    if args.only in (None, "decode"):
+        head = run_decode(args.tokens, args.steps, args.warmup, True)
+        result["head"] = head
+        if not args.no_secondary and args.only is None:
+            for T in (1, 4, 16):
+                if T != args.tokens:
+                    secondary[f"olmoe_decode_T{T}"] = run_decode(T, args.steps, args.warmup, True)
+
+    # ------------------------------------------------------------------ prefill lines
+    def run_prefill(name, shape, syn, banks_p, wr_p, T, bias, steps, warmup):
+        xs = [to_dev_bf16(syn.x(T, stream=s)) for s in range(4)]
+        bias_t = None if bias is None else torch.from_numpy(bias).cuda()
+        wl = Workload(name, shape, T, {"wr": wr_p}, banks_p, xs, bias_t)
+        ms = time_layer(exm, torch, wl, steps, warmup, use_graph)
+        flops = 6.0 * T * shape.k * shape.H * shape.I
+        kt = kernel_times(exm, torch, wl, min(steps, 8), ["prefill_gateup", "prefill_down", "xsum", "combine",
+                                                          "route_logits", "topk", "group", "decode_gateup",
+                                                          "decode_down"])
+        rec = {"T": T, "tokens_per_s": T / (ms * 1e-3), "ms_per_layer": ms, "layer_tflops": flops / (ms * 1e-3) / 1e12,
+               "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+               "kernel_us": {n: v[0] * 1e3 for n, v in kt.items()}}
+        if "prefill_gateup" in kt:
+            gu_fl = 4.0 * T * shape.k * shape.H * shape.I
+            rec["gateup_tflops"] = gu_fl / (kt["prefill_gateup"][0] * 1e-3) / 1e12
+            rec["gateup_mfma_frac"] = rec["gateup_tflops"] / BF16_PEAK_TFLOPS
+        if "prefill_down" in kt:
+            d_fl = 2.0 * T * shape.k * shape.H * shape.I
+            rec["down_tflops"] = d_fl / (kt["prefill_down"][0] * 1e-3) / 1e12
+        log(f"{name}: {rec['tokens_per_s']:.0f} tok/s, {ms:.3f} ms/layer, {rec['layer_tflops']:.1f} TFLOP/s "
+            f"({rec['layer_mfma_frac'] * 100:.1f}% of bf16 MFMA)")
+        return rec
+
+    if not args.no_secondary and args.only in (None, "prefill"):
+        bias = olmoe_syn.zipf_bias()
+        for T in (128, 512, 2048):
+            secondary[f"olmoe_prefill_zipf_T{T}"] = run_prefill(f"olmoe_prefill_zipf_T{T}", OLMOE, olmoe_syn,
+                                                                banks[:2], wr, T, bias, 20, 3)
+    if banks is not None:
+        del banks
+        torch.cuda.empty_cache()
+    if not args.no_secondary and args.only in (None, "large"):
+        syn = SyntheticLayer(LARGE, seed=0)
+        t0 = time.time()
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(4) as ex:
+            blobs = [b for b in ex.map(lambda e: exm.quantize_pack(*syn.expert(e)), range(LARGE.E))]
+        bank = exm.bank_from_blobs(blobs)
+        del blobs
+        log(f"built large-expert layer ({bank.base.numel() / 1e6:.0f} MB) in {time.time() - t0:.1f}s")
+        secondary["large_prefill_T4096"] = run_prefill("large_prefill_T4096", LARGE, syn, [bank],
+                                                       to_dev_bf16(syn.router()), 4096, None, 10, 2)
+
+    if "head" not in result:
+        print(json.dumps({"secondary": secondary}))
+        return
+    head = result["head"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(olmoe_syn, OLMOE, args.tokens, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.2f} tok/s on {cpu['cores']} threads")
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_layer"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"olmoe_decode_T{args.tokens}", "hidden": H, "experts": E, "top_k": k,
+                   "intermediate": I, "tokens_per_call": args.tokens, "weights": "int4 group-128 symmetric, bf16 scales",
+                   "rotated_banks": args.rotate, "hip_graph": use_graph,
+                   "layer_hbm_gbs": head["layer_hbm_gbs"], "layer_hbm_frac": head["layer_hbm_frac"],
+                   "distinct_experts_mean": head["distinct_experts_mean"], "kernel_us": head.get("kernel_us")},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -229,6 +229,18 @@ int exmoe_slot_cache_reset_stats(exmoe_slot_cache* cache);
 /* Waits for outstanding copies, frees everything. NULL is a no-op. */
 int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 
+/* ------------------------------------------------------------------------------------
+ * Per-kernel timing for benchmarks (not part of the layer's semantics). While enabled,
+ * each kernel launch of the library is bracketed by a hipEvent pair on its launch stream
+ * (skipped on a stream that is being captured into a graph). exmoe_profile_read
+ * synchronizes the recorded events and returns the accumulated milliseconds and launch
+ * count of one kernel by name: "route_logits", "topk", "group", "decode_gateup",
+ * "decode_down", "combine", "xsum", "prefill_gateup", "prefill_down". Process-global.
+ * ---------------------------------------------------------------------------------- */
+int exmoe_profile_enable(int on);
+int exmoe_profile_reset(void);
+int exmoe_profile_read(const char* kernel_name, double* total_ms, uint64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

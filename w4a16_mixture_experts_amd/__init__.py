@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libexmoe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libexmoe.so is not built ({LIB_PATH}); run w4a16_mixture_experts_amd.build_lib")
+    raise ImportError(f"libexmoe.so is not built ({LIB_PATH}); run python w4a16_mixture_experts_amd/build_lib.py")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes (exmoe.h)
@@ -75,6 +75,9 @@ _SIGS = {
     "exmoe_slot_cache_stats": (_i, [_vp, ctypes.POINTER(CacheStatsC)]),
     "exmoe_slot_cache_reset_stats": (_i, [_vp]),
     "exmoe_slot_cache_destroy": (_i, [_vp]),
+    "exmoe_profile_enable": (_i, [_i]),
+    "exmoe_profile_reset": (_i, []),
+    "exmoe_profile_read": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -339,3 +342,20 @@ class SlotCache:
             self.close()
         except Exception:
             pass
+
+
+# ----------------------------------------------------------------------------- kernel timing
+def profile_enable(on: bool = True):
+    _check(_lib.exmoe_profile_enable(int(on)))
+
+
+def profile_reset():
+    _check(_lib.exmoe_profile_reset())
+
+
+def profile_read(kernel: str):
+    """(total milliseconds, launches) of one library kernel since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_uint64(0)
+    _check(_lib.exmoe_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

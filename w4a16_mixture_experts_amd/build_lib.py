@@ -1,7 +1,7 @@
 """Compile libexmoe.so (all HIP kernels and the C ABI) for gfx950, in-tree.
 
-Run as ``python -m w4a16_mixture_experts_amd.build_lib``; called by the repository's
-build entry point. hipcc cross-compiles without a GPU.
+Run as ``python w4a16_mixture_experts_amd/build_lib.py`` (by path, so that a stale
+library is not loaded first); called by the repository's build entry point. hipcc cross-compiles without a GPU.
 """
 from __future__ import annotations
 
@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 
-SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "group.hip", "moe_decode.hip", "moe_prefill.hip"]
+SOURCES = ["api.cpp", "slot_cache.cpp", "profile.cpp", "route.hip", "group.hip", "moe_decode.hip", "moe_prefill.hip"]
 
 
 def hipcc() -> str:

@@ -33,6 +33,20 @@ int hip_error(hipError_t e, const char* what);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Event pair around one kernel launch when profiling is enabled (exmoe_profile_enable).
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
 // ---- kernel launchers (defined in the .hip files); each returns a HIP error code
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s);

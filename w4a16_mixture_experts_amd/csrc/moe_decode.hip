@@ -296,8 +296,14 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
-  hipLaunchKernelGGL(decode_gateup_kernel, dim3(a.I / (kTileRows * kGuRB), ny), dim3(256), 0, s, a, -1);
-  hipLaunchKernelGGL(decode_down_kernel, dim3(a.H / (kTileRows * kDownRB), ny), dim3(256), 0, s, a, -1);
+  {
+    ProfScope prof("decode_gateup", s);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3(a.I / (kTileRows * kGuRB), ny), dim3(256), 0, s, a, -1);
+  }
+  {
+    ProfScope prof("decode_down", s);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(a.H / (kTileRows * kDownRB), ny), dim3(256), 0, s, a, -1);
+  }
   return hipGetLastError();
 }
 
@@ -310,6 +316,7 @@ hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipSt
 
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  ProfScope prof("combine", s);
   hipLaunchKernelGGL(combine_kernel, dim3((a.H + 63) / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256),
                      0, s, a);
   return hipGetLastError();

@@ -309,11 +309,20 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
   const int TK = a.T * a.k;
   const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
   const int G = a.H / kGroup;
-  hipLaunchKernelGGL(xsum_kernel, dim3((a.T * G + 255) / 256), dim3(256), 0, s, a.x, a.T, a.H, a.xsum);
+  {
+    ProfScope prof("xsum", s);
+    hipLaunchKernelGGL(xsum_kernel, dim3((a.T * G + 255) / 256), dim3(256), 0, s, a.x, a.T, a.H, a.xsum);
+  }
   const int rt_gu = a.I / 128;
-  hipLaunchKernelGGL(prefill_kernel<true>, dim3(max_tt * rt_gu), dim3(kPfThreads), 0, s, a, -1, rt_gu);
+  {
+    ProfScope prof("prefill_gateup", s);
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(max_tt * rt_gu), dim3(kPfThreads), 0, s, a, -1, rt_gu);
+  }
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
-  hipLaunchKernelGGL(prefill_kernel<false>, dim3(max_tt * rt_d), dim3(kPfThreads), 0, s, a, -1, rt_d);
+  {
+    ProfScope prof("prefill_down", s);
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(max_tt * rt_d), dim3(kPfThreads), 0, s, a, -1, rt_d);
+  }
   return launch_combine(a, s);
 }
 

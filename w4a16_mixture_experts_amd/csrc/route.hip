@@ -136,6 +136,7 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
                                int E, uint16_t* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + kRouteTB - 1) / kRouteTB, (E + kRouteEB - 1) / kRouteEB);
+  ProfScope prof("route_logits", s);
   hipLaunchKernelGGL(route_logits_kernel, grid, dim3(256), 0, s, x, wr, bias, T, H, E, logits);
   return hipGetLastError();
 }
@@ -143,6 +144,7 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
                        int renormalize, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  ProfScope prof("topk", s);
   hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, given_ids, T, E, k,
                      renormalize, ids, w);
   return hipGetLastError();
