@@ -38,6 +38,7 @@ static int check_shape(int T, int H, int I, int E, int k) {
   if (E < 1 || E > kMaxExperts) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "E must be in [1, 256] (got %d)", E);
   if (k < 1 || k > E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "k must be in [1, E] (got k=%d, E=%d)", k, E);
   if (k > 64) return set_error(EXMOE_ERR_UNSUPPORTED, "k > 64 is not supported (got %d)", k);
+  if (H > kMaxDim || I > kMaxDim) return set_error(EXMOE_ERR_UNSUPPORTED, "H and I must be <= %d", kMaxDim);
   if ((long long)T * k > (1LL << 30)) return set_error(EXMOE_ERR_UNSUPPORTED, "T*k too large");
   return EXMOE_OK;
 }
@@ -472,8 +473,18 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
-  EXMOE_HIP(launch_topk(logits, nullptr, T, E, k, renormalize, topk_ids, topk_weights, stream));
-  EXMOE_HIP(launch_group(topk_ids, T, k, E, expert_offsets, sorted_flat, flat_to_sorted, stream));
+  if (choose_path(T, E, k, flags) == EXMOE_PATH_DECODE && decode_fused_routing_ok(T, k)) {
+    MoeArgs a{};
+    a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
+    a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
+    a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
+    moe_workspace_layout(T, H, I, E, k, EXMOE_PATH_DECODE, &a, workspace);
+    EXMOE_HIP(launch_moe_decode_fused(a, logits, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
+                                      flat_to_sorted, stream));
+    return EXMOE_OK;
+  }
+  EXMOE_HIP(launch_topk_group(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
+                              flat_to_sorted, stream));
   return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
                           k, flags, y, workspace, ws_bytes, stream);
 }

@@ -15,6 +15,7 @@ constexpr int kTileRows = 16;    // output rows per packed tile
 constexpr int kTileBytes = 1024; // 16 rows x 128 inputs x 4 bits
 constexpr int kScaleBytes = 32;  // 16 bf16 scales per tile
 constexpr int kMaxExperts = 256;
+constexpr int kMaxDim = 16384;   // largest hidden / intermediate size (zero-row length)
 
 __host__ __device__ inline size_t n_tiles(int H, int I) {
   return 2 * (size_t)(I / kTileRows) * (H / kGroup) + (size_t)(H / kTileRows) * (I / kGroup);
@@ -52,6 +53,9 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
                                int E, uint16_t* logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
                        int renormalize, int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int renormalize, int32_t* ids,
+                             float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
+                             hipStream_t s);
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_flat,
                         int32_t* flat_to_sorted, hipStream_t s);
 
@@ -78,6 +82,12 @@ struct MoeArgs {
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s);
+bool decode_fused_routing_ok(int T, int k);
+// Decode path with the top-k selection and grouping redone inside the gate/up kernel; the
+// routing outputs are published to the given buffers (a.offsets etc. must alias them).
+hipError_t launch_moe_decode_fused(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
+                                   float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
+                                   hipStream_t s);
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);

@@ -17,11 +17,28 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Compile-time constants hidden from constant folding, so that (a & m) | o below is
+// selected as one v_and_or_b32 (m in an SGPR, o in a VGPR: one constant-bus read)
+// instead of v_and + v_or with literals. The asm only moves constants; its VGPR result
+// feeds VALU ops alone (no VALU-to-MFMA hazard hides behind it, since the compiler's
+// hazard checks do not see through asm).
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
+}
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
 // One packed word (8 nibbles u = q + 8, input j at bit 4(j/2) for even j, 16 + 4(j/2) for
-// odd j) -> 8 bf16 operand values 128 + u, exact. Register p holds inputs 2p (low half)
-// and 2p+1 (high half). The "+128 + 8" offset is removed by the correction chain below.
+// odd j) -> 8 bf16 operand values 128 + u, exact, in 7 VALU ops. Register p holds inputs
+// 2p (low half) and 2p+1 (high half). The "+128 + 8" offset is removed by the -136
+// correction of the group's MFMA chain.
 __device__ __forceinline__ bf16x8 dequant_word(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, magic = 0x43004300u;   // bf16 128.0 in both halves
+  const uint32_t m = opaque_sgpr(0x000F000Fu), magic = opaque_vgpr(0x43004300u);  // bf16 128.0 x2
   i32x4 r;
   r[0] = (int)((w & m) | magic);
   r[1] = (int)(((w >> 4) & m) | magic);
@@ -68,6 +85,68 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Cross-lane reductions on DPP row rotations (within 16-lane rows) plus four readlanes
+// across the rows; the result is wave-uniform. Much shorter latency than LDS permutes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = dpp_u32<0x121>(v); v = o > v ? o : v;   // row_ror:1
+  o = dpp_u32<0x122>(v); v = o > v ? o : v;   // row_ror:2
+  o = dpp_u32<0x124>(v); v = o > v ? o : v;   // row_ror:4
+  o = dpp_u32<0x128>(v); v = o > v ? o : v;   // row_ror:8
+  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), e = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  a = a > b ? a : b;
+  c = c > e ? c : e;
+  return a > c ? a : c;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  float o;
+  o = __uint_as_float(dpp_u32<0x121>(__float_as_uint(v))); v = fmaxf(v, o);
+  o = __uint_as_float(dpp_u32<0x122>(__float_as_uint(v))); v = fmaxf(v, o);
+  o = __uint_as_float(dpp_u32<0x124>(__float_as_uint(v))); v = fmaxf(v, o);
+  o = __uint_as_float(dpp_u32<0x128>(__float_as_uint(v))); v = fmaxf(v, o);
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, e));
+}
+// Sum in a fixed order (deterministic): row rotations, then rows 0+1+2+3.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<0x121>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x122>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((a + b) + c) + e;
+}
+__device__ __forceinline__ double dpp_f64_ror(double v, int which) {
+  const long long b = __double_as_longlong(v);
+  int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+  switch (which) {
+    case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x121, 0xF, 0xF, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x121, 0xF, 0xF, false); break;
+    case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x122, 0xF, 0xF, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x122, 0xF, 0xF, false); break;
+    case 4: lo = __builtin_amdgcn_update_dpp(0, lo, 0x124, 0xF, 0xF, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x124, 0xF, 0xF, false); break;
+    default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x128, 0xF, 0xF, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x128, 0xF, 0xF, false); break;
+  }
+  return __longlong_as_double(((long long)(unsigned)lo) | ((long long)hi << 32));
+}
+// fp64 sum over each 16-lane row (every lane of the row gets the row's sum).
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64_ror(v, 1);
+  v += dpp_f64_ror(v, 2);
+  v += dpp_f64_ror(v, 4);
+  v += dpp_f64_ror(v, 8);
+  return v;
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {

@@ -5,7 +5,8 @@
 //   gate/up: rows = 128 gate rows + the matching 128 up rows (one 128-wide slice of the
 //            intermediate dimension), epilogue h = bf16(silu(g) * u) plus the fp32 sum of
 //            each token's 128 rounded h values (the next kernel's dequant correction);
-//   down:    rows = 256 output rows, epilogue y_perm = o * routing weight (fp32).
+//   down:    rows = 256 output rows, epilogue y_perm = o * routing weight (fp32), stored in
+//            flat (token, slot) order for the combine.
 // The activation tile of each 128-input group is gathered (gate/up: through the token
 // permutation) into LDS, double-buffered, rows padded to 272 B so that the 16 tokens of a
 // fragment read hit distinct banks. Packed int4 tiles go straight from HBM to registers
@@ -23,6 +24,10 @@ constexpr int kPfThreads = 512;
 constexpr int kPfBN = 128;                 // tokens per workgroup tile
 constexpr int kPfRows = 256;               // output rows per workgroup tile
 constexpr int kLdsStride = kGroup + 8;     // bf16 elements per LDS row (272 B)
+
+// All-zero row read for rows past a segment's end (device globals start zeroed; never
+// written).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row_pf[kMaxDim];
 
 // Which expert / token tile / row tile this workgroup owns. Token tiles are counted per
 // expert (ceil(count / 128)); a single wave scans the counts (E <= 256).
@@ -123,20 +128,20 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
   // ---- staging of the activation tile: thread -> (row, 4 chunks of 16 B)
   const int st_row = tid >> 2, st_c = tid & 3;
   const bool st_valid = pt.tok0 + st_row < pt.cnt;
-  const uint16_t* st_src;
-  if (GATEUP) {
-    const int tok = st_valid ? a.sorted_flat[pt.seg0 + pt.tok0 + st_row] / a.k : 0;
-    st_src = a.x + (size_t)tok * a.H;
-  } else {
-    st_src = a.h + (size_t)(pt.seg0 + (st_valid ? pt.tok0 + st_row : 0)) * a.I;
+  // Rows past the segment read the zero row: loads stay unconditional, so the compiler
+  // counts them exactly and the prefetch stays in flight.
+  const uint16_t* st_src = g_zero_row_pf;
+  if (st_valid) {
+    if (GATEUP)
+      st_src = a.x + (size_t)(a.sorted_flat[pt.seg0 + pt.tok0 + st_row] / a.k) * a.H;
+    else
+      st_src = a.h + (size_t)(pt.seg0 + pt.tok0 + st_row) * a.I;
   }
   uint4 st_reg[4];
   auto stage_load = [&](int g) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      st_reg[i] = st_valid ? *reinterpret_cast<const uint4*>(st_src + g * kGroup + (st_c + 4 * i) * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; i++)
+      st_reg[i] = *reinterpret_cast<const uint4*>(st_src + g * kGroup + (st_c + 4 * i) * 8);
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
@@ -182,15 +187,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
 
   for (int g = 0; g < G; g++) {
     const int buf = g & 1;
-    if (g + 1 < G) {
-      stage_load(g + 1);
-      w_load(g + 1, wnext, snext);
-    }
+    const int gn = g + 1 < G ? g + 1 : g;         // the last prefetch repeats a group, harmlessly
+    stage_load(gn);
+    w_load(gn, wnext, snext);
     // correction seeds: -136 * group sum of each token's activations
     f32x4 tmp[4][4];
 #pragma unroll
     for (int bj = 0; bj < 4; bj++) {
-      const float c = cval[bj] ? -136.0f * csum[(size_t)crow[bj] * G + g] : 0.f;
+      const float cs = csum[(size_t)crow[bj] * G + g];
+      const float c = cval[bj] ? -136.0f * cs : 0.f;
 #pragma unroll
       for (int ai = 0; ai < 4; ai++) tmp[ai][bj] = f32x4{c, c, c, c};
     }
@@ -216,13 +221,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
     for (int ai = 0; ai < 4; ai++)
 #pragma unroll
       for (int bj = 0; bj < 4; bj++) scale_accum(acc[ai][bj], tmp[ai][bj], scur[ai]);
-    if (g + 1 < G) {
-      stage_store(buf ^ 1);
+    stage_store(buf ^ 1);
 #pragma unroll
-      for (int ai = 0; ai < 4; ai++) {
-        wcur[ai] = wnext[ai];
-        scur[ai] = snext[ai];
-      }
+    for (int ai = 0; ai < 4; ai++) {
+      wcur[ai] = wnext[ai];
+      scur[ai] = snext[ai];
     }
     __syncthreads();
   }
@@ -272,13 +275,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
     for (int bj = 0; bj < 4; bj++) {
       const int r = pt.tok0 + wt * 64 + bj * 16 + (lane & 15);
       if (r < pt.cnt) {
-        const float wgt = a.w[a.sorted_flat[pt.seg0 + r]];
+        const int f = a.sorted_flat[pt.seg0 + r];     // y_perm rows are in flat (token, slot) order
+        const float wgt = a.w[f];
 #pragma unroll
         for (int ai = 0; ai < 4; ai++) {
           if (!rvalid[ai]) continue;
           const int col = (rt * 16 + 4 * wr + ai) * 16 + 4 * (lane >> 4);
           const f32x4 o = acc[ai][bj];
-          *reinterpret_cast<float4*>(a.y_perm + (size_t)(pt.seg0 + r) * a.H + col) =
+          *reinterpret_cast<float4*>(a.y_perm + (size_t)f * a.H + col) =
               make_float4(o[0] * wgt, o[1] * wgt, o[2] * wgt, o[3] * wgt);
         }
       }

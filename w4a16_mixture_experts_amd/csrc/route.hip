@@ -6,62 +6,92 @@
 // summation order. Selection: (logit descending, expert id ascending) on the bf16 logits.
 #include "common.h"
 #include "device.h"
+#include "group_block.h"
+#include "topk.h"
 
 namespace exmoe {
 
 // ---------------------------------------------------------------------------------
-// Logits. A workgroup of 256 threads owns 4 tokens x 4 experts; 16 lanes split each
-// (token, expert) dot product over H in interleaved 8-element chunks (each 16-lane
-// group reads 256 contiguous bytes), then reduce in fp64 with lane shuffles.
+// Logits. A lane group owns a block of TB tokens x EB experts and splits H among its
+// LANES lanes in interleaved 16-byte chunks (contiguous bytes across the group); each
+// chunk is converted to fp64 once and feeds TB*EB fp64 FMAs (bf16 products are exact in
+// fp64). Partial sums are added with DPP row rotations (and across rows with readlane
+// when LANES = 64); one lane rounds once to bf16. Few tokens: LANES = 64, small blocks,
+// many waves. Many tokens: LANES = 16, 4 x 4 blocks for operand reuse.
 // ---------------------------------------------------------------------------------
-constexpr int kRouteTB = 4, kRouteEB = 4, kRouteSplit = 16;
-
-__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr,
-                                                           const float* __restrict__ bias, int T,
-                                                           int H, int E,
-                                                           uint16_t* __restrict__ logits) {
-  const int tid = threadIdx.x;
-  const int sp = tid % kRouteSplit;
-  const int p = tid / kRouteSplit;          // 0..15
-  const int t = blockIdx.x * kRouteTB + p / kRouteEB;
-  const int e = blockIdx.y * kRouteEB + p % kRouteEB;
-  const bool valid = t < T && e < E;
-  double acc = 0.0;
-  if (valid) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
-    const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
-    const int chunks = H / 8;
-    for (int c = sp; c < chunks; c += kRouteSplit) {
-      uint4 xv = xr[c], wv = wrow[c];
-      const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w};
-      const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
+template <int TB, int EB, int LANES>
+__global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias, int T,
+                                                          int H, int E,
+                                                          uint16_t* __restrict__ logits) {
+  const int lane = (int)lane_id();
+  const int li = lane % LANES;
+  const int nEB = (E + EB - 1) / EB;
+  const int blk = blockIdx.x * (64 / LANES) + lane / LANES;   // (token block, expert block)
+  const int tb = blk / nEB, eb = blk % nEB;
+  const int t0 = tb * TB, e0 = eb * EB;
+  double acc[TB][EB];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        float x0 = __uint_as_float(xa[q] << 16), x1 = __uint_as_float(xa[q] & 0xFFFF0000u);
-        float w0 = __uint_as_float(wa[q] << 16), w1 = __uint_as_float(wa[q] & 0xFFFF0000u);
-        acc += (double)(x0 * w0);   // bf16 x bf16 is exact in fp32
-        acc += (double)(x1 * w1);
+  for (int i = 0; i < TB; i++)
+#pragma unroll
+    for (int j = 0; j < EB; j++) acc[i][j] = 0.0;
+  if (t0 < T) {
+    const int chunks = H / 8;
+    for (int c = li; c < chunks; c += LANES) {
+      double xv[TB][8], wv[EB][8];
+#pragma unroll
+      for (int i = 0; i < TB; i++) {
+        const int t = t0 + i < T ? t0 + i : T - 1;
+        const uint4 u = reinterpret_cast<const uint4*>(x + (size_t)t * H)[c];
+        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          xv[i][2 * q] = (double)__uint_as_float(q4[q] << 16);
+          xv[i][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < EB; j++) {
+        const int e = e0 + j < E ? e0 + j : E - 1;
+        const uint4 u = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
+        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          wv[j][2 * q] = (double)__uint_as_float(q4[q] << 16);
+          wv[j][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TB; i++)
+#pragma unroll
+        for (int j = 0; j < EB; j++)
+#pragma unroll
+          for (int q = 0; q < 8; q++) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
     }
   }
 #pragma unroll
-  for (int off = kRouteSplit / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (valid && sp == 0) {
-    if (bias) acc += (double)bias[e];
-    logits[(size_t)t * E + e] = f64_to_bf16(acc);
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// Top-k + weights: one wave per token. Each lane holds up to 4 experts (E <= 256) as
-// 32-bit keys (order-preserving logit bits << 16 | (0xFFFF - id)); k rounds of a wave
-// max pick the winners in slot order. -0 is canonicalized to +0 so the two tie.
-// ---------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(uint16_t b, int e) {
-  if (b == 0x8000) b = 0;
-  uint32_t o = (b & 0x8000) ? (uint32_t)(~b & 0xFFFF) : (uint32_t)(b | 0x8000);
-  return (o << 16) | (uint32_t)(0xFFFF - e);
+  for (int i = 0; i < TB; i++)
+#pragma unroll
+    for (int j = 0; j < EB; j++) {
+      double s = row16_sum_f64(acc[i][j]);
+      if (LANES == 64) {
+        // rows 0..3 of the wave, added in a fixed order
+        const long long b = __double_as_longlong(s);
+        const int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+        double r[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          r[q] = __longlong_as_double(((long long)(unsigned)__builtin_amdgcn_readlane(lo, 16 * q)) |
+                                      ((long long)__builtin_amdgcn_readlane(hi, 16 * q) << 32));
+        s = ((r[0] + r[1]) + r[2]) + r[3];
+      }
+      const int t = t0 + i, e = e0 + j;
+      if (li == 0 && t < T && e < E) {
+        const double v = bias ? s + (double)bias[e] : s;
+        logits[(size_t)t * E + e] = f64_to_bf16(v);
+      }
+    }
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const uint16_t* __restrict__ logits,
@@ -72,72 +102,69 @@ __global__ __launch_bounds__(256) void topk_kernel(const uint16_t* __restrict__ 
   const int lane = (int)lane_id();
   const int t = blockIdx.x * 4 + threadIdx.x / 64;
   if (t >= T) return;
-  const uint16_t* lrow = logits + (size_t)t * E;
-  uint32_t key[4];
-  float lv[4];
-  float m_all = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    int e = lane + 64 * q;
-    if (e < E) {
-      uint16_t b = lrow[e];
-      key[q] = order_key(b, e);
-      lv[q] = bf16_to_f32(b);
-      m_all = fmaxf(m_all, lv[q]);
-    } else {
-      key[q] = 0;
-      lv[q] = -INFINITY;
-    }
-  }
-  m_all = wave_max(m_all);
-  // Slot j (k <= 64) lands in lane j.
-  float my_sel = -INFINITY;
-  int my_id = -1;
-  if (given_ids) {
-    if (lane < k) {
-      my_id = given_ids[(size_t)t * k + lane];
-      my_sel = (my_id >= 0 && my_id < E) ? bf16_to_f32(lrow[my_id]) : -INFINITY;
-    }
-  } else {
-    for (int j = 0; j < k; j++) {
-      uint32_t best = key[0];
-#pragma unroll
-      for (int q = 1; q < 4; q++) best = key[q] > best ? key[q] : best;
-      best = wave_max(best);
-      const int id = 0xFFFF - (int)(best & 0xFFFF);
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        if (lane + 64 * q == id) key[q] = 0;     // the owner removes the winner
-      if (lane == j) {
-        my_id = id;
-        my_sel = bf16_to_f32(lrow[id]);
-      }
-    }
-  }
-  float m, denom;
-  if (renormalize) {
-    m = wave_max(my_sel);
-    denom = wave_sum(lane < k ? expf(my_sel - m) : 0.f);
-  } else {
-    m = m_all;
-    float z = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-      if (lane + 64 * q < E) z += expf(lv[q] - m);
-    denom = wave_sum(z);
-  }
+  int id;
+  float wt;
+  topk_token(logits + (size_t)t * E, given_ids ? given_ids + (size_t)t * k : nullptr, E, k, renormalize, id, wt);
   if (lane < k) {
-    if (ids) ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = expf(my_sel - m) / denom;
+    if (ids) ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
+}
+
+// Top-k of every token and the grouping in one workgroup (small token counts): the ids
+// stay in LDS between the two phases, saving a launch.
+constexpr int kTopkGroupThreads = 256;
+__global__ __launch_bounds__(kTopkGroupThreads) void topk_group_kernel(const uint16_t* __restrict__ logits,
+                                                                  int T, int E, int k, int renormalize,
+                                                                  int32_t* __restrict__ ids,
+                                                                  float* __restrict__ w,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted_flat,
+                                                                  int32_t* __restrict__ flat_to_sorted) {
+  __shared__ int32_t s_ids[kTopkGroupMaxRows];
+  __shared__ GroupSharedT<kTopkGroupThreads> gs;
+  const int lane = (int)lane_id(), wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kTopkGroupThreads / 64) {
+    int id;
+    float wt;
+    topk_token(logits + (size_t)t * E, nullptr, E, k, renormalize, id, wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+      s_ids[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  group_block<kTopkGroupThreads>(s_ids, T * k, E, offsets, sorted_flat, flat_to_sorted, gs);
 }
 
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((T + kRouteTB - 1) / kRouteTB, (E + kRouteEB - 1) / kRouteEB);
   ProfScope prof("route_logits", s);
-  hipLaunchKernelGGL(route_logits_kernel, grid, dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+  if (T <= 64) {
+    // one wave per 2 tokens x 2 experts, the whole wave on H
+    const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
+    hipLaunchKernelGGL((route_logits_kernel<2, 2, 64>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
+  } else {
+    const int blocks = ((T + 3) / 4) * ((E + 3) / 4);
+    hipLaunchKernelGGL((route_logits_kernel<4, 4, 16>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T, H, E,
+                       logits);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int renormalize, int32_t* ids,
+                             float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
+                             hipStream_t s) {
+  if (T * k > kTopkGroupMaxRows) {
+    hipError_t e = launch_topk(logits, nullptr, T, E, k, renormalize, ids, w, s);
+    if (e != hipSuccess) return e;
+    return launch_group(ids, T, k, E, offsets, sorted_flat, flat_to_sorted, s);
+  }
+  ProfScope prof("topk_group", s);
+  hipLaunchKernelGGL(topk_group_kernel, dim3(1), dim3(kTopkGroupThreads), 0, s, logits, T, E, k, renormalize, ids, w,
+                     offsets, sorted_flat, flat_to_sorted);
   return hipGetLastError();
 }
 
