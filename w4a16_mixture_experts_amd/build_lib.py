@@ -25,6 +25,9 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 SOURCES = ["api.cpp", "slot_cache.cpp", "profile.cpp", "route.hip", "group.hip", "moe_decode.hip", "moe_prefill.hip"]
+# Per-file flags. The grouped GEMM keeps MFMA results in VGPRs: they are scaled by VALU
+# FMAs right away, and AGPR results would cost one v_accvgpr_read per element.
+FILE_FLAGS = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -34,7 +37,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE + extra
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE + FILE_FLAGS.get(src, []) + extra
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -351,8 +351,9 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   };
   const size_t o_h = take(rows * I * 2);
   const size_t o_yp = take(rows * H * 4);
-  const size_t o_gs = take(rows * (I / kGroup) * 4);
-  const size_t o_xs = take((size_t)T * (H / kGroup) * 4);
+  // correction seeds of the prefill kernels: [group][sorted row], rows padded by one tile
+  const size_t o_gs = take((rows + 128) * (I / kGroup) * 4);
+  const size_t o_xs = take((rows + 128) * (H / kGroup) * 4);
   const size_t o_ct = take((size_t)(H / 32 + 1) * 4);
   const size_t o_db = take(16);
   if (a && ws) {

@@ -74,8 +74,8 @@ struct MoeArgs {
   // workspace carve-up
   uint16_t* h;        // bf16 [T*k, I], sorted-row order
   float* y_perm;      // fp32 [T*k, H], sorted-row order, already multiplied by the routing weight
-  float* gsum;        // fp32 [T*k, I/128] group sums of h (prefill down correction)
-  float* xsum;        // fp32 [T, H/128] group sums of x (prefill gate/up correction)
+  float* gsum;        // fp32 [I/128][T*k + 128]: -136 * group sums of h per sorted row (down seeds)
+  float* xsum;        // fp32 [H/128][T*k + 128]: -136 * group sums of x per sorted row (gate/up seeds)
   uint32_t* counters; // decode last-arriver counters
   uint32_t* debug;    // debug word(s)
 };

@@ -1,7 +1,8 @@
 // Prefill-sized expert layer (many tokens per expert): grouped GEMMs on bf16 MFMA, gfx950.
 //
 // Every selected expert runs over the tokens grouped to it (ExactMoE abstract; Fig. 1).
-// One workgroup (8 waves) computes a 256-row x 128-token output tile of one expert:
+// One workgroup (4 waves, one per SIMD, up to 512 registers each) computes a 256-row x
+// 128-token output tile of one expert; each wave owns 64 rows x all 128 tokens:
 //   gate/up: rows = 128 gate rows + the matching 128 up rows (one 128-wide slice of the
 //            intermediate dimension), epilogue h = bf16(silu(g) * u) plus the fp32 sum of
 //            each token's 128 rounded h values (the next kernel's dequant correction);
@@ -13,15 +14,16 @@
 // (one 1 KiB tile per wave-wide 128-bit load, prefetched a group ahead) and are turned
 // into exact bf16 operands 128 + u in registers. Each group's MFMA chain starts from
 // -136 * (group sum of the activations), so it ends at sum(x * q); the bf16 scale of the
-// row is applied once per group in fp32. Waves: 4 along rows x 2 along tokens; each wave
-// owns 4 x 4 tiles of 16 x 16.
+// row is applied once per group in fp32. A wave dequantizes its 4 row fragments of a group
+// once and reuses each across the 8 token subtiles (16 tokens each), which keeps the
+// VALU work per MFMA near 1 + 8/8.
 #include "common.h"
 #include "device.h"
 
 namespace exmoe {
 
-constexpr int kPfThreads = 512;
 constexpr int kPfBN = 128;                 // tokens per workgroup tile
+constexpr int kPfWaves = 8;                // waves per workgroup (2 row subtiles each)
 constexpr int kPfRows = 256;               // output rows per workgroup tile
 constexpr int kLdsStride = kGroup + 8;     // bf16 elements per LDS row (272 B)
 
@@ -85,15 +87,23 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
   return t.tok0 < t.cnt;
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int fixed_expert,
-                                                               int n_row_tiles) {
+// NW waves per workgroup; each wave owns NA = 16 / NW row subtiles (of 16 rows) and all
+// 8 token subtiles of the 256 x 128 tile. Tokens are the M operand of the MFMA and weight
+// rows the N operand, so a lane's 4 accumulator values belong to one weight row (one
+// scale) and 4 consecutive tokens (one float4 of correction seeds).
+template <bool GATEUP, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixed_expert,
+                                                           int n_row_tiles) {
+  constexpr int NT = NW * 64;            // threads
+  constexpr int NA = 16 / NW;            // row subtiles per wave
+  constexpr int NST = kPfBN * 16 / NT;   // 16-byte staging chunks per thread and group
   __shared__ __attribute__((aligned(16))) uint16_t s_act[2][kPfBN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) float s_seed[2][kPfBN];
   __shared__ int s_scan[kMaxExperts + 1];
-  __shared__ float s_gsum[4][kPfBN];
+  __shared__ float s_gsum[NW][kPfBN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave & 3, wt = wave >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile addresses stay scalar
   const int rt = blockIdx.x % n_row_tiles;
   const int tt_lin = blockIdx.x / n_row_tiles;
   PfTile pt;
@@ -109,24 +119,29 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
   const int K = GATEUP ? a.H : a.I;
   const int G = K / kGroup;
   const size_t tile_down0 = 2 * (size_t)(a.I / kTileRows) * (a.H / kGroup);
+  const int rows_pad = a.T * a.k + kPfBN;          // row count of the seed arrays
+  const float* seeds = GATEUP ? a.xsum : a.gsum;   // [group][sorted row], already * -136
 
-  // tile index (without the group) of this wave's 4 row subtiles
-  size_t tbase[4];
-  bool rvalid[4];
+  // tile index (without the group) of this wave's NA row subtiles; gate/up subtiles come
+  // in (gate, up) pairs of one 16-row block of the intermediate dimension
+  size_t tbase[NA];
+  bool rvalid[NA];
 #pragma unroll
-  for (int ai = 0; ai < 4; ai++) {
-    rvalid[ai] = GATEUP || (rt * 16 + 4 * wr + ai) < a.H / kTileRows;
+  for (int ai = 0; ai < NA; ai++) {
     if (GATEUP) {
-      const int rbI = rt * 8 + 2 * wr + (ai >> 1);
+      rvalid[ai] = true;
+      const int rbI = rt * 8 + (NA / 2) * wave + (ai >> 1);
       tbase[ai] = (size_t)(rbI * 2 + (ai & 1)) * G;
     } else {
-      const int rbH = rt * 16 + 4 * wr + ai;
+      const int rbH = rt * 16 + NA * wave + ai;
+      rvalid[ai] = rbH < a.H / kTileRows;
       tbase[ai] = tile_down0 + (size_t)(rvalid[ai] ? rbH : 0) * G;
     }
   }
 
-  // ---- staging of the activation tile: thread -> (row, 4 chunks of 16 B)
-  const int st_row = tid >> 2, st_c = tid & 3;
+  // ---- staging of the activation tile (and the group's correction seeds)
+  constexpr int TPR = NT / kPfBN;        // threads per row
+  const int st_row = tid / TPR, st_c = tid % TPR;
   const bool st_valid = pt.tok0 + st_row < pt.cnt;
   // Rows past the segment read the zero row: loads stay unconditional, so the compiler
   // counts them exactly and the prefetch stays in flight.
@@ -137,195 +152,212 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeArgs a, int f
     else
       st_src = a.h + (size_t)(pt.seg0 + pt.tok0 + st_row) * a.I;
   }
-  uint4 st_reg[4];
-  auto stage_load = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-      st_reg[i] = *reinterpret_cast<const uint4*>(st_src + g * kGroup + (st_c + 4 * i) * 8);
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-      *reinterpret_cast<uint4*>(&s_act[buf][st_row * kLdsStride + (st_c + 4 * i) * 8]) = st_reg[i];
-  };
+  const float* seed_src = seeds + pt.seg0 + pt.tok0 + st_row;   // + g * rows_pad; padded rows exist
+  uint4 st_reg[NST];
+  float st_seed;
+#define EXMOE_STAGE_LOAD(g_)                                                                     \
+  _Pragma("unroll") for (int i = 0; i < NST; i++)                                               \
+      st_reg[i] = *reinterpret_cast<const uint4*>(st_src + (g_) * kGroup + (st_c + TPR * i) * 8); \
+  st_seed = seed_src[(size_t)(g_) * rows_pad]
+#define EXMOE_STAGE_STORE(buf_)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < NST; i++)                                               \
+      *reinterpret_cast<uint4*>(&s_act[(buf_)][st_row * kLdsStride + (st_c + TPR * i) * 8]) = st_reg[i]; \
+  if (st_c == 0) s_seed[(buf_)][st_row] = st_seed
 
-  // ---- per-lane token rows of the 4 token subtiles (for the correction sums)
-  int crow[4];
-  bool cval[4];
+  f32x4 acc[NA][8];
 #pragma unroll
-  for (int bj = 0; bj < 4; bj++) {
-    const int r = pt.tok0 + wt * 64 + bj * 16 + (lane & 15);
-    cval[bj] = r < pt.cnt;
-    if (GATEUP)
-      crow[bj] = cval[bj] ? a.sorted_flat[pt.seg0 + r] / a.k : 0;   // token
-    else
-      crow[bj] = pt.seg0 + (cval[bj] ? r : 0);                       // sorted row
+  for (int ai = 0; ai < NA; ai++)
+#pragma unroll
+    for (int bj = 0; bj < 8; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wcur[NA], wnext[NA];
+  uint32_t scur[NA], snext[NA];
+#pragma unroll
+  for (int ai = 0; ai < NA; ai++) {
+    const size_t t = tbase[ai];
+    wcur[ai] = tiles[t * 64 + lane];
+    scur[ai] = scales[t * 16 + (lane & 15)];
   }
-  const float* csum = GATEUP ? a.xsum : a.gsum;
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int ai = 0; ai < 4; ai++)
-#pragma unroll
-    for (int bj = 0; bj < 4; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wcur[4], wnext[4];
-  uint2 scur[4], snext[4];
-  auto w_load = [&](int g, uint4* w, uint2* s) {
-#pragma unroll
-    for (int ai = 0; ai < 4; ai++) {
-      const size_t t = tbase[ai] + g;
-      w[ai] = tiles[t * 64 + lane];
-      s[ai] = *reinterpret_cast<const uint2*>(scales + t * 16 + 4 * (lane >> 4));
-    }
-  };
-
-  stage_load(0);
-  w_load(0, wcur, scur);
-  stage_store(0);
+  EXMOE_STAGE_LOAD(0);
+  EXMOE_STAGE_STORE(0);
   __syncthreads();
 
   for (int g = 0; g < G; g++) {
     const int buf = g & 1;
     const int gn = g + 1 < G ? g + 1 : g;         // the last prefetch repeats a group, harmlessly
-    stage_load(gn);
-    w_load(gn, wnext, snext);
-    // correction seeds: -136 * group sum of each token's activations
-    f32x4 tmp[4][4];
+    EXMOE_STAGE_LOAD(gn);
 #pragma unroll
-    for (int bj = 0; bj < 4; bj++) {
-      const float cs = csum[(size_t)crow[bj] * G + g];
-      const float c = cval[bj] ? -136.0f * cs : 0.f;
-#pragma unroll
-      for (int ai = 0; ai < 4; ai++) tmp[ai][bj] = f32x4{c, c, c, c};
+    for (int ai = 0; ai < NA; ai++) {
+      const size_t t = tbase[ai] + gn;
+      wnext[ai] = tiles[t * 64 + lane];
+      snext[ai] = scales[t * 16 + (lane & 15)];
     }
+    // weight fragments of the group, dequantized once: [row subtile][K step]
+    bf16x8 wfr[NA][4];
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-      bf16x8 bfr[4];
+    for (int ai = 0; ai < NA; ai++) {
+      wfr[ai][0] = dequant_word(wcur[ai].x);
+      wfr[ai][1] = dequant_word(wcur[ai].y);
+      wfr[ai][2] = dequant_word(wcur[ai].z);
+      wfr[ai][3] = dequant_word(wcur[ai].w);
+    }
+    float sc[NA];
 #pragma unroll
-      for (int bj = 0; bj < 4; bj++) {
-        const int row = wt * 64 + bj * 16 + (lane & 15);
-        const uint4 v = *reinterpret_cast<const uint4*>(&s_act[buf][row * kLdsStride + 32 * s + 8 * (lane >> 4)]);
-        i32x4 iv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        bfr[bj] = __builtin_bit_cast(bf16x8, iv);
+    for (int ai = 0; ai < NA; ai++) sc[ai] = __uint_as_float(scur[ai] << 16);
+    // token subtiles in pairs: activation fragments of both for all 4 K steps
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      bf16x8 xfr[2][4];
+      f32x4 seed[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int row = (2 * p + j) * 16 + (lane & 15);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; s4++) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&s_act[buf][row * kLdsStride + 32 * s4 + 8 * (lane >> 4)]);
+          i32x4 iv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          xfr[j][s4] = __builtin_bit_cast(bf16x8, iv);
+        }
+        // seeds of tokens 4(l/16)+0..3 of the subtile: -136 * group sum of their activations
+        seed[j] = *reinterpret_cast<const f32x4*>(&s_seed[buf][(2 * p + j) * 16 + 4 * (lane >> 4)]);
       }
 #pragma unroll
-      for (int ai = 0; ai < 4; ai++) {
-        const uint32_t word = s == 0 ? wcur[ai].x : s == 1 ? wcur[ai].y : s == 2 ? wcur[ai].z : wcur[ai].w;
-        const bf16x8 afr = dequant_word(word);
+      for (int j = 0; j < 2; j++) {
+        const int bj = 2 * p + j;
 #pragma unroll
-        for (int bj = 0; bj < 4; bj++) tmp[ai][bj] = mfma16(afr, bfr[bj], tmp[ai][bj]);
+        for (int ai = 0; ai < NA; ai++) {
+          f32x4 t = mfma16(xfr[j][0], wfr[ai][0], seed[j]);
+          t = mfma16(xfr[j][1], wfr[ai][1], t);
+          t = mfma16(xfr[j][2], wfr[ai][2], t);
+          t = mfma16(xfr[j][3], wfr[ai][3], t);
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[ai][bj][i] += sc[ai] * t[i];
+        }
       }
     }
+    EXMOE_STAGE_STORE(buf ^ 1);
 #pragma unroll
-    for (int ai = 0; ai < 4; ai++)
-#pragma unroll
-      for (int bj = 0; bj < 4; bj++) scale_accum(acc[ai][bj], tmp[ai][bj], scur[ai]);
-    stage_store(buf ^ 1);
-#pragma unroll
-    for (int ai = 0; ai < 4; ai++) {
+    for (int ai = 0; ai < NA; ai++) {
       wcur[ai] = wnext[ai];
       scur[ai] = snext[ai];
     }
     __syncthreads();
   }
+#undef EXMOE_STAGE_LOAD
+#undef EXMOE_STAGE_STORE
 
-  // ---- epilogue
+  // ---- epilogue: lane l holds weight row (l % 16) of each row subtile and tokens
+  // bj*16 + 4(l/16) + i of each token subtile
+  const int tl0 = 4 * (lane >> 4);
   if (GATEUP) {
-    float gpart[4] = {0.f, 0.f, 0.f, 0.f};
+    float gpart[8][4];
 #pragma unroll
-    for (int rbl = 0; rbl < 2; rbl++) {
-      const int col = (rt * 8 + 2 * wr + rbl) * 16 + 4 * (lane >> 4);
+    for (int bj = 0; bj < 8; bj++)
 #pragma unroll
-      for (int bj = 0; bj < 4; bj++) {
+      for (int i = 0; i < 4; i++) gpart[bj][i] = 0.f;
+#pragma unroll
+    for (int rbl = 0; rbl < NA / 2; rbl++) {
+      const int col = (rt * 8 + (NA / 2) * wave + rbl) * 16 + (lane & 15);
+#pragma unroll
+      for (int bj = 0; bj < 8; bj++) {
         const f32x4 gv = acc[2 * rbl][bj], uv = acc[2 * rbl + 1][bj];
-        uint16_t hb[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          hb[i] = f32_to_bf16(gv[i] / (1.0f + expf(-gv[i])) * uv[i]);
-          gpart[bj] += bf16_to_f32(hb[i]);
-        }
-        const int r = pt.tok0 + wt * 64 + bj * 16 + (lane & 15);
-        if (r < pt.cnt) {
-          uint2 pk;
-          pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-          pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-          *reinterpret_cast<uint2*>(a.h + (size_t)(pt.seg0 + r) * a.I + col) = pk;
+          const uint16_t hb = f32_to_bf16(gv[i] / (1.0f + expf(-gv[i])) * uv[i]);
+          gpart[bj][i] += bf16_to_f32(hb);
+          const int r = pt.tok0 + bj * 16 + tl0 + i;
+          if (r < pt.cnt) a.h[(size_t)(pt.seg0 + r) * a.I + col] = hb;
         }
       }
     }
-    // per-token sum over this workgroup's 128 intermediate columns (one down group)
+    // per-token sum over this workgroup's 128 intermediate columns (one down group):
+    // the 16 lanes of a row hold 16 columns each
 #pragma unroll
-    for (int bj = 0; bj < 4; bj++) {
-      float v = gpart[bj];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (lane < 16) s_gsum[wr][wt * 64 + bj * 16 + lane] = v;
-    }
+    for (int bj = 0; bj < 8; bj++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float v = gpart[bj][i];
+        v += __uint_as_float(dpp_u32<0x121>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x122>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+        if ((lane & 15) == 0) s_gsum[wave][bj * 16 + tl0 + i] = v;
+      }
     __syncthreads();
     if (tid < kPfBN) {
       const int r = pt.tok0 + tid;
       if (r < pt.cnt) {
-        const float v = ((s_gsum[0][tid] + s_gsum[1][tid]) + s_gsum[2][tid]) + s_gsum[3][tid];
-        a.gsum[(size_t)(pt.seg0 + r) * (a.I / kGroup) + rt] = v;
+        float v = s_gsum[0][tid];
+#pragma unroll
+        for (int w = 1; w < NW; w++) v += s_gsum[w][tid];
+        a.gsum[(size_t)rt * rows_pad + pt.seg0 + r] = -136.0f * v;
       }
     }
   } else {
 #pragma unroll
-    for (int bj = 0; bj < 4; bj++) {
-      const int r = pt.tok0 + wt * 64 + bj * 16 + (lane & 15);
-      if (r < pt.cnt) {
-        const int f = a.sorted_flat[pt.seg0 + r];     // y_perm rows are in flat (token, slot) order
-        const float wgt = a.w[f];
+    for (int bj = 0; bj < 8; bj++)
 #pragma unroll
-        for (int ai = 0; ai < 4; ai++) {
-          if (!rvalid[ai]) continue;
-          const int col = (rt * 16 + 4 * wr + ai) * 16 + 4 * (lane >> 4);
-          const f32x4 o = acc[ai][bj];
-          *reinterpret_cast<float4*>(a.y_perm + (size_t)f * a.H + col) =
-              make_float4(o[0] * wgt, o[1] * wgt, o[2] * wgt, o[3] * wgt);
+      for (int i = 0; i < 4; i++) {
+        const int r = pt.tok0 + bj * 16 + tl0 + i;
+        if (r < pt.cnt) {
+          const int f = a.sorted_flat[pt.seg0 + r];     // y_perm rows are in flat (token, slot) order
+          const float wgt = a.w[f];
+#pragma unroll
+          for (int ai = 0; ai < NA; ai++) {
+            if (!rvalid[ai]) continue;
+            const int col = (rt * 16 + NA * wave + ai) * 16 + (lane & 15);
+            a.y_perm[(size_t)f * a.H + col] = acc[ai][bj][i] * wgt;
+          }
         }
       }
-    }
   }
 }
 
-// Group sums of x in fp32 (one wave per token row of 128-wide groups): xsum[t, g].
-__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                   float* __restrict__ xsum) {
+// Correction seeds of the gate/up kernel: xsum[g][r] = -136 * (sum over group g of the
+// activations of sorted row r's token), fp32, one thread per (row, group); rows past T*k
+// (padding read by partial tiles) are zero.
+__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x,
+                                                   const int32_t* __restrict__ sorted_flat, int TK,
+                                                   int k, int H, int rows_pad, float* __restrict__ xsum) {
   const int G = H / kGroup;
-  const int i = blockIdx.x * 256 + threadIdx.x;     // one (token, group) per thread
-  if (i >= T * G) return;
-  const int t = i / G, g = i % G;
-  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + g * kGroup);
+  const int i = blockIdx.x * 256 + threadIdx.x;     // one (group, row) per thread
+  if (i >= G * rows_pad) return;
+  const int g = i / rows_pad, r = i % rows_pad;
   float s = 0.f;
+  if (r < TK) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)(sorted_flat[r] / k) * H + g * kGroup);
 #pragma unroll 4
-  for (int c = 0; c < kGroup / 8; c++) {
-    const uint4 v = p[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int c = 0; c < kGroup / 8; c++) {
+      const uint4 v = p[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 4; q++) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
+      for (int q = 0; q < 4; q++) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
+    }
   }
-  xsum[i] = s;
+  xsum[i] = -136.0f * s;
 }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
   const int TK = a.T * a.k;
   const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
   const int G = a.H / kGroup;
+  const int rows_pad = TK + kPfBN;
   {
     ProfScope prof("xsum", s);
-    hipLaunchKernelGGL(xsum_kernel, dim3((a.T * G + 255) / 256), dim3(256), 0, s, a.x, a.T, a.H, a.xsum);
+    hipLaunchKernelGGL(xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
+                       a.H, rows_pad, a.xsum);
   }
   const int rt_gu = a.I / 128;
   {
     ProfScope prof("prefill_gateup", s);
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(max_tt * rt_gu), dim3(kPfThreads), 0, s, a, -1, rt_gu);
+    hipLaunchKernelGGL((prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, a, -1,
+                       rt_gu);
   }
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
   {
     ProfScope prof("prefill_down", s);
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(max_tt * rt_d), dim3(kPfThreads), 0, s, a, -1, rt_d);
+    hipLaunchKernelGGL((prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, a, -1,
+                       rt_d);
   }
   return launch_combine(a, s);
 }
