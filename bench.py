@@ -51,8 +51,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "large"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache"], default=None,
                     help="run a single workload (for profiling)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB three times (traffic-counter calibration)")
     return ap.parse_args()
 
 
@@ -79,7 +81,7 @@ def build_olmoe(exm, torch, rotate):
     banks = [bank0] + [exm.ExpertBank(base=bank0.base.clone(), stride=bank0.stride) for _ in range(rotate - 1)]
     torch.cuda.synchronize()
     log(f"built OLMoE-shaped layer: {rotate} bank copies of {bank0.base.numel() / 1e6:.1f} MB in {time.time() - t0:.1f}s")
-    return lay, banks
+    return lay, banks, blobs
 
 
 def bytes_per_call(exm, torch, lay_syn, shape, wr, xs_dev, T, bias=None):
@@ -91,14 +93,14 @@ def bytes_per_call(exm, torch, lay_syn, shape, wr, xs_dev, T, bias=None):
     return np.array(D)
 
 
-def time_layer(exm, torch, wl, steps, warmup, use_graph):
+def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0):
     shape = wl.shape
-    bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k)
+    bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k, flags)
     wr = wl.layer["wr"]
 
     def step(i):
         exm.moe_layer(wl.xs[i % len(wl.xs)], wr, wl.banks[i % len(wl.banks)], shape.I, shape.k, bias=wl.bias,
-                      buffers=bufs)
+                      flags=flags, buffers=bufs)
 
     for i in range(warmup):
         step(i)
@@ -189,6 +191,7 @@ def main():
         sys.exit(2)
     import torch
     import w4a16_mixture_experts_amd as exm
+    from w4a16_mixture_experts_amd.profiling import read_traffic
     from synthetic import OLMOE, LARGE, SyntheticLayer
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
@@ -201,8 +204,19 @@ def main():
     use_graph = not args.no_graph
 
     olmoe_syn = banks = None
-    if args.only in (None, "decode", "prefill"):
-        olmoe_syn, banks = build_olmoe(exm, torch, args.rotate)
+    if args.calib_copy_mib:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            exm.device_copy(dst, src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {nb} bytes")
+        del src, dst
+
+    if args.only in (None, "decode", "prefill", "cache"):
+        olmoe_syn, banks, olmoe_blobs = build_olmoe(exm, torch, args.rotate)
         wr = to_dev_bf16(olmoe_syn.router())
 
     # ------------------------------------------------------------------ decode (headline)
@@ -222,10 +236,14 @@ def main():
             rec["kernel_us"] = {n: v[0] * 1e3 for n, v in kt.items()}
             ms_gu = kt["decode_gateup"][0]
             gu_alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2
+            tr = read_traffic(os.path.join(ROOT, "profiles", f"traffic_decode_gateup_olmoe_decode_T{T}.txt"),
+                              "decode_gateup_kernel")
             rec["roofline"] = {"bound": "hbm", "achieved": gu_alg / (ms_gu * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": gu_alg / (ms_gu * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "traffic": None, "kernel": "decode_gateup_kernel",
+                               "traffic": None if tr is None else tr["bytes"], "kernel": "decode_gateup_kernel",
                                "algorithmic_bytes_per_launch": gu_alg, "avg_launch_us": ms_gu * 1e3}
+            if tr is not None:
+                rec["roofline"]["traffic_over_algorithmic"] = tr["bytes"] / gu_alg
             if "decode_down" in kt:
                 ms_d = kt["decode_down"][0]
                 d_alg = D.mean() * down_bytes + T * k * I * 2 + 2 * T * k * H * 4 + T * H * 2
@@ -235,13 +253,101 @@ def main():
             f"layer {rec['layer_hbm_gbs']:.0f} GB/s ({rec['layer_hbm_frac'] * 100:.1f}% of HBM)")
         return rec
 
+    def run_sequential(T, steps, warmup):
+        """Fused layer vs the per-expert sequential W4 path, both launched eagerly (the
+        sequential path reads the segment offsets back to the host, so it cannot be captured)."""
+        xs = [to_dev_bf16(olmoe_syn.x(T, stream=s)) for s in range(64)]
+        wl = Workload(f"olmoe_decode_T{T}", OLMOE, T, {"wr": wr}, banks, xs)
+        fused = time_layer(exm, torch, wl, steps, warmup, False)
+        seq = time_layer(exm, torch, wl, steps, warmup, False, flags=exm.PATH_SEQUENTIAL)
+        log(f"decode T={T} eager: fused {fused * 1e3:.1f} us, sequential {seq * 1e3:.1f} us, ratio {seq / fused:.2f}")
+        return {"T": T, "fused_eager_us": fused * 1e3, "sequential_eager_us": seq * 1e3,
+                "fused_over_sequential_speedup": seq / fused}
+
     if args.only in (None, "decode"):
         head = run_decode(args.tokens, args.steps, args.warmup, True)
         result["head"] = head
         if not args.no_secondary and args.only is None:
+            secondary["olmoe_decode_T16_fused_vs_sequential"] = run_sequential(16, 64, 8)
+        if not args.no_secondary and args.only is None:
             for T in (1, 4, 16):
                 if T != args.tokens:
                     secondary[f"olmoe_decode_T{T}"] = run_decode(T, args.steps, args.warmup, True)
+
+    # ------------------------------------------------------------------ slot cache (decode through 16 layers)
+    def run_slot_cache(slots_list, layers=16, steps=128):
+        """Batch-1 decode through a stack of `layers` OLMoE-shaped layers whose experts sit in a
+        pinned host pool behind `slots` GPU slots per layer (LRU). The routing of each
+        (step, layer) comes from a Zipf(1.1) popularity trace with temporal reuse 0.5; the
+        first `steps` steps of the trace warm the cache, the next `steps` are timed. Every
+        layer shares one set of expert values (values do not change bytes moved or time);
+        the routing differs per layer."""
+        from synthetic import slot_cache_trace
+        trace = slot_cache_trace(E, k, layers, 2 * steps, seed=0)
+        ids_dev = torch.from_numpy(trace.reshape(2 * steps, layers, 1, k)).cuda()
+        xs = [to_dev_bf16(olmoe_syn.x(1, stream=5000 + st)) for st in range(2 * steps)]
+        # pinned-host -> device copy rate of one packed expert, for reference
+        pin = torch.empty(expert_bytes, dtype=torch.uint8).pin_memory()
+        dev = torch.empty(expert_bytes, dtype=torch.uint8, device="cuda")
+        for _ in range(4):
+            dev.copy_(pin, non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for _ in range(64):
+            dev.copy_(pin, non_blocking=True)
+        torch.cuda.synchronize()
+        h2d_gbs = 64 * expert_bytes / (time.time() - t0) / 1e9
+        del pin, dev
+        out = {}
+        for S in slots_list:
+            cache = exm.SlotCache(layers, E, S, expert_bytes)
+            for l in range(layers):
+                for e in range(E):
+                    cache.fill(l, e, olmoe_blobs[e])
+            if S == E:
+                cache.preload()
+
+            def run(lo, hi):
+                for st in range(lo, hi):
+                    x = xs[st]
+                    for l in range(layers):
+                        ids = ids_dev[st, l]
+                        logits, _, _ = exm.route_topk(x, wr, k)
+                        w = exm.route_weights(logits, ids)
+                        off, sf, fs = exm.group_tokens(ids, E)
+                        bank = cache.acquire(l, sorted(int(e) for e in trace[st, l]))
+                        exm.moe_forward(x, ids, w, off, sf, fs, bank, I)
+
+            cache.reset_stats()
+            torch.cuda.synchronize()
+            t0 = time.time()
+            run(0, steps)
+            torch.cuda.synchronize()
+            cold_s = time.time() - t0
+            cold = cache.stats()
+            cache.reset_stats()
+            t0 = time.time()
+            run(steps, 2 * steps)
+            torch.cuda.synchronize()
+            warm_s = time.time() - t0
+            st = cache.stats()
+            cache.close()
+            rec = {"slots": S, "layers": layers, "steps": steps, "tokens_per_s": steps / warm_s,
+                   "ms_per_token": warm_s / steps * 1e3, "resident": bool(st["resident"]),
+                   "lookups": st["lookups"], "hits": st["hits"], "misses": st["misses"],
+                   "evictions": st["evictions"], "hit_rate": st["hits"] / max(st["lookups"], 1),
+                   "h2d_bytes": st["h2d_bytes"], "h2d_gb_per_token": st["h2d_bytes"] / steps / 1e9,
+                   "h2d_gbs_achieved": st["h2d_bytes"] / warm_s / 1e9, "h2d_gbs_pinned_copy": h2d_gbs,
+                   "device_bytes": st["device_bytes"], "pinned_host_bytes": st["pinned_host_bytes"],
+                   "cold": {"tokens_per_s": steps / cold_s, "hit_rate": cold["hits"] / max(cold["lookups"], 1),
+                            "misses": cold["misses"], "h2d_bytes": cold["h2d_bytes"]}}
+            log(f"slot cache S={S}: {rec['tokens_per_s']:.1f} tok/s through {layers} layers, hit rate "
+                f"{rec['hit_rate'] * 100:.1f}%, H2D {st['h2d_bytes'] / 1e9:.2f} GB over {steps} steps")
+            out[f"slot_cache_S{S}"] = rec
+        return out
+
+    if not args.no_secondary and args.only in (None, "cache"):
+        secondary.update(run_slot_cache([8, 16, 32, 64]))
 
     # ------------------------------------------------------------------ prefill lines
     def run_prefill(name, shape, syn, banks_p, wr_p, T, bias, steps, warmup):

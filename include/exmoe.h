@@ -231,8 +231,9 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 
 /* ------------------------------------------------------------------------------------
  * Per-kernel timing for benchmarks (not part of the layer's semantics). While enabled,
- * each kernel launch of the library is bracketed by a hipEvent pair on its launch stream
- * (skipped on a stream that is being captured into a graph). exmoe_profile_read
+ * each kernel of the library is launched with a hipEvent pair that stamps that kernel's
+ * own start and end on its launch stream (hipExtLaunchKernelGGL; skipped on a stream that
+ * is being captured into a graph). exmoe_profile_read
  * synchronizes the recorded events and returns the accumulated milliseconds and launch
  * count of one kernel by name: "route_logits", "topk", "group", "decode_gateup",
  * "decode_down", "combine", "xsum", "prefill_gateup", "prefill_down". Process-global.
@@ -240,6 +241,12 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 int exmoe_profile_enable(int on);
 int exmoe_profile_reset(void);
 int exmoe_profile_read(const char* kernel_name, double* total_ms, uint64_t* launches);
+
+/* Plain device copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned),
+ * one pass of 16-byte loads and stores, asynchronous on `stream`. Not part of the layer:
+ * it is the kernel of known HBM traffic (bytes read + bytes written) against which the
+ * hardware traffic counters are calibrated. Kernel name in traces: exmoe::copy_kernel. */
+int exmoe_device_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libexmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libexmoe.so is not built ({LIB_PATH}); run python w4a16_mixture_experts_amd/build_lib.py")
+# torch ships its own HIP runtime under the SONAME libamdhip64.so.7 but links it by the
+# name libamdhip64.so. Loading torch first makes this library bind to that same runtime;
+# loaded the other way round, the process would hold two HIP runtimes, and a kernel
+# launched from one does not see the device the other initialised.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes (exmoe.h)
@@ -78,6 +86,7 @@ _SIGS = {
     "exmoe_profile_enable": (_i, [_i]),
     "exmoe_profile_reset": (_i, []),
     "exmoe_profile_read": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]),
+    "exmoe_device_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -359,3 +368,11 @@ def profile_read(kernel: str):
     n = ctypes.c_uint64(0)
     _check(_lib.exmoe_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def device_copy(dst, src):
+    """Plain device copy of src into dst (same byte size, multiple of 16) on the current stream."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("device_copy: size mismatch")
+    _check(_lib.exmoe_device_copy(_vp(dst.data_ptr()), _vp(src.data_ptr()), n, _stream()))

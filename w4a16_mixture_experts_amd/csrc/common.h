@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -34,19 +35,38 @@ int hip_error(hipError_t e, const char* what);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Event pair around one kernel launch when profiling is enabled (exmoe_profile_enable).
+// Per-kernel timing for benchmarks (exmoe_profile_enable). While profiling is on and the
+// stream is not being captured, the scope holds an event pair that EXMOE_LAUNCH hands to
+// hipExtLaunchKernelGGL, which stamps the kernel's own start and end; otherwise
+// EXMOE_LAUNCH is a plain launch.
 class ProfScope {
  public:
   ProfScope(const char* name, hipStream_t s);
   ~ProfScope();
   ProfScope(const ProfScope&) = delete;
   ProfScope& operator=(const ProfScope&) = delete;
+  bool timing() const { return a_ != nullptr && b_ != nullptr; }
+  hipEvent_t start() const { return a_; }
+  hipEvent_t stop() const { return b_; }
+  void used() { used_ = true; }
 
  private:
   const char* name_;
   hipStream_t s_;
   hipEvent_t a_ = nullptr, b_ = nullptr;
+  bool used_ = false;
 };
+
+#define EXMOE_LAUNCH(prof, kernel, grid, block, shmem, stream, ...)                                     \
+  do {                                                                                                 \
+    if ((prof).timing()) {                                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (prof).start(), (prof).stop(), 0,      \
+                            __VA_ARGS__);                                                              \
+      (prof).used();                                                                                   \
+    } else {                                                                                           \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                             \
+    }                                                                                                  \
+  } while (0)
 
 // ---- kernel launchers (defined in the .hip files); each returns a HIP error code
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_flat,
                         int32_t* flat_to_sorted, hipStream_t s) {
   ProfScope prof("group", s);
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), 0, s, ids, T * k, E, offsets,
+  EXMOE_LAUNCH(prof, group_kernel, dim3(1), dim3(kGroupThreads), 0, s, ids, T * k, E, offsets,
                      sorted_flat, flat_to_sorted);
   return hipGetLastError();
 }

@@ -380,24 +380,24 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecRoute& rt, in
     const bool split = items_gu < kDecSplitBelow;
     if (rt.logits) {
       if (!split)
-        hipLaunchKernelGGL((decode_gateup_kernel<1, true>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
+        EXMOE_LAUNCH(prof, (decode_gateup_kernel<1, true>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
       else
-        hipLaunchKernelGGL((decode_gateup_kernel<4, true>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
+        EXMOE_LAUNCH(prof, (decode_gateup_kernel<4, true>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
     } else {
       if (!split)
-        hipLaunchKernelGGL((decode_gateup_kernel<1, false>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
+        EXMOE_LAUNCH(prof, (decode_gateup_kernel<1, false>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
       else
-        hipLaunchKernelGGL((decode_gateup_kernel<4, false>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
+        EXMOE_LAUNCH(prof, (decode_gateup_kernel<4, false>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
     }
   }
   const int items_d = ny * (a.H / kTileRows);
   {
     ProfScope prof("decode_down", s);
     if (items_d >= kDecSplitBelow)
-      hipLaunchKernelGGL(decode_down_kernel<1>, dim3((items_d + kDecWaves - 1) / kDecWaves), dim3(kDecThreads), 0,
+      EXMOE_LAUNCH(prof, decode_down_kernel<1>, dim3((items_d + kDecWaves - 1) / kDecWaves), dim3(kDecThreads), 0,
                          s, a, fixed_expert);
     else
-      hipLaunchKernelGGL(decode_down_kernel<4>, dim3(items_d), dim3(kDecThreads), 0, s, a, fixed_expert);
+      EXMOE_LAUNCH(prof, decode_down_kernel<4>, dim3(items_d), dim3(kDecThreads), 0, s, a, fixed_expert);
   }
   return hipGetLastError();
 }
@@ -433,7 +433,7 @@ hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipSt
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   ProfScope prof("combine", s);
-  hipLaunchKernelGGL(combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, a);
+  EXMOE_LAUNCH(prof, combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -344,19 +344,19 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
   const int rows_pad = TK + kPfBN;
   {
     ProfScope prof("xsum", s);
-    hipLaunchKernelGGL(xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
+    EXMOE_LAUNCH(prof, xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
                        a.H, rows_pad, a.xsum);
   }
   const int rt_gu = a.I / 128;
   {
     ProfScope prof("prefill_gateup", s);
-    hipLaunchKernelGGL((prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, a, -1,
+    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, a, -1,
                        rt_gu);
   }
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
   {
     ProfScope prof("prefill_down", s);
-    hipLaunchKernelGGL((prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, a, -1,
+    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, a, -1,
                        rt_d);
   }
   return launch_combine(a, s);

@@ -1,7 +1,7 @@
-// Optional per-kernel event timing for benchmarks: when enabled, every kernel launch of the
-// library is bracketed by a hipEvent pair on its launch stream; exmoe_profile_read
-// synchronizes those events and returns per-kernel totals. Off by default; never active
-// while a stream is being captured into a graph.
+// Optional per-kernel timing for benchmarks: when enabled, every kernel of the library is
+// launched with a hipEvent pair that stamps the kernel's own start and end on its launch
+// stream (hipExtLaunchKernelGGL); exmoe_profile_read synchronizes those events and returns
+// per-kernel totals. Off by default; never active while a stream is being captured.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -53,14 +53,22 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), s_(s) {
   if (!g_on || capturing(s)) return;
   a_ = take_event();
   b_ = take_event();
-  if (a_ && b_) (void)hipEventRecord(a_, s);
+  if (!a_ || !b_) {
+    if (a_) g_free.push_back(a_);
+    if (b_) g_free.push_back(b_);
+    a_ = b_ = nullptr;
+  }
 }
 
 ProfScope::~ProfScope() {
   if (!a_ || !b_) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  (void)hipEventRecord(b_, s_);
-  g_pending.push_back({name_, a_, b_});
+  if (used_) {
+    g_pending.push_back({name_, a_, b_});
+  } else {
+    g_free.push_back(a_);
+    g_free.push_back(b_);
+  }
 }
 
 }  // namespace exmoe

@@ -145,10 +145,10 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (T <= 64) {
     // one wave per 2 tokens x 2 experts, the whole wave on H
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
-    hipLaunchKernelGGL((route_logits_kernel<2, 2, 64>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
+    EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
   } else {
     const int blocks = ((T + 3) / 4) * ((E + 3) / 4);
-    hipLaunchKernelGGL((route_logits_kernel<4, 4, 16>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T, H, E,
+    EXMOE_LAUNCH(prof, (route_logits_kernel<4, 4, 16>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T, H, E,
                        logits);
   }
   return hipGetLastError();
@@ -163,7 +163,7 @@ hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int re
     return launch_group(ids, T, k, E, offsets, sorted_flat, flat_to_sorted, s);
   }
   ProfScope prof("topk_group", s);
-  hipLaunchKernelGGL(topk_group_kernel, dim3(1), dim3(kTopkGroupThreads), 0, s, logits, T, E, k, renormalize, ids, w,
+  EXMOE_LAUNCH(prof, topk_group_kernel, dim3(1), dim3(kTopkGroupThreads), 0, s, logits, T, E, k, renormalize, ids, w,
                      offsets, sorted_flat, flat_to_sorted);
   return hipGetLastError();
 }
@@ -172,7 +172,7 @@ hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, 
                        int renormalize, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   ProfScope prof("topk", s);
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, given_ids, T, E, k,
+  EXMOE_LAUNCH(prof, topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, given_ids, T, E, k,
                      renormalize, ids, w);
   return hipGetLastError();
 }

@@ -1,0 +1,28 @@
+// Plain device copy: the kernel of known traffic used to calibrate HBM byte counters.
+#include "common.h"
+
+namespace exmoe {
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace exmoe
+
+using namespace exmoe;
+
+extern "C" int exmoe_device_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (!dst || !src) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "exmoe_device_copy: NULL pointer");
+  if (bytes % 16 || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "exmoe_device_copy: size and pointers must be 16-byte multiples");
+  if (bytes == 0) return EXMOE_OK;
+  const size_t n = bytes / 16;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  ProfScope prof("copy", stream);
+  EXMOE_LAUNCH(prof, copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
+               static_cast<uint4*>(dst), n);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? EXMOE_OK : hip_error(e, "copy_kernel launch");
+}

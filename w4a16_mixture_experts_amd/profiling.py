@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Summaries of rocprofv3 output for the library's kernels (standard library only).
+
+    python3 w4a16_mixture_experts_amd/profiling.py stats  DIR --cmd "..." --out FILE
+    python3 w4a16_mixture_experts_amd/profiling.py traffic --kernel decode_gateup_kernel \\
+        --fetch DIR --write DIR --copy-bytes N --cmd "..." --out FILE
+
+`stats` turns a `rocprofv3 --kernel-trace --stats` run into a per-kernel table (calls,
+average, median, min, max and total duration). `traffic` turns two `rocprofv3 --pmc`
+runs, one of FETCH_SIZE and one of WRITE_SIZE (KiB per dispatch), into HBM bytes per
+launch of one kernel. Each counter is scaled by the ratio between the known traffic of
+`exmoe::copy_kernel` (N bytes read and N bytes written per dispatch, N larger than the
+on-package caches) and what the same counter reads for that copy in the same run. The
+traffic file records a hash of the kernel's sources; `read_traffic` returns nothing once
+the sources have changed since the counters were taken.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sqlite3
+import statistics
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# Sources each profiled kernel is compiled from.
+KERNEL_SOURCES = {
+    "decode_gateup_kernel": ["moe_decode.hip", "device.h", "common.h", "group_block.h", "topk.h"],
+    "decode_down_kernel": ["moe_decode.hip", "device.h", "common.h", "group_block.h", "topk.h"],
+    "prefill_kernel": ["moe_prefill.hip", "device.h", "common.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name.split("(")[0].replace("void ", "").strip()
+    return n.replace("exmoe::", "")
+
+
+def _csv_rows(d: str, suffix: str):
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            yield from csv.DictReader(fh)
+
+
+def _grid(r) -> str:
+    if "Grid_Size_X" in r:
+        g = [int(r["Grid_Size_" + a]) for a in "XYZ"]
+        w = [int(r.get("Workgroup_Size_" + a, 1) or 1) for a in "XYZ"]
+        return "x".join(str(gi // max(wi, 1)) for gi, wi in zip(g, w) if gi > 0) + f" wg{w[0] * w[1] * w[2]}"
+    return str(r.get("Grid_Size", "?"))
+
+
+def kernel_durations(d: str) -> dict[tuple[str, str], list[float]]:
+    """(kernel name, launch grid in workgroups) -> durations in microseconds, from a
+    kernel-trace run."""
+    out: dict[tuple[str, str], list[float]] = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        out.setdefault((short_name(r["Kernel_Name"]), _grid(r)), []).append(us)
+    if out:
+        return out
+    for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(db)
+        for name, st, en in con.execute("select name, start, end from kernels"):
+            out.setdefault((short_name(name), "?"), []).append((en - st) / 1000.0)
+    return out
+
+
+def dispatch_counters(d: str, counter: str) -> dict[str, list[float]]:
+    """Kernel name -> per-dispatch values of one counter, from a --pmc run."""
+    per: dict[tuple[str, str], float] = {}
+    rows = list(_csv_rows(d, "counter_collection.csv"))
+    if rows:
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = (short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    else:
+        for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+            con = sqlite3.connect(db)
+            q = "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?"
+            for name, did, val in con.execute(q, (counter,)):
+                key = (short_name(name), str(did))
+                per[key] = per.get(key, 0.0) + float(val)
+    out: dict[str, list[float]] = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _ours(name: str) -> bool:
+    return name.split("<")[0] in ("route_logits_kernel", "topk_kernel", "topk_group_kernel", "group_kernel",
+                                  "decode_gateup_kernel", "decode_down_kernel", "combine_kernel", "xsum_kernel",
+                                  "prefill_kernel", "copy_kernel")
+
+
+def _match(values: dict[str, list[float]], kernel: str) -> list[float]:
+    got = []
+    for name, v in values.items():
+        base = name.split("<")[0]
+        if base == kernel:
+            got += v
+    return got
+
+
+def cmd_stats(args):
+    durs = kernel_durations(args.dir)
+    lines = [f"# rocprofv3 kernel-trace summary: {args.title}", f"# command: {args.cmd}",
+             "# one row per (kernel, launch grid in workgroups x workgroup size); durations in",
+             "# microseconds per launch; library kernels first, then the rest", "",
+             f"{'kernel':44s} {'grid':>16s} {'calls':>7s} {'avg':>9s} {'median':>9s} {'min':>9s} {'max':>9s} "
+             f"{'total_ms':>9s}"]
+    order = sorted(durs.items(), key=lambda kv: (not _ours(kv[0][0]), -sum(kv[1])))
+    for (name, grid), v in order:
+        v = sorted(v)
+        lines.append(f"{name[:44]:44s} {grid:>16s} {len(v):7d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} "
+                     f"{v[0]:9.2f} {v[-1]:9.2f} {sum(v) / 1e3:9.3f}")
+    text = "\n".join(lines) + "\n"
+    _emit(text, args.out)
+
+
+def cmd_traffic(args):
+    fetch = dispatch_counters(args.fetch, "FETCH_SIZE")
+    write = dispatch_counters(args.write, "WRITE_SIZE")
+    kf, kw = _match(fetch, args.kernel), _match(write, args.kernel)
+    cf, cw = _match(fetch, "copy_kernel"), _match(write, "copy_kernel")
+    if not (kf and kw and cf and cw):
+        sys.exit(f"missing dispatches: kernel fetch {len(kf)} write {len(kw)}, copy fetch {len(cf)} write {len(cw)}")
+    copy_kib = args.copy_bytes / 1024.0
+    f_fac = copy_kib / statistics.median(cf)
+    w_fac = copy_kib / statistics.median(cw)
+    fk, wk = statistics.mean(kf), statistics.mean(kw)
+    traffic = (fk * f_fac + wk * w_fac) * 1024.0
+    lines = [f"# HBM traffic per launch of exmoe::{args.kernel}: {args.title}",
+             f"# fetch command: {args.cmd_fetch or args.cmd}",
+             f"# write command: {args.cmd_write or args.cmd}",
+             "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by",
+             "# (known copy bytes) / (counter reading of exmoe::copy_kernel in the same run).",
+             f"kernel: {args.kernel}",
+             f"source_sha256: {source_hash(args.kernel)}",
+             f"dispatches_fetch: {len(kf)}",
+             f"dispatches_write: {len(kw)}",
+             f"fetch_kib_per_dispatch_raw: {fk:.1f}",
+             f"write_kib_per_dispatch_raw: {wk:.1f}",
+             f"copy_bytes: {args.copy_bytes}",
+             f"copy_fetch_kib_raw: {statistics.median(cf):.1f}",
+             f"copy_write_kib_raw: {statistics.median(cw):.1f}",
+             f"fetch_factor: {f_fac:.4f}",
+             f"write_factor: {w_fac:.4f}",
+             f"traffic_bytes_per_launch: {traffic:.0f}"]
+    _emit("\n".join(lines) + "\n", args.out)
+
+
+def cmd_counters(args):
+    lines = [f"# rocprofv3 --pmc per-dispatch means: {args.title}", f"# command: {args.cmd}", ""]
+    for c in args.counter:
+        vals = dispatch_counters(args.dir, c)
+        for name, v in sorted(vals.items()):
+            if _ours(name):
+                lines.append(f"{name[:44]:44s} {c:28s} dispatches={len(v):5d} mean={statistics.mean(v):.6g}")
+    _emit("\n".join(lines) + "\n", args.out)
+
+
+def read_traffic(path: str, kernel: str):
+    """HBM bytes per launch recorded in a traffic file, or None when the file is missing or
+    the kernel's sources have changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("kernel") != kernel or kv.get("source_sha256") != source_hash(kernel):
+        return None
+    return {"bytes": float(kv["traffic_bytes_per_launch"]), "fetch_factor": float(kv["fetch_factor"]),
+            "write_factor": float(kv["write_factor"]), "source_sha256": kv["source_sha256"]}
+
+
+def _emit(text: str, out: str | None):
+    if out:
+        os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+        with open(out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--title", default="")
+    a.add_argument("--out")
+    b = sub.add_parser("traffic")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--cmd", default="")
+    b.add_argument("--cmd-fetch", default="")
+    b.add_argument("--cmd-write", default="")
+    b.add_argument("--title", default="")
+    b.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--counter", action="append", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--out")
+    args = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.what](args)
+
+
+if __name__ == "__main__":
+    main()
