@@ -246,7 +246,7 @@ def main():
                 rec["roofline"]["traffic_over_algorithmic"] = tr["bytes"] / gu_alg
             if "decode_down" in kt:
                 ms_d = kt["decode_down"][0]
-                d_alg = D.mean() * down_bytes + T * k * I * 2 + 2 * T * k * H * 4 + T * H * 2
+                d_alg = D.mean() * down_bytes + T * k * I * 2 + T * k * H * 4 + T * k * 4
                 rec["down_kernel"] = {"achieved_gbs": d_alg / (ms_d * 1e-3) / 1e9, "avg_launch_us": ms_d * 1e3,
                                       "algorithmic_bytes_per_launch": d_alg}
         log(f"decode T={T}: {rec['tokens_per_s']:.0f} tok/s, {rec['us_per_layer']:.2f} us/layer, "
