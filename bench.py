@@ -232,7 +232,7 @@ def main():
                "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if want_kernels:
             kt = kernel_times(exm, torch, wl, min(steps, 256),
-                              ["route_logits", "topk", "group", "topk_group", "decode_gateup", "decode_down", "combine"])
+                              ["route_logits", "route_token", "topk", "group", "topk_group", "decode_gateup", "decode_down", "combine"])
             rec["kernel_us"] = {n: v[0] * 1e3 for n, v in kt.items()}
             ms_gu = kt["decode_gateup"][0]
             gu_alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2

@@ -475,17 +475,20 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
   if (!workspace || ws_bytes < need)
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
-  if (choose_path(T, E, k, flags) == EXMOE_PATH_DECODE && decode_fused_routing_ok(T, k)) {
+  if (choose_path(T, E, k, flags) == EXMOE_PATH_DECODE && (long long)T * k <= kDecMaxRows) {
+    // Decode sizes: one workgroup per token routes it; the gate/up kernel groups the rows
+    // from the ids and publishes the grouping.
     MoeArgs a{};
     a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
     a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
     a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
     moe_workspace_layout(T, H, I, E, k, EXMOE_PATH_DECODE, &a, workspace);
-    EXMOE_HIP(launch_moe_decode_fused(a, logits, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
-                                      flat_to_sorted, stream));
+    EXMOE_HIP(launch_route_token(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids, topk_weights,
+                                 stream));
+    EXMOE_HIP(launch_moe_decode_from_ids(a, expert_offsets, sorted_flat, flat_to_sorted, stream));
     return EXMOE_OK;
   }
+  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
   EXMOE_HIP(launch_topk_group(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
                               flat_to_sorted, stream));
   return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,

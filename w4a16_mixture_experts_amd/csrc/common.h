@@ -101,13 +101,18 @@ struct MoeArgs {
 };
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);
+// Routed rows up to which the decode kernels group the rows themselves from the top-k ids.
+constexpr int kDecMaxRows = 1024;
+// Decode path from offsets and permutation given by the caller.
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s);
-bool decode_fused_routing_ok(int T, int k);
-// Decode path with the top-k selection and grouping redone inside the gate/up kernel; the
-// routing outputs are published to the given buffers (a.offsets etc. must alias them).
-hipError_t launch_moe_decode_fused(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
-                                   float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
-                                   hipStream_t s);
+// Logits, top-k selection and routing weights of each token by one workgroup per token.
+hipError_t launch_route_token(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
+                              int k, int renormalize, uint16_t* logits, int32_t* ids, float* w, hipStream_t s);
+// Decode path from the top-k ids alone (T * k <= kDecMaxRows): the gate/up kernel groups
+// the routed rows itself and publishes the grouping to offsets / sorted_flat /
+// flat_to_sorted, which a.offsets and a.sorted_flat must alias.
+hipError_t launch_moe_decode_from_ids(const MoeArgs& a, int32_t* offsets, int32_t* sorted_flat,
+                                      int32_t* flat_to_sorted, hipStream_t s);
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);

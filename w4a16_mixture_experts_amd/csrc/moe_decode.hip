@@ -1,347 +1,410 @@
 // Decode-sized expert layer (a few tokens per expert), gfx950.
 //
 // Every selected expert runs (ExactMoE abstract; Fig. 1). With a handful of tokens per
-// expert the layer is bound by streaming the packed int4 weights from HBM, so these
-// kernels are laid out for bandwidth and short dependency chains:
-//  * a workgroup owns one active expert and a slice of output rows; each wave streams
-//    whole 1 KiB tiles (one wave-wide 128-bit load each) in chunks of two 128-input
-//    groups, double-buffered in registers, with the activation fragments of the same
-//    groups issued alongside, so loads stay in flight while the previous chunk computes;
-//  * the tokens of the expert (padded to 16) ride in the N dimension of
-//    v_mfma_f32_16x16x32_bf16; more than 16 tokens loop over 16-token tiles;
-//  * when few workgroups would exist (batch-1 decode), the four waves split the
-//    reduction dimension instead of the rows and add their partial sums through LDS.
+// expert the layer is bound by streaming the packed int4 weights from HBM, so the expert
+// kernels are laid out for bandwidth:
+//  * a workgroup (8 waves) owns one active expert and a slice of output rows; each wave
+//    streams whole 1 KiB tiles (one wave-wide 128-bit load each), two tiles per 128-input
+//    group, kDecRing groups ahead in registers;
+//  * the expert's tokens (up to 16 per pass) are staged once per workgroup in LDS and
+//    ride in the N dimension of v_mfma_f32_16x16x32_bf16; the activation operand comes
+//    from LDS (rows skewed by 16 bytes, so the 16 token rows hit distinct banks);
+//  * when too few workgroups would exist (batch 1-4), KS waves split the reduction
+//    dimension of each row block and add their partial sums through LDS.
 // Dequantization is exact: a packed word becomes bf16 operands 128 + u (u = q + 8) with
-// two bitwise ops per pair; an MFMA chain of the constant -136 against the same
-// activation fragments seeds each group's accumulator with -136 * sum(x), so each group
-// chain ends at sum(x * q); the bf16 row scale is applied once per group in fp32.
+// two bitwise ops per pair; each group's accumulator is seeded with -136 * (sum of that
+// group's activations of the token), computed in the workgroup from the staged rows, so
+// the chain ends at sum(x * q); the bf16 row scale is applied once per group in fp32.
 //
-// Kernel 1 (gate/up): h = bf16(silu(W_gate x) * (W_up x)). In the whole-layer call it
-//   also redoes the top-k selection and grouping of the (few) tokens from the bf16 logits
-//   in every workgroup -- a microsecond of ALU instead of another launch -- and
-//   workgroup (0, 0) publishes that routing for the following kernels.
-// Kernel 2 (down): o = W_down h, times the routing weight, into y_perm (fp32).
-// Kernel 3 (combine): y[t] = bf16(sum over slots j in order of y_perm[row(t, j)]).
+// Kernel 1 (gate/up): h = bf16(silu(W_gate x) * (W_up x)), rows in expert-grouped order.
+//   In the whole-layer call it groups the routed rows itself from the top-k ids (a
+//   histogram, scan and ballot over at most kDecMaxRows rows in LDS) and publishes the
+//   grouping: the first workgroup of each expert writes its segment of the permutation,
+//   workgroup 0 the offsets.
+// Kernel 2 (down): o = W_down h, times the routing weight, into y_perm (flat order, fp32).
+// Kernel 3 (combine): y[t] = bf16(sum over slots j in order of y_perm[t k + j]).
 // Workgroups never wait on each other: a device-scope release costs a serialized L2
-// write-back on this chip, far more than a kernel boundary inside a graph.
+// write-back on this chip, more than a kernel boundary inside a graph.
 #include "common.h"
 #include "device.h"
-#include "group_block.h"
-#include "topk.h"
 
 namespace exmoe {
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / 64;
-// Below this many (expert, 16-row block) items the four waves of a workgroup share one
-// item and split its reduction dimension (more waves in flight for batch-1 decode).
-constexpr int kDecSplitBelow = 1024;
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecTok = 16;                  // tokens per pass: the MFMA N dimension
+constexpr int kDecKC = 2048;                 // reduction columns staged in LDS at a time
+constexpr int kDecKG = kDecKC / kGroup;      // 128-input groups per staged chunk
+constexpr int kDecXS = kDecKC + 8;           // LDS row stride (bf16): 16-byte skew per row
+constexpr int kDecRing = 4;                  // weight groups in flight per wave
 
-struct Frag4 {
-  bf16x8 s[4];
-};
 
-// -136 * (sum of the group's activations) in the C layout (lane l: token l % 16).
-__device__ __forceinline__ f32x4 corr_chain(const Frag4& act) {
-  const bf16x8 n136 = neg136_operand();
-  f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; s++) c = mfma16(n136, act.s[s], c);
-  return c;
-}
-
-// sum_k x_k q_k over one tile for rows 4(l/16)+i, token l%16.
-__device__ __forceinline__ f32x4 tile_chain(uint4 words, const Frag4& act, f32x4 corr) {
-  f32x4 c = corr;
-  c = mfma16(dequant_word(words.x), act.s[0], c);
-  c = mfma16(dequant_word(words.y), act.s[1], c);
-  c = mfma16(dequant_word(words.z), act.s[2], c);
-  c = mfma16(dequant_word(words.w), act.s[3], c);
-  return c;
-}
-
-// Routing state shared by a workgroup.
-constexpr int kDecMaxRows = 1024;   // T*k routed rows handled by the in-kernel routing
-struct DecShared {
-  int32_t offsets[kMaxExperts + 1];
+// In the routing set-up the staging area holds the ids; afterwards the staged rows, and at
+// the end of a pass the partial-sum reduction. Row kDecTok stays zero: token slots past
+// the expert's rows read it.
+struct DecLDS {
+  uint16_t xs[(kDecTok + 1) * kDecXS];       // staged activation rows + one zero row
+  float seed[(kDecTok + 1) * kDecKG];        // -136 * group sums of the staged rows (+ zeros)
+  int32_t cnt[kMaxExperts];
+  int32_t off[kMaxExperts + 1];
   int32_t act[kMaxExperts];
+  int32_t rows[kDecMaxRows];                 // flat indices of this expert's rows (grouped here)
+  int32_t pf[kDecTok];                       // flat indices of the current pass (-1: padding)
   int32_t n_act;
 };
-struct DecFusedShared {          // only in the variant that redoes the routing
-  int32_t ids[kDecMaxRows];
-  float w[kDecMaxRows];
-  int32_t sorted[kDecMaxRows];
-  int32_t f2s[kDecMaxRows];
-  GroupSharedT<kDecThreads> gs;
-};
 
-template <bool F>
-struct FusedSlot {
-  DecFusedShared v;
-  __device__ DecFusedShared* ptr() { return &v; }
-};
-template <>
-struct FusedSlot<false> {
-  int unused;
-  __device__ DecFusedShared* ptr() { return nullptr; }
-};
-
-struct DecRoute {
-  const uint16_t* logits;   // non-NULL: recompute top-k + grouping in every workgroup
-  int renormalize;
-  int32_t* ids_out;         // published by workgroup (0, 0)
-  float* w_out;
-  int32_t* offsets_out;
-  int32_t* sorted_out;
-  int32_t* f2s_out;
-};
-
-// Fills sh.offsets / sh.act / sh.n_act (and, in fused mode, the routing arrays). Returns
-// the sorted_flat pointer to use (LDS copy in fused mode, caller's array otherwise).
-__device__ const int32_t* dec_routing(const MoeArgs& a, const DecRoute& rt, int fixed_expert, DecShared& sh,
-                                     DecFusedShared* fs) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* sorted = a.sorted_flat;
-  if (fs) {
-    DecFusedShared& f = *fs;
-    for (int t = wave; t < a.T; t += kDecWaves) {
-      int id;
-      float wt;
-      topk_token(rt.logits + (size_t)t * a.E, nullptr, a.E, a.k, rt.renormalize, id, wt);
-      if (lane < a.k) {
-        f.ids[t * a.k + lane] = id;
-        f.w[t * a.k + lane] = wt;
-      }
-    }
-    __syncthreads();
-    group_block<kDecThreads>(f.ids, a.T * a.k, a.E, sh.offsets, f.sorted, f.f2s, f.gs);
-    __syncthreads();
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
-      const int n = a.T * a.k;
-      for (int i = tid; i < n; i += kDecThreads) {
-        rt.ids_out[i] = f.ids[i];
-        rt.w_out[i] = f.w[i];
-        rt.sorted_out[i] = f.sorted[i];
-        rt.f2s_out[i] = f.f2s[i];
-      }
-      for (int i = tid; i <= a.E; i += kDecThreads) rt.offsets_out[i] = sh.offsets[i];
-    }
-    sorted = f.sorted;
-  } else {
-    for (int i = tid; i <= a.E; i += kDecThreads) sh.offsets[i] = a.offsets[i];
-    __syncthreads();
-  }
-  if (wave == 0) {
-    if (fixed_expert >= 0) {
-      if (lane == 0) {
-        sh.act[0] = fixed_expert;
-        sh.n_act = 1;
-      }
-    } else {
-      int base = 0;
-      for (int c0 = 0; c0 < a.E; c0 += 64) {
-        const int e = c0 + lane;
-        const bool on = e < a.E && sh.offsets[e + 1] > sh.offsets[e];
-        const uint64_t m = __ballot(on);
-        if (on) sh.act[base + __popcll(m & ((1ull << lane) - 1ull))] = e;
-        base += __popcll(m);
-      }
-      if (lane == 0) sh.n_act = base;
-    }
-  }
-  __syncthreads();
-  return sorted;
-}
-
-struct ExpertRef {
+struct DecExpert {
   int e, seg0, cnt;
   const uint4* tiles;
   const uint16_t* scales;
 };
 
-__device__ __forceinline__ bool dec_expert(const MoeArgs& a, const DecShared& sh, int idx, ExpertRef& r) {
-  if (idx >= sh.n_act) return false;
-  r.e = sh.act[idx];
-  r.seg0 = sh.offsets[r.e];
-  r.cnt = sh.offsets[r.e + 1] - r.seg0;
-  if (r.cnt <= 0) return false;
-  const int slot = a.e2s ? a.e2s[r.e] : r.e;
+// Routing source of the gate/up kernel. kSrcGiven: offsets and permutation come from the
+// caller. kSrcIds: top-k ids given; the rows are grouped here and the grouping published
+// to the pointers below for the kernels that follow.
+constexpr int kSrcGiven = 0, kSrcIds = 1;
+struct DecPublish {
+  int32_t* offsets;
+  int32_t* sorted_flat;
+  int32_t* flat_to_sorted;
+};
+
+// The routing inputs of the set-up (ids or offsets), loaded into registers as the kernel's
+// very first loads: a wave's vector loads complete in issue order, so these must not
+// queue behind the weight prefetch. Unconditional loads at clamped indices.
+constexpr int kDecPre = kDecMaxRows / kDecThreads;   // ids <= 2 * 512, offsets <= 257
+struct DecPre {
+  int32_t v[kDecPre];
+};
+template <int SRC>
+__device__ __forceinline__ DecPre dec_preload(const MoeArgs& a) {
+  DecPre pr;
+  const int tid = threadIdx.x;
+  const int n = SRC == kSrcIds ? a.T * a.k : a.E + 1;
+#pragma unroll
+  for (int m = 0; m < kDecPre; m++) {
+    int i = tid + m * kDecThreads;
+    i = i < n ? i : n - 1;
+    pr.v[m] = SRC == kSrcIds ? a.ids[i] : a.offsets[i];
+  }
+  return pr;
+}
+
+template <int SRC, bool ALL>
+__device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, const DecPre& pr, int fixed_expert,
+                          int aidx, bool first_of_expert, int slot_known, DecExpert& ex) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int TK = a.T * a.k;
+  int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);
+  if (SRC == kSrcIds) {
+#pragma unroll
+    for (int m = 0; m < kDecPre; m++)
+      if (tid + m * kDecThreads < TK) ids_l[tid + m * kDecThreads] = pr.v[m];
+  }
+  if (SRC != kSrcGiven) {
+    for (int i = tid; i < a.E; i += kDecThreads) L.cnt[i] = 0;
+    __syncthreads();
+    for (int f = tid; f < TK; f += kDecThreads) {
+      const int e = ids_l[f];
+      if ((unsigned)e < (unsigned)a.E) atomicAdd(&L.cnt[e], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 < a.E; c0 += 64) {
+        const int e = c0 + lane;
+        const int v = e < a.E ? L.cnt[e] : 0;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(incl, d);
+          if (lane >= d) incl += u;
+        }
+        if (e < a.E) L.off[e] = base + incl - v;
+        base += __shfl(incl, 63);
+      }
+      if (lane == 0) L.off[a.E] = base;
+    }
+  } else {
+    if (tid <= a.E) L.off[tid] = pr.v[0];
+  }
+  __syncthreads();
+  if (!ALL && wave == 0) {
+    if (fixed_expert >= 0) {
+      if (lane == 0) {
+        L.act[0] = fixed_expert;
+        L.n_act = 1;
+      }
+    } else {
+      int base = 0;
+      for (int c0 = 0; c0 < a.E; c0 += 64) {
+        const int e = c0 + lane;
+        const bool on = e < a.E && L.off[e + 1] > L.off[e];
+        const uint64_t m = __ballot(on);
+        if (on) L.act[base + __popcll(m & ((1ull << lane) - 1ull))] = e;
+        base += __popcll(m);
+      }
+      if (lane == 0) L.n_act = base;
+    }
+  }
+  __syncthreads();
+  if (!ALL && aidx >= L.n_act) return false;
+  // uniform values: keep them (and the addresses built from them) in scalar registers
+  ex.e = ALL ? aidx : __builtin_amdgcn_readfirstlane(L.act[aidx]);
+  ex.seg0 = __builtin_amdgcn_readfirstlane(L.off[ex.e]);
+  ex.cnt = __builtin_amdgcn_readfirstlane(L.off[ex.e + 1]) - ex.seg0;
+  if (SRC != kSrcGiven) {
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 < TK; c0 += 64) {
+        const int f = c0 + lane;
+        const bool on = f < TK && ids_l[f] == ex.e;
+        const uint64_t m = __ballot(on);
+        if (on) L.rows[base + __popcll(m & ((1ull << lane) - 1ull))] = f;
+        base += __popcll(m);
+      }
+    }
+    __syncthreads();
+    if (first_of_expert) {
+      for (int r = tid; r < ex.cnt; r += kDecThreads) {
+        const int f = L.rows[r];
+        pub.sorted_flat[ex.seg0 + r] = f;
+        pub.flat_to_sorted[f] = ex.seg0 + r;
+      }
+    }
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= a.E; i += kDecThreads) pub.offsets[i] = L.off[i];
+  }
+  if (ex.cnt <= 0) return false;
+  const int slot = ALL ? slot_known : a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[ex.e]) : ex.e;
   if (slot < 0) {
-    if (threadIdx.x == 0) atomicOr(a.debug, 1u);   // routed expert without a slot
+    if (tid == 0) atomicOr(a.debug, 1u);   // routed expert without a slot
     return false;
   }
   const uint8_t* blob = a.base + a.stride * (size_t)slot;
-  r.tiles = reinterpret_cast<const uint4*>(blob);
-  r.scales = reinterpret_cast<const uint16_t*>(blob + n_tiles(a.H, a.I) * kTileBytes);
+  ex.tiles = reinterpret_cast<const uint4*>(blob);
+  ex.scales = reinterpret_cast<const uint16_t*>(blob + n_tiles(a.H, a.I) * kTileBytes);
   return true;
 }
 
-// ------------------------------------------------------------------------------------
-// Streaming core. One wave owns one (expert, 16-row block) item and walks its 128-input
-// groups g = g0, g0 + gstep, ...: NM packed tiles per group (2 = gate and up, 1 = down)
-// with their scales from HBM, kept kWRing groups ahead in registers, and the activation
-// fragments of the same groups from L2 (the expert's token rows; padding lanes read the
-// zero row), kept kXRing groups ahead. Loads are unconditional (indices past the end
-// repeat the last group), so the compiler can count them and keep them in flight.
-// ------------------------------------------------------------------------------------
-constexpr int kWRing = 4;
-constexpr int kXRing = 2;
-template <int NM>
-struct WSlot {
-  uint4 w[NM];
-  uint2 s[NM];
+struct WSlot2 {
+  uint4 w[2];
+  uint2 s[2];
 };
 
-// Padding token slots read this all-zero row (device globals start zeroed; never written).
-__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kMaxDim];
-
-__device__ __forceinline__ Frag4 load_act(const uint16_t* row_ptr, int col0) {
-  Frag4 f;
+// ------------------------------------------------------------------------------------
+// One kernel body for both projections. GATEUP: wave row = one 16-row block of I, its
+// gate and up tiles; reduction over H. DOWN: wave row = two 16-row blocks of H; reduction
+// over I. Workgroup = (active expert, chunk of output rows); KS waves per wave row split
+// the groups of each staged chunk (g = kpart, kpart + KS, ...).
+// ------------------------------------------------------------------------------------
+template <bool GATEUP, int SRC, int KS, bool ALL>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a, DecPublish pub, int fixed_expert,
+                                                                    int nchunk) {
+  __shared__ DecLDS L;
   const int lane = (int)lane_id();
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const uint4 u = *reinterpret_cast<const uint4*>(row_ptr + col0 + 32 * s + 8 * (lane >> 4));
-    i32x4 v = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
-    f.s[s] = __builtin_bit_cast(bf16x8, v);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int aidx = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+
+  constexpr int RBW = kDecWaves / KS;           // wave rows per workgroup
+  constexpr int PER = kDecKG / KS;              // groups of a staged chunk per wave
+  const int wrow = wave / KS, kpart = wave % KS;
+  const int K = GATEUP ? a.H : a.I;
+  const int G = K / kGroup;
+  const int nK = (K + kDecKC - 1) / kDecKC;
+  int rb0, rb1;
+  bool live0, live1;
+  size_t t0, t1;
+  if (GATEUP) {
+    rb0 = chunk * RBW + wrow;
+    rb1 = rb0;
+    live0 = live1 = rb0 < a.I / kTileRows;
+    const int rbc = live0 ? rb0 : a.I / kTileRows - 1;
+    t0 = (size_t)(rbc * 2) * G;
+    t1 = (size_t)(rbc * 2 + 1) * G;
+  } else {
+    const int nrb = a.H / kTileRows;
+    rb0 = (chunk * RBW + wrow) * 2;
+    rb1 = rb0 + 1;
+    live0 = rb0 < nrb;
+    live1 = rb1 < nrb;
+    const size_t dbase = 2 * (size_t)(a.I / kTileRows) * (a.H / kGroup);
+    t0 = dbase + (size_t)(live0 ? rb0 : nrb - 1) * G;
+    t1 = dbase + (size_t)(live1 ? rb1 : nrb - 1) * G;
   }
-  return f;
-}
-
-template <int NM, typename F>
-__device__ __forceinline__ void stream_groups(const uint4* tiles, const uint16_t* scales, const size_t* tbase,
-                                              int g0, int gstep, int ngroups, const uint16_t* xrow, F&& consume) {
-  const int lane = (int)lane_id();
-  auto gidx = [&](int i) { return g0 + (i < ngroups ? i : ngroups - 1) * gstep; };
-  auto issue_w = [&](int i, WSlot<NM>& w) {
-    const int g = gidx(i);
-#pragma unroll
-    for (int m = 0; m < NM; m++) {
-      const size_t t = tbase[m] + g;
-      w.w[m] = tiles[t * 64 + lane];
-      w.s[m] = *reinterpret_cast<const uint2*>(scales + t * 16 + 4 * (lane >> 4));
-    }
+  // The blob through a buffer resource: uniform byte offsets of the wave's two tile rows
+  // go in scalar registers, the lane's offset in one vector register.
+  const uint32_t sc_base = (uint32_t)(n_tiles(a.H, a.I) * kTileBytes);
+  const int nbytes = (int)packed_bytes(a.H, a.I);
+  const uint32_t lo_t = (uint32_t)lane * 16u, lo_s = (uint32_t)(lane >> 4) * 8u;
+  const uint32_t t0b = (uint32_t)t0 * kTileBytes, t1b = (uint32_t)t1 * kTileBytes;
+  const uint32_t s0b = sc_base + (uint32_t)t0 * kScaleBytes, s1b = sc_base + (uint32_t)t1 * kScaleBytes;
+  // Sequence index s -> group: staged chunk c = s / PER holds ngc groups, split in KS
+  // contiguous runs of pg; positions past a run repeat its last group (cache hits).
+  auto gof = [&](int s) {
+    const int c = s / PER, i = s % PER;
+    const int ngc = G - c * kDecKG < kDecKG ? G - c * kDecKG : kDecKG;
+    const int pg = (ngc + KS - 1) / KS;
+    const int g = c * kDecKG + kpart * pg + (i < pg ? i : pg - 1);
+    return g < G ? (g >= 0 ? g : 0) : G - 1;
   };
-  WSlot<NM> W[kWRing];
-  Frag4 X[kXRing];
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int s, WSlot2& w) {
+    const uint32_t g = (uint32_t)gof(s);
+    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t0b + g * kTileBytes), 0));
+    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t1b + g * kTileBytes), 0));
+    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s0b + g * kScaleBytes), 0));
+    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s1b + g * kScaleBytes), 0));
+  };
+
+  for (int i = tid; i < kDecXS / 8; i += kDecThreads)
+    *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
+
+  const DecPre pre = dec_preload<SRC>(a);
+  // ALL: the grid covers every expert, so the expert (hence its weights) is known at once:
+  // the first ring of weight loads goes out right behind the routing inputs and arrives
+  // while the routing is worked out. Loads through a resource of zero length (expert
+  // without a slot, or no next pass) return zeros without touching memory; issuing them
+  // anyway keeps every wave's load count fixed, so the waits stay exact.
+  WSlot2 W[kDecRing];
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
+  int slot = 0;
+  if (ALL) {
+    slot = a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[aidx]) : aidx;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
+                                             slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < kWRing; j++) issue_w(j, W[j]);
-#pragma unroll
-  for (int j = 0; j < kXRing; j++) X[j] = load_act(xrow, gidx(j) * kGroup);
-  for (int i0 = 0; i0 < ngroups; i0 += kWRing) {
-#pragma unroll
-    for (int j = 0; j < kWRing; j++) {
-      if (i0 + j < ngroups) consume(W[j], X[j % kXRing]);
-      issue_w(i0 + j + kWRing, W[j]);
-      X[j % kXRing] = load_act(xrow, gidx(i0 + j + kXRing) * kGroup);
-    }
+    for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
-}
+  DecExpert ex;
+  if (!dec_setup<SRC, ALL>(a, L, pub, pre, fixed_expert, aidx, chunk == 0, slot, ex)) return;
+  if (!ALL) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
+  }
+  const __amdgpu_buffer_rsrc_t rsrc_none = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, 0, 0x00020000);
 
-// ------------------------------------------------------------------------------------
-// gate/up + SiLU*up.  KSPLIT = 1: each wave owns its own item (expert, row block).
-//                     KSPLIT = 4: the 4 waves of a workgroup share one item and split its
-//                     groups (g = wave mod 4), adding partial sums through LDS.
-// ------------------------------------------------------------------------------------
-template <int KSPLIT, bool FUSED>
-__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(MoeArgs a, DecRoute rt, int fixed_expert) {
-  __shared__ DecShared sh;
-  __shared__ FusedSlot<FUSED> fsh;
-  __shared__ f32x4 red[KSPLIT > 1 ? kDecWaves : 1][2][64];
-  const int lane = (int)lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int32_t* sorted = dec_routing(a, rt, fixed_expert, sh, fsh.ptr());
-  const int nrb = a.I / kTileRows;
-  const int item = KSPLIT == 1 ? (int)blockIdx.x * kDecWaves + wave : (int)blockIdx.x;
-  ExpertRef ex;
-  if (!dec_expert(a, sh, item / nrb, ex)) return;       // uniform per wave (KSPLIT 1) or workgroup
-  const int rb = item % nrb;
-  const int G = a.H / kGroup;
-  const int g0 = KSPLIT == 1 ? 0 : wave;
-  const int ngroups = (G - g0 + KSPLIT - 1) / KSPLIT;
-  const size_t tbase[2] = {(size_t)(rb * 2) * G, (size_t)(rb * 2 + 1) * G};
-  const int n = lane & 15;
-  const int ntt = (ex.cnt + 15) / 16;
+  const int npass = (ex.cnt + kDecTok - 1) / kDecTok;
+  for (int p = 0; p < npass; p++) {
+    const int nrow = ex.cnt - p * kDecTok < kDecTok ? ex.cnt - p * kDecTok : kDecTok;
+    if (GATEUP && tid < kDecTok) {
+      const int r = p * kDecTok + tid;
+      L.pf[tid] = r < ex.cnt ? (SRC != kSrcGiven ? L.rows[r] : a.sorted_flat[ex.seg0 + r]) : -1;
+    }
+    // down: the rows to stage are contiguous in h; the flat index is needed only at the end
+    int f_out = -1;
+    if (!GATEUP && (lane & 15) < nrow) f_out = a.sorted_flat[ex.seg0 + p * kDecTok + (lane & 15)];
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int tt = 0; tt < ntt; tt++) {
-    const int r = tt * 16 + n;
-    const bool valid = r < ex.cnt;
-    const uint16_t* xrow = valid ? a.x + (size_t)(sorted[ex.seg0 + r] / a.k) * a.H : g_zero_row;
-    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    if (ngroups > 0)
-      stream_groups<2>(ex.tiles, ex.scales, tbase, g0, KSPLIT, ngroups, xrow,
-                       [&](const WSlot<2>& w, const Frag4& act) {
-                         const f32x4 corr = corr_chain(act);
-                         scale_accum(accg, tile_chain(w.w[0], act, corr), w.s[0]);
-                         scale_accum(accu, tile_chain(w.w[1], act, corr), w.s[1]);
-                       });
-    if (KSPLIT > 1) {
-      red[wave][0][lane] = accg;
-      red[wave][1][lane] = accu;
-      __syncthreads();
-      if (wave == 0)
-        for (int w = 1; w < kDecWaves; w++) {
-          accg += red[w][0][lane];
-          accu += red[w][1][lane];
+    for (int c = 0; c < nK; c++) {
+      const int kc0 = c * kDecKC;
+      const int kcw = K - kc0 < kDecKC ? K - kc0 : kDecKC;
+      const int ngc = kcw / kGroup;
+      __syncthreads();   // previous chunk consumed; pass row list visible
+      {
+        const int cw8 = kcw / 8;
+        for (int q = tid; q < nrow * cw8; q += kDecThreads) {
+          const int r = q / cw8, c8 = q - r * cw8;
+          const size_t row = GATEUP ? (size_t)(L.pf[r] / a.k) * a.H : (size_t)(ex.seg0 + p * kDecTok + r) * a.I;
+          *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) =
+              *reinterpret_cast<const uint4*>((GATEUP ? a.x : a.h) + row + kc0 + c8 * 8);
         }
-    }
-    if ((KSPLIT == 1 || wave == 0) && valid) {
-      uint16_t hb[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(accg[i] / (1.0f + expf(-accg[i])) * accu[i]);
-      uint2 pk;
-      pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-      pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-      *reinterpret_cast<uint2*>(a.h + (size_t)(ex.seg0 + r) * a.I + rb * 16 + 4 * (lane >> 4)) = pk;
-    }
-    if (KSPLIT > 1) __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------------------------------
-// down (+ routing weight) into y_perm, in flat (token, slot) order so that the combine
-// reads it without an index. Same two layouts as gate/up, rows of H.
-// ------------------------------------------------------------------------------------
-template <int KSPLIT>
-__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(MoeArgs a, int fixed_expert) {
-  __shared__ DecShared sh;
-  __shared__ f32x4 red[KSPLIT > 1 ? kDecWaves : 1][64];
-  const int lane = (int)lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  DecRoute none{};
-  const int32_t* sorted = dec_routing(a, none, fixed_expert, sh, nullptr);
-  const int nrb = a.H / kTileRows;
-  const int item = KSPLIT == 1 ? (int)blockIdx.x * kDecWaves + wave : (int)blockIdx.x;
-  ExpertRef ex;
-  if (!dec_expert(a, sh, item / nrb, ex)) return;
-  const int rb = item % nrb;
-  const int G = a.I / kGroup;
-  const int g0 = KSPLIT == 1 ? 0 : wave;
-  const int ngroups = (G - g0 + KSPLIT - 1) / KSPLIT;
-  const size_t tbase[1] = {2 * (size_t)(a.I / kTileRows) * (a.H / kGroup) + (size_t)rb * G};
-  const int n = lane & 15;
-  const int ntt = (ex.cnt + 15) / 16;
-
-  for (int tt = 0; tt < ntt; tt++) {
-    const int r = tt * 16 + n;
-    const bool valid = r < ex.cnt;
-    const uint16_t* hrow = valid ? a.h + (size_t)(ex.seg0 + r) * a.I : g_zero_row;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (ngroups > 0)
-      stream_groups<1>(ex.tiles, ex.scales, tbase, g0, KSPLIT, ngroups, hrow,
-                       [&](const WSlot<1>& w, const Frag4& act) {
-                         scale_accum(acc, tile_chain(w.w[0], act, corr_chain(act)), w.s[0]);
-                       });
-    if (KSPLIT > 1) {
-      red[wave][lane] = acc;
+      }
       __syncthreads();
-      if (wave == 0)
-        for (int w = 1; w < kDecWaves; w++) acc += red[w][lane];
+      for (int q = tid; q < nrow * ngc * 2; q += kDecThreads) {
+        const int r = q / (ngc * 2), gg = (q >> 1) % ngc, half = q & 1;
+        const uint16_t* src = L.xs + r * kDecXS + gg * kGroup + half * 64;
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * i);
+          const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int m = 0; m < 4; m++) {
+            s += __uint_as_float(q4[m] << 16);
+            s += __uint_as_float(q4[m] & 0xFFFF0000u);
+          }
+        }
+        const float o = __shfl_xor(s, 1);
+        if (!half) L.seed[r * kDecKG + gg] = -136.0f * (s + o);
+      }
+      __syncthreads();
+
+      const int pg = (ngc + KS - 1) / KS;
+      const int myrow = (lane & 15) < nrow ? (lane & 15) : kDecTok;   // padding slots read the zero row
+      const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
+      const float* srow = L.seed + myrow * kDecKG;
+#pragma unroll
+      for (int i0 = 0; i0 < PER; i0 += kDecRing) {
+#pragma unroll
+        for (int j = 0; j < kDecRing; j++) {
+          const int gl = kpart * pg + i0 + j;
+          if (i0 + j < pg && gl < ngc) {
+            bf16x8 act[4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; s4++) act[s4] = *reinterpret_cast<const bf16x8*>(xrow + gl * kGroup + 32 * s4);
+            const float sd = srow[gl];
+            f32x4 c0 = {sd, sd, sd, sd}, c1 = c0;
+            c0 = mfma16(dequant_word(W[j].w[0].x), act[0], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].x), act[0], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].y), act[1], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].y), act[1], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].z), act[2], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].z), act[2], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].w), act[3], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].w), act[3], c1);
+            scale_accum(acc0, c0, W[j].s[0]);
+            scale_accum(acc1, c1, W[j].s[1]);
+          }
+          // past this pass's last group the ring runs on into the next pass (the same
+          // groups again); after the last pass it loads nothing
+          const int sn = c * PER + i0 + j + kDecRing, wrap = sn >= nK * PER;
+          issue(wrap ? (p + 1 < npass ? rsrc : rsrc_none) : rsrc, wrap ? sn - nK * PER : sn, W[j]);
+        }
+      }
     }
-    if ((KSPLIT == 1 || wave == 0) && valid) {
-      const int f = sorted[ex.seg0 + r];
-      const float wt = a.w[f];
-      *reinterpret_cast<float4*>(a.y_perm + (size_t)f * a.H + rb * 16 + 4 * (lane >> 4)) =
-          make_float4(acc[0] * wt, acc[1] * wt, acc[2] * wt, acc[3] * wt);
+
+    if (KS > 1) {
+      __syncthreads();   // every wave done with the staged rows: reuse them for partial sums
+      f32x4* red = reinterpret_cast<f32x4*>(L.xs);
+      red[(wave * 2 + 0) * 64 + lane] = acc0;
+      red[(wave * 2 + 1) * 64 + lane] = acc1;
+      __syncthreads();
+      if (kpart == 0) {
+#pragma unroll
+        for (int kp = 1; kp < KS; kp++) {
+          acc0 += red[((wave + kp) * 2 + 0) * 64 + lane];
+          acc1 += red[((wave + kp) * 2 + 1) * 64 + lane];
+        }
+      }
     }
-    if (KSPLIT > 1) __syncthreads();
+    if (kpart == 0) {
+      const int r = lane & 15;
+      const int f = GATEUP ? L.pf[r] : f_out;
+      if (f >= 0) {
+        if (GATEUP) {
+          if (live0) {
+            uint16_t hb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(acc0[i] / (1.0f + expf(-acc0[i])) * acc1[i]);
+            uint2 pk;
+            pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+            pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+            *reinterpret_cast<uint2*>(a.h + (size_t)(ex.seg0 + p * kDecTok + r) * a.I + rb0 * 16 + 4 * (lane >> 4)) = pk;
+          }
+        } else {
+          const float wt = a.w[f];
+          float* yrow = a.y_perm + (size_t)f * a.H + 4 * (lane >> 4);
+          if (live0)
+            *reinterpret_cast<float4*>(yrow + rb0 * 16) = make_float4(acc0[0] * wt, acc0[1] * wt, acc0[2] * wt, acc0[3] * wt);
+          if (live1)
+            *reinterpret_cast<float4*>(yrow + rb1 * 16) = make_float4(acc1[0] * wt, acc1[1] * wt, acc1[2] * wt, acc1[3] * wt);
+        }
+      }
+    }
+    __syncthreads();   // pass row list and reduction space free for the next pass
   }
 }
 
@@ -370,64 +433,73 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
-static hipError_t launch_decode_experts(const MoeArgs& a, const DecRoute& rt, int fixed_expert, int ny,
+// Smallest reduction split that gives the launch enough workgroups to cover the chip.
+static int pick_ks(int wgs_at_ks1) {
+  int ks = 1;
+  while (ks < 4 && wgs_at_ks1 * ks < 320) ks *= 2;
+  return ks;
+}
+
+template <bool GATEUP, int SRC>
+static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& pub, int fixed_expert, int ny,
+                          hipStream_t s) {
+  // workgroups per expert at KS = 1: gate/up 8 row blocks of I each; down 16 row blocks of H
+  const int per1 = GATEUP ? a.I / (kTileRows * kDecWaves) : (a.H / kTileRows + 2 * kDecWaves - 1) / (2 * kDecWaves);
+  const dim3 block(kDecThreads);
+  if (fixed_expert < 0 && (long long)a.T * a.k >= 2LL * a.E) {
+    // most experts active: one row of workgroups per expert (no active-expert list)
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, true>), dim3(a.E * per1), block, 0, s, a, pub,
+                 fixed_expert, per1);
+    return;
+  }
+  const int ks = pick_ks(ny * per1);
+  const int nchunk = per1 * ks;
+  const dim3 grid(ny * nchunk);
+  if (ks == 1)
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+  else if (ks == 2)
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 2, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+  else
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+}
+
+static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub, int fixed_expert, int ny,
                                         hipStream_t s) {
-  // ny = upper bound of active experts; items = (active expert, 16-row block)
-  const int items_gu = ny * (a.I / kTileRows);
   {
     ProfScope prof("decode_gateup", s);
-    const dim3 g1((items_gu + kDecWaves - 1) / kDecWaves), g4(items_gu);
-    const bool split = items_gu < kDecSplitBelow;
-    if (rt.logits) {
-      if (!split)
-        EXMOE_LAUNCH(prof, (decode_gateup_kernel<1, true>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
-      else
-        EXMOE_LAUNCH(prof, (decode_gateup_kernel<4, true>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
-    } else {
-      if (!split)
-        EXMOE_LAUNCH(prof, (decode_gateup_kernel<1, false>), g1, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
-      else
-        EXMOE_LAUNCH(prof, (decode_gateup_kernel<4, false>), g4, dim3(kDecThreads), 0, s, a, rt, fixed_expert);
-    }
+    if (pub)
+      launch_expert<true, kSrcIds>(prof, a, *pub, fixed_expert, ny, s);
+    else
+      launch_expert<true, kSrcGiven>(prof, a, DecPublish{}, fixed_expert, ny, s);
   }
-  const int items_d = ny * (a.H / kTileRows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     ProfScope prof("decode_down", s);
-    if (items_d >= kDecSplitBelow)
-      EXMOE_LAUNCH(prof, decode_down_kernel<1>, dim3((items_d + kDecWaves - 1) / kDecWaves), dim3(kDecThreads), 0,
-                         s, a, fixed_expert);
-    else
-      EXMOE_LAUNCH(prof, decode_down_kernel<4>, dim3(items_d), dim3(kDecThreads), 0, s, a, fixed_expert);
+    launch_expert<false, kSrcGiven>(prof, a, DecPublish{}, fixed_expert, ny, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
-  DecRoute none{};
-  hipError_t e = launch_decode_experts(a, none, -1, ny, s);
+  hipError_t e = launch_decode_experts(a, nullptr, -1, ny, s);
   if (e != hipSuccess) return e;
   return launch_combine(a, s);
 }
 
-// Redoing the routing in every gate/up workgroup beats a separate top-k launch only when
-// there are very few tokens (measured: batch 1 and 2).
-bool decode_fused_routing_ok(int T, int k) { return T <= 2 && T * k <= kDecMaxRows; }
-
-hipError_t launch_moe_decode_fused(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
-                                   float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
-                                   hipStream_t s) {
+hipError_t launch_moe_decode_from_ids(const MoeArgs& a, int32_t* offsets, int32_t* sorted_flat,
+                                      int32_t* flat_to_sorted, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
-  DecRoute rt{logits, renormalize, ids, w, offsets, sorted_flat, flat_to_sorted};
-  hipError_t e = launch_decode_experts(a, rt, -1, ny, s);
+  const DecPublish pub{offsets, sorted_flat, flat_to_sorted};
+  hipError_t e = launch_decode_experts(a, &pub, -1, ny, s);
   if (e != hipSuccess) return e;
   return launch_combine(a, s);
 }
 
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s) {
   (void)rows;
-  DecRoute none{};
-  return launch_decode_experts(a, none, expert, 1, s);
+  return launch_decode_experts(a, nullptr, expert, 1, s);
 }
 
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {

@@ -19,7 +19,7 @@ namespace exmoe {
 // when LANES = 64); one lane rounds once to bf16. Few tokens: LANES = 64, small blocks,
 // many waves. Many tokens: LANES = 16, 4 x 4 blocks for operand reuse.
 // ---------------------------------------------------------------------------------
-template <int TB, int EB, int LANES>
+template <int TB, int EB, int LANES, int MC>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias, int T,
@@ -38,36 +38,54 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
     for (int j = 0; j < EB; j++) acc[i][j] = 0.0;
   if (t0 < T) {
     const int chunks = H / 8;
-    for (int c = li; c < chunks; c += LANES) {
-      double xv[TB][8], wv[EB][8];
+    // MC chunks per lane are loaded before any arithmetic: one memory latency per piece
+    for (int c0 = 0; c0 < chunks; c0 += LANES * MC) {
+      uint4 xu[TB][MC], wu[EB][MC];
 #pragma unroll
-      for (int i = 0; i < TB; i++) {
-        const int t = t0 + i < T ? t0 + i : T - 1;
-        const uint4 u = reinterpret_cast<const uint4*>(x + (size_t)t * H)[c];
-        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+      for (int m = 0; m < MC; m++) {
+        int c = c0 + li + LANES * m;
+        c = c < chunks ? c : chunks - 1;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          xv[i][2 * q] = (double)__uint_as_float(q4[q] << 16);
-          xv[i][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+        for (int i = 0; i < TB; i++) {
+          const int t = t0 + i < T ? t0 + i : T - 1;
+          xu[i][m] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[c];
+        }
+#pragma unroll
+        for (int j = 0; j < EB; j++) {
+          const int e = e0 + j < E ? e0 + j : E - 1;
+          wu[j][m] = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
         }
       }
 #pragma unroll
-      for (int j = 0; j < EB; j++) {
-        const int e = e0 + j < E ? e0 + j : E - 1;
-        const uint4 u = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
-        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+      for (int m = 0; m < MC; m++) {
+        if (c0 + li + LANES * m < chunks) {
+          double xv[TB][8], wv[EB][8];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          wv[j][2 * q] = (double)__uint_as_float(q4[q] << 16);
-          wv[j][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+          for (int i = 0; i < TB; i++) {
+            const uint32_t q4[4] = {xu[i][m].x, xu[i][m].y, xu[i][m].z, xu[i][m].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              xv[i][2 * q] = (double)__uint_as_float(q4[q] << 16);
+              xv[i][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < EB; j++) {
+            const uint32_t q4[4] = {wu[j][m].x, wu[j][m].y, wu[j][m].z, wu[j][m].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              wv[j][2 * q] = (double)__uint_as_float(q4[q] << 16);
+              wv[j][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < TB; i++)
+#pragma unroll
+            for (int j = 0; j < EB; j++)
+#pragma unroll
+              for (int q = 0; q < 8; q++) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < TB; i++)
-#pragma unroll
-        for (int j = 0; j < EB; j++)
-#pragma unroll
-          for (int q = 0; q < 8; q++) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
     }
   }
 #pragma unroll
@@ -138,6 +156,109 @@ __global__ __launch_bounds__(kTopkGroupThreads) void topk_group_kernel(const uin
   group_block<kTopkGroupThreads>(s_ids, T * k, E, offsets, sorted_flat, flat_to_sorted, gs);
 }
 
+
+// ---------------------------------------------------------------------------------
+// Whole routing of one token by one workgroup (decode sizes): its E logits with the
+// same per-lane arithmetic as route_logits_kernel<.., .., 64, ..> (lanes split H in
+// interleaved 16-byte chunks, ascending; fp64 partials added by DPP row sums and a
+// fixed-order readlane combine), then the top-k selection and the weights from the bf16
+// logits kept in LDS. Each wave takes 4 experts at a time and issues all loads of a
+// 2048-column piece (the token's chunks and the 4 router rows) before the first FMA, so
+// a piece costs one memory latency.
+// ---------------------------------------------------------------------------------
+constexpr int kRouteTokThreads = 1024;
+constexpr int kRouteTokEB = 4;     // experts per wave at a time
+constexpr int kRouteTokMC = 4;     // 16-byte chunks per lane per 2048-column piece
+__global__ __launch_bounds__(kRouteTokThreads) void route_token_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ wr,
+                                                                       const float* __restrict__ bias, int H, int E,
+                                                                       int k, int renormalize,
+                                                                       uint16_t* __restrict__ logits,
+                                                                       int32_t* __restrict__ ids,
+                                                                       float* __restrict__ w) {
+  __shared__ uint16_t s_log[kMaxExperts];
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  const int chunks = H / 8;
+  constexpr int EB = kRouteTokEB, MC = kRouteTokMC;
+  for (int e0 = wave * EB; e0 < E; e0 += EB * (kRouteTokThreads / 64)) {
+    double acc[EB];
+#pragma unroll
+    for (int j = 0; j < EB; j++) acc[j] = 0.0;
+    for (int c0 = 0; c0 < chunks; c0 += 64 * MC) {
+      uint4 xu[MC], wu[EB][MC];
+#pragma unroll
+      for (int m = 0; m < MC; m++) {
+        int c = c0 + lane + 64 * m;
+        c = c < chunks ? c : chunks - 1;
+        xu[m] = xr[c];
+#pragma unroll
+        for (int j = 0; j < EB; j++) {
+          const int e = e0 + j < E ? e0 + j : E - 1;
+          wu[j][m] = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MC; m++) {
+        if (c0 + lane + 64 * m < chunks) {
+          const uint32_t xq[4] = {xu[m].x, xu[m].y, xu[m].z, xu[m].w};
+          double xv[8];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            xv[2 * q] = (double)__uint_as_float(xq[q] << 16);
+            xv[2 * q + 1] = (double)__uint_as_float(xq[q] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int j = 0; j < EB; j++) {
+            const uint32_t q4[4] = {wu[j][m].x, wu[j][m].y, wu[j][m].z, wu[j][m].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              acc[j] = fma(xv[2 * q], (double)__uint_as_float(q4[q] << 16), acc[j]);
+              acc[j] = fma(xv[2 * q + 1], (double)__uint_as_float(q4[q] & 0xFFFF0000u), acc[j]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EB; j++) {
+      const double s16 = row16_sum_f64(acc[j]);
+      const long long b = __double_as_longlong(s16);
+      const int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+      double r[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        r[q] = __longlong_as_double(((long long)(unsigned)__builtin_amdgcn_readlane(lo, 16 * q)) |
+                                    ((long long)__builtin_amdgcn_readlane(hi, 16 * q) << 32));
+      const double sum = ((r[0] + r[1]) + r[2]) + r[3];
+      const int e = e0 + j;
+      if (lane == 0 && e < E) s_log[e] = f64_to_bf16(bias ? sum + (double)bias[e] : sum);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kRouteTokThreads) logits[(size_t)t * E + i] = s_log[i];
+  if (wave == 0) {
+    int id;
+    float wt;
+    topk_token(s_log, nullptr, E, k, renormalize, id, wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+    }
+  }
+}
+
+hipError_t launch_route_token(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
+                              int k, int renormalize, uint16_t* logits, int32_t* ids, float* w, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  ProfScope prof("route_token", s);
+  EXMOE_LAUNCH(prof, route_token_kernel, dim3(T), dim3(kRouteTokThreads), 0, s, x, wr, bias, H, E, k, renormalize,
+               logits, ids, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
@@ -145,10 +266,10 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (T <= 64) {
     // one wave per 2 tokens x 2 experts, the whole wave on H
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
-    EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
+    EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
   } else {
     const int blocks = ((T + 3) / 4) * ((E + 3) / 4);
-    EXMOE_LAUNCH(prof, (route_logits_kernel<4, 4, 16>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T, H, E,
+    EXMOE_LAUNCH(prof, (route_logits_kernel<4, 4, 16, 2>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T, H, E,
                        logits);
   }
   return hipGetLastError();
