@@ -232,18 +232,24 @@ def main():
                "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if want_kernels:
             kt = kernel_times(exm, torch, wl, min(steps, 256),
-                              ["route_logits", "route_token", "topk", "group", "topk_group", "decode_gateup", "decode_down", "combine"])
+                              ["route_logits", "route_token", "topk", "group", "topk_group", "decode_gateup", "decode_down", "decode_fused", "combine"])
             rec["kernel_us"] = {n: v[0] * 1e3 for n, v in kt.items()}
-            ms_gu = kt["decode_gateup"][0]
-            gu_alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2
-            tr = read_traffic(os.path.join(ROOT, "profiles", f"traffic_decode_gateup_olmoe_decode_T{T}.txt"),
-                              "decode_gateup_kernel")
-            rec["roofline"] = {"bound": "hbm", "achieved": gu_alg / (ms_gu * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": gu_alg / (ms_gu * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "traffic": None if tr is None else tr["bytes"], "kernel": "decode_gateup_kernel",
-                               "algorithmic_bytes_per_launch": gu_alg, "avg_launch_us": ms_gu * 1e3}
+            if "decode_fused" in kt:
+                # gate/up and down in one kernel: weights of every active expert, x in,
+                # one fp32 output row per routed row
+                kname, ms_k = "decode_fused_kernel", kt["decode_fused"][0]
+                alg = D.mean() * expert_bytes + T * H * 2 + T * k * H * 4
+            else:
+                kname, ms_k = "decode_expert_kernel", kt["decode_gateup"][0]   # its gate/up instance
+                alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2
+            tr = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{kname.replace('_kernel', '')}_olmoe_decode_T{T}.txt"),
+                              kname)
+            rec["roofline"] = {"bound": "hbm", "achieved": alg / (ms_k * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": alg / (ms_k * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "traffic": None if tr is None else tr["bytes"], "kernel": kname,
+                               "algorithmic_bytes_per_launch": alg, "avg_launch_us": ms_k * 1e3}
             if tr is not None:
-                rec["roofline"]["traffic_over_algorithmic"] = tr["bytes"] / gu_alg
+                rec["roofline"]["traffic_over_algorithmic"] = tr["bytes"] / alg
             if "decode_down" in kt:
                 ms_d = kt["decode_down"][0]
                 d_alg = D.mean() * down_bytes + T * k * I * 2 + T * k * H * 4 + T * k * 4

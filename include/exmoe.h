@@ -173,7 +173,13 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
 
 /* Whole layer in one call: route (exmoe_route_topk), group (exmoe_group_tokens) and the
  * expert layer (exmoe_moe_forward), with the routing results written to caller buffers
- * (logits may be NULL). Same arguments and rules as those three calls. */
+ * (logits is required here: the selection reads it back). Same arguments and rules as
+ * those three calls.
+ * Workspace contract (this call only): its first 4096 bytes hold arrival counters that
+ * persist between calls. They must be zero before the first call on a workspace (allocate
+ * it zero-filled or clear it once); every call leaves them zero, and no other call of the
+ * library writes them, so one workspace may serve calls of any shape and path. Calls
+ * that share a workspace must not overlap in time (same stream, or synchronized). */
 size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags);
 int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
                     const exmoe_expert_bank* bank, int T, int H, int I, int E, int k,

@@ -248,8 +248,10 @@ def moe_workspace_bytes(T, H, I, E, k, flags=PATH_AUTO) -> int:
 
 
 def alloc_workspace(nbytes: int, device="cuda"):
+    """Zero-filled workspace: the layer call keeps arrival counters, zero between calls,
+    in its first 4096 bytes."""
     torch = _torch()
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
 
 
 def moe_forward(x, ids, weights, offsets, sorted_flat, flat_to_sorted, bank: ExpertBank, I: int,

@@ -340,12 +340,18 @@ static int choose_path(int T, int E, int k, int flags) {
 }
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+// Workspace header: routing arrival counters (one per 256-byte line, so that their atomics
+// do not serialize on one cache line) and a debug word.
+constexpr size_t kWsHeaderBytes = 4096, kWsCounterOffset = 0, kWsDebugOffset = 2048;
+static_assert(kWsCounterOffset + (size_t)kRouteSelCounters * kRouteCounterStride * 4 <= kWsDebugOffset,
+              "counters overlap the debug word");
 
 namespace exmoe {
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws) {
-  (void)E; (void)path;
   const size_t rows = (size_t)T * k;
-  size_t off = 0;
+  // the first kWsHeaderBytes are the same in every layout: they hold the routing kernel's
+  // arrival counters, which persist (as zeros) from one call to the next
+  size_t off = kWsHeaderBytes;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += align256(bytes);
@@ -356,16 +362,21 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   // correction seeds of the prefill kernels: [group][sorted row], rows padded by one tile
   const size_t o_gs = take((rows + 128) * (I / kGroup) * 4);
   const size_t o_xs = take((rows + 128) * (H / kGroup) * 4);
-  const size_t o_ct = take((size_t)(H / 32 + 1) * 4);
-  const size_t o_db = take(16);
+  // fused decode: down-projection partial outputs per 128-wide slice of I
+  const bool fused = path == EXMOE_PATH_DECODE && decode_fused_ok(T, I, E, k);
+  const size_t o_pt = take(fused ? (size_t)(I / kGroup) * rows * H * 4 : 0);
+  const size_t o_sel = take((size_t)E * 16);
   if (a && ws) {
     uint8_t* b = static_cast<uint8_t*>(ws);
+    a->sel = b + o_sel;
     a->h = reinterpret_cast<uint16_t*>(b + o_h);
     a->y_perm = reinterpret_cast<float*>(b + o_yp);
     a->gsum = reinterpret_cast<float*>(b + o_gs);
     a->xsum = reinterpret_cast<float*>(b + o_xs);
-    a->counters = reinterpret_cast<uint32_t*>(b + o_ct);
-    a->debug = reinterpret_cast<uint32_t*>(b + o_db);
+    a->part = fused ? reinterpret_cast<float*>(b + o_pt) : nullptr;
+    a->nparts = fused ? I / kGroup : 0;
+    a->counters = reinterpret_cast<uint32_t*>(b + kWsCounterOffset);
+    a->debug = reinterpret_cast<uint32_t*>(b + kWsDebugOffset);
   }
   return off;
 }
@@ -476,16 +487,23 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if (choose_path(T, E, k, flags) == EXMOE_PATH_DECODE && (long long)T * k <= kDecMaxRows) {
-    // Decode sizes: one workgroup per token routes it; the gate/up kernel groups the rows
-    // from the ids and publishes the grouping.
+    // Decode sizes: the expert kernel groups the rows itself and publishes the grouping;
+    // for a few tokens it also makes the top-k selection from the logits, otherwise one
+    // workgroup per token routes it first.
     MoeArgs a{};
     a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
     a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
     a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
     moe_workspace_layout(T, H, I, E, k, EXMOE_PATH_DECODE, &a, workspace);
-    EXMOE_HIP(launch_route_token(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids, topk_weights,
-                                 stream));
-    EXMOE_HIP(launch_moe_decode_from_ids(a, expert_offsets, sorted_flat, flat_to_sorted, stream));
+    if (decode_table_routing_ok(T, H, E, k)) {
+      EXMOE_HIP(launch_route_sel(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids, topk_weights,
+                                 a.sel, a.counters, stream));
+      EXMOE_HIP(launch_moe_decode_routed(a, a.sel, expert_offsets, sorted_flat, flat_to_sorted, stream));
+    } else {
+      EXMOE_HIP(launch_route_token(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids,
+                                   topk_weights, stream));
+      EXMOE_HIP(launch_moe_decode_routed(a, nullptr, expert_offsets, sorted_flat, flat_to_sorted, stream));
+    }
     return EXMOE_OK;
   }
   EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));

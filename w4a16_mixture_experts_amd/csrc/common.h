@@ -16,6 +16,7 @@ constexpr int kTileRows = 16;    // output rows per packed tile
 constexpr int kTileBytes = 1024; // 16 rows x 128 inputs x 4 bits
 constexpr int kScaleBytes = 32;  // 16 bf16 scales per tile
 constexpr int kMaxExperts = 256;
+constexpr int kMaxK = 64;
 constexpr int kMaxDim = 16384;   // largest hidden / intermediate size (zero-row length)
 
 __host__ __device__ inline size_t n_tiles(int H, int I) {
@@ -93,10 +94,13 @@ struct MoeArgs {
   uint16_t* y;
   // workspace carve-up
   uint16_t* h;        // bf16 [T*k, I], sorted-row order
+  float* part;        // fp32 [I/128][T*k, H]: fused decode, down output of each 128-wide slice of I
+  int nparts;         // slices in part (0: the combine reads y_perm)
   float* y_perm;      // fp32 [T*k, H], sorted-row order, already multiplied by the routing weight
   float* gsum;        // fp32 [I/128][T*k + 128]: -136 * group sums of h per sorted row (down seeds)
   float* xsum;        // fp32 [H/128][T*k + 128]: -136 * group sums of x per sorted row (gate/up seeds)
-  uint32_t* counters; // decode last-arriver counters
+  uint8_t* sel;       // u8 [E][16]: decode expert table, sel[e][t] = slot + 1 of token t (0: not routed)
+  uint32_t* counters; // arrival counters of the routing kernel (zero between launches)
   uint32_t* debug;    // debug word(s)
 };
 
@@ -105,14 +109,27 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
 constexpr int kDecMaxRows = 1024;
 // Decode path from offsets and permutation given by the caller.
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s);
+// Whether the decode path runs gate/up and down in one kernel (down outputs per 128-wide
+// slice of I, summed by the combine): enough workgroups and few slices.
+bool decode_fused_ok(int T, int I, int E, int k);
 // Logits, top-k selection and routing weights of each token by one workgroup per token.
 hipError_t launch_route_token(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
                               int k, int renormalize, uint16_t* logits, int32_t* ids, float* w, hipStream_t s);
-// Decode path from the top-k ids alone (T * k <= kDecMaxRows): the gate/up kernel groups
-// the routed rows itself and publishes the grouping to offsets / sorted_flat /
-// flat_to_sorted, which a.offsets and a.sorted_flat must alias.
-hipError_t launch_moe_decode_from_ids(const MoeArgs& a, int32_t* offsets, int32_t* sorted_flat,
-                                      int32_t* flat_to_sorted, hipStream_t s);
+// Logits, top-k, weights and the decode expert table of T <= kRouteSelMaxTok tokens in one
+// launch (arrival counters: ceil(T / 2) of them, zero before the launch and after it).
+constexpr int kRouteSelMaxTok = 16;
+constexpr int kRouteSelCounters = 8, kRouteCounterStride = 64;   // counter i at word i * stride
+hipError_t launch_route_sel(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
+                            int renormalize, uint16_t* logits, int32_t* ids, float* w, uint8_t* sel,
+                            uint32_t* counters, hipStream_t s);
+// Decode path that groups the routed rows inside its gate/up kernel (T * k <= kDecMaxRows),
+// from ids (sel == nullptr) or from the expert table of launch_route_sel (when
+// decode_table_routing_ok: every token row is then staged before the weight stream). The
+// gate/up kernel publishes the grouping into offsets / sorted_flat / flat_to_sorted; a.ids,
+// a.offsets and a.sorted_flat must alias those buffers.
+bool decode_table_routing_ok(int T, int H, int E, int k);
+hipError_t launch_moe_decode_routed(const MoeArgs& a, const uint8_t* sel, int32_t* offsets, int32_t* sorted_flat,
+                                    int32_t* flat_to_sorted, hipStream_t s);
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);

@@ -27,6 +27,8 @@
 // write-back on this chip, more than a kernel boundary inside a graph.
 #include "common.h"
 #include "device.h"
+#include "group_block.h"
+#include "topk.h"
 
 namespace exmoe {
 
@@ -37,6 +39,7 @@ constexpr int kDecKC = 2048;                 // reduction columns staged in LDS 
 constexpr int kDecKG = kDecKC / kGroup;      // 128-input groups per staged chunk
 constexpr int kDecXS = kDecKC + 8;           // LDS row stride (bf16): 16-byte skew per row
 constexpr int kDecRing = 4;                  // weight groups in flight per wave
+constexpr int kSelStride = 16;               // bytes per expert row of the routing table (T <= 16)
 
 
 // In the routing set-up the staging area holds the ids; afterwards the staged rows, and at
@@ -50,6 +53,7 @@ struct DecLDS {
   int32_t act[kMaxExperts];
   int32_t rows[kDecMaxRows];                 // flat indices of this expert's rows (grouped here)
   int32_t pf[kDecTok];                       // flat indices of the current pass (-1: padding)
+  int32_t srows[kDecTok];                    // this expert's flat indices (table routing)
   int32_t n_act;
 };
 
@@ -59,27 +63,37 @@ struct DecExpert {
   const uint16_t* scales;
 };
 
-// Routing source of the gate/up kernel. kSrcGiven: offsets and permutation come from the
-// caller. kSrcIds: top-k ids given; the rows are grouped here and the grouping published
-// to the pointers below for the kernels that follow.
-constexpr int kSrcGiven = 0, kSrcIds = 1;
+// Routing source of the expert kernels. kSrcGiven: offsets and permutation come from the
+// caller. kSrcIds: top-k ids given; the rows are grouped here and the first workgroup of
+// each expert publishes its segment (workgroup 0 the offsets). kSrcSel (T <= 16, H <=
+// kDecKC): the routing kernel's table sel[e][t] = slot + 1 when token t selected expert
+// e, else 0; every token row of x is staged before the weight stream starts, and a
+// publisher workgroup (the grid's last) groups the ids for the caller's outputs.
+constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2;
 struct DecPublish {
+  const uint8_t* sel;        // [E][kSelStride] bytes
   int32_t* offsets;
   int32_t* sorted_flat;
   int32_t* flat_to_sorted;
 };
 
-// The routing inputs of the set-up (ids or offsets), loaded into registers as the kernel's
-// very first loads: a wave's vector loads complete in issue order, so these must not
-// queue behind the weight prefetch. Unconditional loads at clamped indices.
-constexpr int kDecPre = kDecMaxRows / kDecThreads;   // ids <= 2 * 512, offsets <= 257
+// The routing inputs of the set-up (ids, offsets or the table), loaded into registers as
+// the kernel's very first loads: a wave's vector loads complete in issue order, so these
+// must not queue behind the weight prefetch. Unconditional loads at clamped indices.
+constexpr int kDecPre = 4;   // per thread: ids <= 2 * 512, offsets <= 257, one 16-byte table row
 struct DecPre {
   int32_t v[kDecPre];
 };
 template <int SRC>
-__device__ __forceinline__ DecPre dec_preload(const MoeArgs& a) {
+__device__ __forceinline__ DecPre dec_preload(const MoeArgs& a, const DecPublish& pub) {
   DecPre pr;
   const int tid = threadIdx.x;
+  if (SRC == kSrcSel) {
+    const int e = tid < a.E ? tid : a.E - 1;
+    const uint4 u = *reinterpret_cast<const uint4*>(pub.sel + (size_t)e * kSelStride);
+    pr.v[0] = (int32_t)u.x; pr.v[1] = (int32_t)u.y; pr.v[2] = (int32_t)u.z; pr.v[3] = (int32_t)u.w;
+    return pr;
+  }
   const int n = SRC == kSrcIds ? a.T * a.k : a.E + 1;
 #pragma unroll
   for (int m = 0; m < kDecPre; m++) {
@@ -90,23 +104,70 @@ __device__ __forceinline__ DecPre dec_preload(const MoeArgs& a) {
   return pr;
 }
 
+// Every token row of x (T <= kDecTok, H <= kDecKC) into the staging rows, indexed by
+// token: all loads in flight at once, then the stores.
+__device__ __forceinline__ void dec_prestage_x(const MoeArgs& a, DecLDS& L) {
+  constexpr int SQ = kDecTok * (kDecKC / 8) / kDecThreads;
+  const int tid = threadIdx.x;
+  const int cw8 = a.H / 8;
+  uint4 v[SQ];
+#pragma unroll
+  for (int m = 0; m < SQ; m++) {
+    const int q = tid + m * kDecThreads;
+    int r = q / cw8;
+    const int c8 = q - r * cw8;
+    r = r < a.T ? r : a.T - 1;
+    v[m] = *reinterpret_cast<const uint4*>(a.x + (size_t)r * a.H + c8 * 8);
+  }
+#pragma unroll
+  for (int m = 0; m < SQ; m++) {
+    const int q = tid + m * kDecThreads;
+    const int r = q / cw8, c8 = q - r * cw8;
+    if (r < a.T) *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) = v[m];
+  }
+}
+
+// Publisher of a table-routed launch (the grid's last workgroup): stable grouping of the
+// ids the routing kernel wrote, into the caller's offsets / sorted_flat / flat_to_sorted.
+__device__ void dec_publish(const MoeArgs& a, DecLDS& L, const DecPublish& pub) {
+  int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);
+  auto& gs = *reinterpret_cast<GroupSharedT<kDecThreads>*>(L.xs + 2 * kDecMaxRows);
+  const int TK = a.T * a.k;
+  for (int f = threadIdx.x; f < TK; f += kDecThreads) ids_l[f] = a.ids[f];
+  __syncthreads();
+  group_block<kDecThreads>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
+}
+
 template <int SRC, bool ALL>
 __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, const DecPre& pr, int fixed_expert,
                           int aidx, bool first_of_expert, int slot_known, DecExpert& ex) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int TK = a.T * a.k;
-  int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);
-  if (SRC == kSrcIds) {
+  int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);            // staging rows are free (ids mode)
+  uint8_t* selb = reinterpret_cast<uint8_t*>(L.rows);            // table rows (sel mode)
+  if (SRC == kSrcSel) {
+    if (tid < a.E) {
+      const uint4 u = make_uint4((uint32_t)pr.v[0], (uint32_t)pr.v[1], (uint32_t)pr.v[2], (uint32_t)pr.v[3]);
+      *reinterpret_cast<uint4*>(selb + tid * kSelStride) = u;
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < 16; q++) c += (q < a.T && ((w4[q >> 2] >> (8 * (q & 3))) & 0xFFu)) ? 1 : 0;
+      L.cnt[tid] = c;
+    }
+  } else if (SRC == kSrcIds) {
 #pragma unroll
     for (int m = 0; m < kDecPre; m++)
       if (tid + m * kDecThreads < TK) ids_l[tid + m * kDecThreads] = pr.v[m];
   }
   if (SRC != kSrcGiven) {
-    for (int i = tid; i < a.E; i += kDecThreads) L.cnt[i] = 0;
-    __syncthreads();
-    for (int f = tid; f < TK; f += kDecThreads) {
-      const int e = ids_l[f];
-      if ((unsigned)e < (unsigned)a.E) atomicAdd(&L.cnt[e], 1);
+    if (SRC == kSrcIds) {
+      for (int i = tid; i < a.E; i += kDecThreads) L.cnt[i] = 0;
+      __syncthreads();
+      for (int f = tid; f < TK; f += kDecThreads) {
+        const int e = ids_l[f];
+        if ((unsigned)e < (unsigned)a.E) atomicAdd(&L.cnt[e], 1);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -153,7 +214,16 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
   ex.e = ALL ? aidx : __builtin_amdgcn_readfirstlane(L.act[aidx]);
   ex.seg0 = __builtin_amdgcn_readfirstlane(L.off[ex.e]);
   ex.cnt = __builtin_amdgcn_readfirstlane(L.off[ex.e + 1]) - ex.seg0;
-  if (SRC != kSrcGiven) {
+  if (SRC == kSrcSel) {
+    // the tokens that selected this expert, ascending (the table gives each one's slot)
+    if (wave == 0) {
+      const int sb = lane < a.T ? selb[ex.e * kSelStride + lane] : 0;
+      const uint64_t m = __ballot(sb > 0);
+      if (sb > 0) L.srows[__popcll(m & ((1ull << lane) - 1ull))] = lane * a.k + sb - 1;
+    }
+    __syncthreads();
+  }
+  if (SRC == kSrcIds) {
     if (wave == 0) {
       int base = 0;
       for (int c0 = 0; c0 < TK; c0 += 64) {
@@ -261,7 +331,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
   if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
 
-  const DecPre pre = dec_preload<SRC>(a);
+  const DecPre pre = dec_preload<SRC>(a, pub);
+  if (GATEUP && SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+    dec_publish(a, L, pub);
+    return;
+  }
+  if (GATEUP && SRC == kSrcSel) dec_prestage_x(a, L);
   // ALL: the grid covers every expert, so the expert (hence its weights) is known at once:
   // the first ring of weight loads goes out right behind the routing inputs and arrives
   // while the routing is worked out. Loads through a resource of zero length (expert
@@ -291,7 +366,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
     const int nrow = ex.cnt - p * kDecTok < kDecTok ? ex.cnt - p * kDecTok : kDecTok;
     if (GATEUP && tid < kDecTok) {
       const int r = p * kDecTok + tid;
-      L.pf[tid] = r < ex.cnt ? (SRC != kSrcGiven ? L.rows[r] : a.sorted_flat[ex.seg0 + r]) : -1;
+      L.pf[tid] = r < ex.cnt ? (SRC == kSrcSel ? L.srows[r] : SRC == kSrcIds ? L.rows[r] : a.sorted_flat[ex.seg0 + r])
+                             : -1;
     }
     // down: the rows to stage are contiguous in h; the flat index is needed only at the end
     int f_out = -1;
@@ -303,7 +379,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
       const int kcw = K - kc0 < kDecKC ? K - kc0 : kDecKC;
       const int ngc = kcw / kGroup;
       __syncthreads();   // previous chunk consumed; pass row list visible
-      {
+      if (!(GATEUP && SRC == kSrcSel)) {   // table routing: every token row is already staged
         const int cw8 = kcw / 8;
         for (int q = tid; q < nrow * cw8; q += kDecThreads) {
           const int r = q / cw8, c8 = q - r * cw8;
@@ -313,7 +389,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
         }
       }
       __syncthreads();
-      for (int q = tid; q < nrow * ngc * 2; q += kDecThreads) {
+      const int nstaged = GATEUP && SRC == kSrcSel ? a.T : nrow;   // rows indexed by token or by slot
+      for (int q = tid; q < nstaged * ngc * 2; q += kDecThreads) {
         const int r = q / (ngc * 2), gg = (q >> 1) % ngc, half = q & 1;
         const uint16_t* src = L.xs + r * kDecXS + gg * kGroup + half * 64;
         float s = 0.f;
@@ -333,7 +410,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
       __syncthreads();
 
       const int pg = (ngc + KS - 1) / KS;
-      const int myrow = (lane & 15) < nrow ? (lane & 15) : kDecTok;   // padding slots read the zero row
+      // padding slots read the zero row; table routing stages rows by token
+      const int myrow = (lane & 15) < nrow ? (GATEUP && SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
       const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
       const float* srow = L.seed + myrow * kDecKG;
 #pragma unroll
@@ -409,6 +487,243 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
 }
 
 // ------------------------------------------------------------------------------------
+// Fused gate/up + down. Workgroup = (expert, slice c of 128 rows of I); wave w owns row
+// block 8c + w of I. Phase 1 computes h for the slice (gate and up tiles, reduction over
+// H) into LDS; phase 2 applies the slice's 128 columns of W_down, which are exactly input
+// group c of every down tile, to all H outputs: each wave streams the tiles (row block
+// rbd, group c) of its share of H. The result goes to part[c][f][H]; the combine adds the
+// slices and applies the routing weight. h never leaves the chip, and one kernel
+// boundary (its ramp, set-up and tail) disappears. One weight ring runs through both
+// phases: slots 0 .. S1-1 hold gate/up groups, then pairs of down tiles.
+// ------------------------------------------------------------------------------------
+template <int SRC, bool ALL>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a, DecPublish pub, int fixed_expert) {
+  __shared__ DecLDS L;
+  __shared__ float s_hseed[kDecTok];
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int nslice = a.I / kGroup;
+  const int aidx = blockIdx.x / nslice, cs = blockIdx.x % nslice;
+
+  const int G = a.H / kGroup;                  // gate/up groups
+  const int nK = (a.H + kDecKC - 1) / kDecKC;  // staged chunks of x
+  const int S1 = nK * kDecKG;                  // phase-1 ring positions
+  const int nrbd = a.H / kTileRows;            // down row blocks
+  const int per_w = (nrbd + kDecWaves - 1) / kDecWaves;     // down row blocks per wave
+  const int npair = (per_w + 1) / 2;
+  const int S2 = (npair + kDecRing - 1) / kDecRing * kDecRing;   // phase-2 ring positions
+  const int ST = S1 + S2;
+  const int rb = cs * kDecWaves + wave;        // gate/up row block of this wave
+  const int rbd_base = wave * per_w;
+  const int Gd = a.I / kGroup;
+  const uint32_t sc_base = (uint32_t)(n_tiles(a.H, a.I) * kTileBytes);
+  const uint32_t dbase = 2u * (uint32_t)(a.I / kTileRows) * (uint32_t)G;
+  const int nbytes = (int)packed_bytes(a.H, a.I);
+  const uint32_t lo_t = (uint32_t)lane * 16u, lo_s = (uint32_t)(lane >> 4) * 8u;
+  const uint32_t tg0 = (uint32_t)(rb * 2) * G, tg1 = (uint32_t)(rb * 2 + 1) * G;
+  // tile indices of ring position s (uniform): gate/up group, or a pair of down tiles
+  auto tiles_of = [&](int s, uint32_t& ta, uint32_t& tb) {
+    if (s < S1) {
+      const int c = s / kDecKG, i = s % kDecKG;
+      int g = c * kDecKG + i;
+      g = g < G ? g : G - 1;
+      ta = tg0 + g;
+      tb = tg1 + g;
+    } else {
+      const int pi = s - S1;
+      int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
+      const int rmax = rbd_base + per_w - 1 < nrbd - 1 ? rbd_base + per_w - 1 : nrbd - 1;
+      r0 = r0 < rmax ? r0 : rmax;
+      r1 = r1 < rmax ? r1 : rmax;
+      ta = dbase + (uint32_t)r0 * Gd + cs;
+      tb = dbase + (uint32_t)r1 * Gd + cs;
+    }
+  };
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int s, WSlot2& w) {
+    uint32_t ta, tb;
+    tiles_of(s, ta, tb);
+    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(ta * kTileBytes), 0));
+    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(tb * kTileBytes), 0));
+    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + ta * kScaleBytes), 0));
+    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + tb * kScaleBytes), 0));
+  };
+
+  for (int i = tid; i < kDecXS / 8; i += kDecThreads)
+    *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
+
+  const DecPre pre = dec_preload<SRC>(a, pub);
+  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+    dec_publish(a, L, pub);
+    return;
+  }
+  if (SRC == kSrcSel) dec_prestage_x(a, L);
+  WSlot2 W[kDecRing];
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
+  int slot = 0;
+  if (ALL) {
+    slot = a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[aidx]) : aidx;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
+                                             slot >= 0 ? nbytes : 0, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
+  }
+  DecExpert ex;
+  if (!dec_setup<SRC, ALL>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) return;
+  if (!ALL) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
+  }
+  const __amdgpu_buffer_rsrc_t rsrc_none = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, 0, 0x00020000);
+
+  const int npass = (ex.cnt + kDecTok - 1) / kDecTok;
+  for (int p = 0; p < npass; p++) {
+    const int nrow = ex.cnt - p * kDecTok < kDecTok ? ex.cnt - p * kDecTok : kDecTok;
+    if (tid < kDecTok) {
+      const int r = p * kDecTok + tid;
+      L.pf[tid] = r < ex.cnt ? (SRC == kSrcSel ? L.srows[r] : SRC == kSrcIds ? L.rows[r] : a.sorted_flat[ex.seg0 + r])
+                             : -1;
+    }
+    auto next_issue = [&](int sn, WSlot2& w) {
+      // past this pass's last position the ring runs on into the next pass; after the
+      // last pass it loads nothing
+      const int wrap = sn >= ST;
+      issue(wrap ? (p + 1 < npass ? rsrc : rsrc_none) : rsrc, wrap ? sn - ST : sn, w);
+    };
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- phase 1: gate/up over H, activations staged chunk by chunk
+    for (int c = 0; c < nK; c++) {
+      const int kc0 = c * kDecKC;
+      const int kcw = a.H - kc0 < kDecKC ? a.H - kc0 : kDecKC;
+      const int ngc = kcw / kGroup;
+      __syncthreads();   // previous chunk consumed; pass row list visible
+      if (SRC != kSrcSel) {   // table routing: every token row is already staged
+        const int cw8 = kcw / 8;
+        for (int q = tid; q < nrow * cw8; q += kDecThreads) {
+          const int r = q / cw8, c8 = q - r * cw8;
+          *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) = *reinterpret_cast<const uint4*>(
+              a.x + (size_t)(L.pf[r] / a.k) * a.H + kc0 + c8 * 8);
+        }
+      }
+      __syncthreads();
+      const int nstaged = SRC == kSrcSel ? a.T : nrow;   // rows indexed by token or by slot
+      for (int q = tid; q < nstaged * ngc * 2; q += kDecThreads) {
+        const int r = q / (ngc * 2), gg = (q >> 1) % ngc, half = q & 1;
+        const uint16_t* src = L.xs + r * kDecXS + gg * kGroup + half * 64;
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * i);
+          const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int m = 0; m < 4; m++) {
+            sm += __uint_as_float(q4[m] << 16);
+            sm += __uint_as_float(q4[m] & 0xFFFF0000u);
+          }
+        }
+        const float o = __shfl_xor(sm, 1);
+        if (!half) L.seed[r * kDecKG + gg] = -136.0f * (sm + o);
+      }
+      __syncthreads();
+      const int myrow = (lane & 15) < nrow ? (SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
+      const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
+      const float* srow = L.seed + myrow * kDecKG;
+#pragma unroll
+      for (int i0 = 0; i0 < kDecKG; i0 += kDecRing) {
+#pragma unroll
+        for (int j = 0; j < kDecRing; j++) {
+          const int gl = i0 + j;
+          if (gl < ngc) {
+            bf16x8 act[4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; s4++) act[s4] = *reinterpret_cast<const bf16x8*>(xrow + gl * kGroup + 32 * s4);
+            const float sd = srow[gl];
+            f32x4 c0 = {sd, sd, sd, sd}, c1 = c0;
+            c0 = mfma16(dequant_word(W[j].w[0].x), act[0], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].x), act[0], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].y), act[1], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].y), act[1], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].z), act[2], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].z), act[2], c1);
+            c0 = mfma16(dequant_word(W[j].w[0].w), act[3], c0);
+            c1 = mfma16(dequant_word(W[j].w[1].w), act[3], c1);
+            scale_accum(acc0, c0, W[j].s[0]);
+            scale_accum(acc1, c1, W[j].s[1]);
+          }
+          next_issue(c * kDecKG + i0 + j + kDecRing, W[j]);
+        }
+      }
+    }
+    // ---- h of the slice into LDS (bf16, [token][128 + skew]), and its correction seeds
+    __syncthreads();   // all waves done with the staged activations
+    constexpr int kHS = kGroup + 8;
+    uint16_t* hs = L.xs;
+    {
+      // padding token slots computed from the zero row: their h is 0
+      uint16_t hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(acc0[i] / (1.0f + expf(-acc0[i])) * acc1[i]);
+      uint2 pk;
+      pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+      pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+      *reinterpret_cast<uint2*>(hs + (lane & 15) * kHS + wave * 16 + 4 * (lane >> 4)) = pk;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // -136 * sum of the token's 128 h values: four quarter sums, added in a fixed order
+      const uint16_t* hr = hs + (lane & 15) * kHS + 32 * (lane >> 4);
+      float sm = 0.f;
+      for (int i = 0; i < 32; i++) sm += bf16_to_f32(hr[i]);
+      sm += __shfl_xor(sm, 16);
+      sm += __shfl_xor(sm, 32);
+      if (lane < kDecTok) s_hseed[lane] = -136.0f * sm;
+    }
+    __syncthreads();
+    // ---- phase 2: the slice's down column group over all H rows of this wave's share
+    bf16x8 acth[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++)
+      acth[s4] = *reinterpret_cast<const bf16x8*>(hs + (lane & 15) * kHS + 32 * s4 + 8 * (lane >> 4));
+    const float sdh = s_hseed[lane & 15];
+    const int f = L.pf[lane & 15];
+    float* prow = a.part + ((size_t)cs * a.T * a.k + (f >= 0 ? f : 0)) * a.H + 4 * (lane >> 4);
+#pragma unroll
+    for (int i0 = 0; i0 < S2; i0 += kDecRing) {
+#pragma unroll
+      for (int j = 0; j < kDecRing; j++) {
+        const int pi = i0 + j;
+        if (pi < npair) {
+          const int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
+          const int lim = rbd_base + per_w < nrbd ? rbd_base + per_w : nrbd;
+          f32x4 c0 = {sdh, sdh, sdh, sdh}, c1 = c0;
+          c0 = mfma16(dequant_word(W[j].w[0].x), acth[0], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].x), acth[0], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].y), acth[1], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].y), acth[1], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].z), acth[2], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].z), acth[2], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].w), acth[3], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].w), acth[3], c1);
+          f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+          scale_accum(o0, c0, W[j].s[0]);
+          scale_accum(o1, c1, W[j].s[1]);
+          if (f >= 0) {
+            if (r0 < lim)
+              *reinterpret_cast<float4*>(prow + r0 * 16) = make_float4(o0[0], o0[1], o0[2], o0[3]);
+            if (r1 < lim)
+              *reinterpret_cast<float4*>(prow + r1 * 16) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+          }
+        }
+        next_issue(S1 + i0 + j + kDecRing, W[j]);
+      }
+    }
+    __syncthreads();   // pass row list and LDS free for the next pass
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // combine: y[t, rows] = bf16(sum_j y_perm[t k + j, rows]) in slot order
 // ------------------------------------------------------------------------------------
 constexpr int kCombineTok = 16;
@@ -430,6 +745,47 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
   }
 }
 
+// combine of the fused decode: y[t] = bf16(sum over slots j in order of w[t k + j] times
+// (sum over I-slices q in order of part[q][t k + j])). Workgroup = (token, 128 columns); thread = (4
+// columns, slot j) adds the slices of its slot, then the slots are added through LDS.
+constexpr int kCombCols = 128;
+__global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
+  __shared__ float4 red[kMaxK][kCombCols / 4];
+  const int t = blockIdx.y;
+  const int col0 = blockIdx.x * kCombCols;
+  const size_t slice = (size_t)a.T * a.k * a.H;
+  for (int i = threadIdx.x; i < a.k * (kCombCols / 4); i += blockDim.x) {
+    const int j = i / (kCombCols / 4), cq = i % (kCombCols / 4);
+    const int c = col0 + 4 * cq;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < a.H) {
+      const float* src = a.part + ((size_t)t * a.k + j) * a.H + c;
+      for (int q = 0; q < a.nparts; q++) {
+        const float4 v = *reinterpret_cast<const float4*>(src + q * slice);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+      const float wt = a.w[t * a.k + j];
+      s.x *= wt; s.y *= wt; s.z *= wt; s.w *= wt;
+    }
+    red[j][cq] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < kCombCols / 4) {
+    const int cq = threadIdx.x, c = col0 + 4 * cq;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; j++) {
+      const float4 v = red[j][cq];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (c < a.H) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
+      pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+      *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
@@ -446,15 +802,16 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
   // workgroups per expert at KS = 1: gate/up 8 row blocks of I each; down 16 row blocks of H
   const int per1 = GATEUP ? a.I / (kTileRows * kDecWaves) : (a.H / kTileRows + 2 * kDecWaves - 1) / (2 * kDecWaves);
   const dim3 block(kDecThreads);
+  const int extra = GATEUP && SRC == kSrcSel ? 1 : 0;   // the publisher workgroup
   if (fixed_expert < 0 && (long long)a.T * a.k >= 2LL * a.E) {
     // most experts active: one row of workgroups per expert (no active-expert list)
-    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, true>), dim3(a.E * per1), block, 0, s, a, pub,
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, true>), dim3(a.E * per1 + extra), block, 0, s, a, pub,
                  fixed_expert, per1);
     return;
   }
   const int ks = pick_ks(ny * per1);
   const int nchunk = per1 * ks;
-  const dim3 grid(ny * nchunk);
+  const dim3 grid(ny * nchunk + extra);
   if (ks == 1)
     EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
   else if (ks == 2)
@@ -463,14 +820,39 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
     EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
 }
 
+bool decode_fused_ok(int T, int I, int E, int k) {
+  const long long ny = E < (long long)T * k ? E : (long long)T * k;
+  return I / kGroup <= 16 && ny * (I / kGroup) >= 256;
+}
+
 static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub, int fixed_expert, int ny,
                                         hipStream_t s) {
+  if (a.nparts > 0 && fixed_expert < 0) {
+    ProfScope prof("decode_fused", s);
+    const bool all = (long long)a.T * a.k >= 2LL * a.E;
+    const int nslice = a.I / kGroup;
+    const int extra = pub && pub->sel ? 1 : 0;   // the publisher workgroup
+    const dim3 grid((all ? a.E : ny) * nslice + extra), block(kDecThreads);
+    const DecPublish none{};
+#define EXMOE_FUSED(SRC, P)                                                                                   \
+  do {                                                                                                       \
+    if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true>), grid, block, 0, s, a, P, fixed_expert);    \
+    else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false>), grid, block, 0, s, a, P, fixed_expert);       \
+  } while (0)
+    if (!pub) EXMOE_FUSED(kSrcGiven, none);
+    else if (pub->sel) EXMOE_FUSED(kSrcSel, *pub);
+    else EXMOE_FUSED(kSrcIds, *pub);
+#undef EXMOE_FUSED
+    return hipGetLastError();
+  }
   {
     ProfScope prof("decode_gateup", s);
-    if (pub)
-      launch_expert<true, kSrcIds>(prof, a, *pub, fixed_expert, ny, s);
-    else
+    if (!pub)
       launch_expert<true, kSrcGiven>(prof, a, DecPublish{}, fixed_expert, ny, s);
+    else if (pub->sel)
+      launch_expert<true, kSrcSel>(prof, a, *pub, fixed_expert, ny, s);
+    else
+      launch_expert<true, kSrcIds>(prof, a, *pub, fixed_expert, ny, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -488,10 +870,15 @@ hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s) {
   return launch_combine(a, s);
 }
 
-hipError_t launch_moe_decode_from_ids(const MoeArgs& a, int32_t* offsets, int32_t* sorted_flat,
-                                      int32_t* flat_to_sorted, hipStream_t s) {
+bool decode_table_routing_ok(int T, int H, int E, int k) {
+  return T >= 1 && T <= kDecTok && H <= kDecKC && E <= 256 && E * kSelStride <= kDecMaxRows * 4 &&
+         T * k <= kDecMaxRows;
+}
+
+hipError_t launch_moe_decode_routed(const MoeArgs& a, const uint8_t* sel, int32_t* offsets, int32_t* sorted_flat,
+                                    int32_t* flat_to_sorted, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
-  const DecPublish pub{offsets, sorted_flat, flat_to_sorted};
+  const DecPublish pub{sel, offsets, sorted_flat, flat_to_sorted};
   hipError_t e = launch_decode_experts(a, &pub, -1, ny, s);
   if (e != hipSuccess) return e;
   return launch_combine(a, s);
@@ -505,6 +892,10 @@ hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipSt
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   ProfScope prof("combine", s);
+  if (a.nparts > 0) {
+    EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   EXMOE_LAUNCH(prof, combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -20,13 +20,33 @@ __device__ __forceinline__ uint32_t order_key(uint16_t b, int e) {
   return (o << 16) | (uint32_t)(0xFFFF - e);
 }
 
+// Routing weights of the selected slots (slot j in lane j, logit my_sel), shared by both
+// selection methods so that their weights agree bit for bit. renormalize: softmax over
+// the k selected logits; otherwise the full softmax probability (lv: this lane's logits).
+__device__ __forceinline__ float topk_weight(float my_sel, const float* lv, int nq, int E, int k, int renormalize) {
+  const int lane = (int)lane_id();
+  float m, denom;
+  if (renormalize) {
+    m = wave_max_f32(my_sel);
+    denom = wave_sum_f32(lane < k ? expf(my_sel - m) : 0.f);
+  } else {
+    float m_all = -INFINITY;
+    for (int q = 0; q < nq; q++) m_all = fmaxf(m_all, lv[q]);
+    m = wave_max_f32(m_all);
+    float z = 0.f;
+    for (int q = 0; q < nq; q++)
+      if (lane + 64 * q < E) z += expf(lv[q] - m);
+    denom = wave_sum_f32(z);
+  }
+  return lane < k ? expf(my_sel - m) / denom : 0.f;
+}
+
 __device__ __forceinline__ void topk_token(const uint16_t* __restrict__ lrow,
                                            const int32_t* __restrict__ given, int E, int k,
                                            int renormalize, int& my_id, float& my_w) {
   const int lane = (int)lane_id();
   uint32_t key[4];
   float lv[4];
-  float m_all = -INFINITY;
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const int e = lane + 64 * q;
@@ -34,7 +54,6 @@ __device__ __forceinline__ void topk_token(const uint16_t* __restrict__ lrow,
       const uint16_t b = lrow[e];
       key[q] = order_key(b, e);
       lv[q] = bf16_to_f32(b);
-      m_all = fmaxf(m_all, lv[q]);
     } else {
       key[q] = 0;
       lv[q] = -INFINITY;
@@ -64,19 +83,62 @@ __device__ __forceinline__ void topk_token(const uint16_t* __restrict__ lrow,
       }
     }
   }
-  float m, denom;
-  if (renormalize) {
-    m = wave_max_f32(my_sel);
-    denom = wave_sum_f32(lane < k ? expf(my_sel - m) : 0.f);
-  } else {
-    m = wave_max_f32(m_all);
-    float z = 0.f;
+  my_w = topk_weight(my_sel, lv, 4, E, k, renormalize);
+}
+
+// ---------------------------------------------------------------------------------
+// The same selection and weights for E <= 64 by ranks: lane e holds expert e's key; its
+// rank is the number of keys above it (64 independent compares against readlane
+// broadcasts instead of k dependent wave reductions). Keys are distinct, so ranks
+// 0 .. k-1 are the selected experts in slot order; one ballot per slot moves slot j to
+// lane j, and the weights come from topk_weight as in topk_token.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void topk_rank_token(const uint16_t* __restrict__ lrow, int E, int k, int renormalize,
+                                                int& my_id, float& my_w) {
+  const int lane = (int)lane_id();
+  const bool in = lane < E;
+  const uint16_t b = in ? lrow[lane] : (uint16_t)0;
+  const uint32_t key = in ? order_key(b, lane) : 0u;
+  float lv[1] = {in ? bf16_to_f32(b) : -INFINITY};
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j++) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+    r += kj > key ? 1 : 0;
+  }
+  const int rank = in ? r : 64;
+  my_id = -1;
+  float my_sel = -INFINITY;
+  for (int j = 0; j < k; j++) {
+    const int src = (int)__builtin_ctzll(__ballot(rank == j));
+    if (lane == j) my_id = src;
+  }
+  if (lane < k) my_sel = bf16_to_f32(lrow[my_id]);
+  my_w = topk_weight(my_sel, lv, 1, E, k, renormalize);
+}
+
+// The k-th largest selection key of one token (one wave; E <= 256, up to 4 per lane).
+// Keys are distinct, so the selected experts are exactly those whose key is at least
+// this one. Radix selection from the top bit: 32 ballots, no reductions.
+__device__ __forceinline__ uint32_t kth_largest_key(const uint16_t* __restrict__ lrow, int E, int k) {
+  const int lane = (int)lane_id();
+  uint32_t key[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int e = lane + 64 * q;
+    key[q] = e < E ? order_key(lrow[e], e) : 0u;
+  }
+  const int nq = (E + 63) / 64;
+  uint32_t prefix = 0;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t cand = prefix | (1u << b);
+    int cnt = 0;
 #pragma unroll
     for (int q = 0; q < 4; q++)
-      if (lane + 64 * q < E) z += expf(lv[q] - m);
-    denom = wave_sum_f32(z);
+      if (q < nq) cnt += __popcll(__ballot(key[q] >= cand));
+    if (cnt >= k) prefix = cand;
   }
-  my_w = lane < k ? expf(my_sel - m) / denom : 0.f;
+  return prefix;
 }
 
 }  // namespace exmoe

@@ -29,8 +29,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 # Sources each profiled kernel is compiled from.
 KERNEL_SOURCES = {
-    "decode_gateup_kernel": ["moe_decode.hip", "device.h", "common.h", "group_block.h", "topk.h"],
-    "decode_down_kernel": ["moe_decode.hip", "device.h", "common.h", "group_block.h", "topk.h"],
+    "decode_expert_kernel": ["moe_decode.hip", "device.h", "common.h"],
+    "decode_fused_kernel": ["moe_decode.hip", "device.h", "common.h"],
     "prefill_kernel": ["moe_prefill.hip", "device.h", "common.h"],
 }
 
@@ -104,7 +104,8 @@ def dispatch_counters(d: str, counter: str) -> dict[str, list[float]]:
 def _ours(name: str) -> bool:
     return name.split("<")[0] in ("route_logits_kernel", "topk_kernel", "topk_group_kernel", "group_kernel",
                                   "decode_gateup_kernel", "decode_down_kernel", "combine_kernel", "xsum_kernel",
-                                  "prefill_kernel", "copy_kernel")
+                                  "prefill_kernel", "copy_kernel", "route_token_kernel", "decode_expert_kernel",
+                                  "decode_fused_kernel", "combine_parts_kernel")
 
 
 def _match(values: dict[str, list[float]], kernel: str) -> list[float]:
