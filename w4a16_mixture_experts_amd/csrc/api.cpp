@@ -363,8 +363,9 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   const size_t o_gs = take((rows + 128) * (I / kGroup) * 4);
   const size_t o_xs = take((rows + 128) * (H / kGroup) * 4);
   // fused decode: down-projection partial outputs per 128-wide slice of I
-  const bool fused = path == EXMOE_PATH_DECODE && decode_fused_ok(T, I, E, k);
-  const size_t o_pt = take(fused ? (size_t)(I / kGroup) * rows * H * 4 : 0);
+  const int fused_waves = path == EXMOE_PATH_DECODE ? decode_fused_waves(T, I, E, k) : 0;
+  const int nparts = fused_waves ? I / (kTileRows * fused_waves) : 0;
+  const size_t o_pt = take((size_t)nparts * rows * H * 4);
   const size_t o_sel = take((size_t)E * 16);
   if (a && ws) {
     uint8_t* b = static_cast<uint8_t*>(ws);
@@ -373,8 +374,8 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
     a->y_perm = reinterpret_cast<float*>(b + o_yp);
     a->gsum = reinterpret_cast<float*>(b + o_gs);
     a->xsum = reinterpret_cast<float*>(b + o_xs);
-    a->part = fused ? reinterpret_cast<float*>(b + o_pt) : nullptr;
-    a->nparts = fused ? I / kGroup : 0;
+    a->part = nparts ? reinterpret_cast<float*>(b + o_pt) : nullptr;
+    a->nparts = nparts;
     a->counters = reinterpret_cast<uint32_t*>(b + kWsCounterOffset);
     a->debug = reinterpret_cast<uint32_t*>(b + kWsDebugOffset);
   }

@@ -84,7 +84,7 @@ constexpr int kDecPre = 4;   // per thread: ids <= 2 * 512, offsets <= 257, one 
 struct DecPre {
   int32_t v[kDecPre];
 };
-template <int SRC>
+template <int SRC, int NT>
 __device__ __forceinline__ DecPre dec_preload(const MoeArgs& a, const DecPublish& pub) {
   DecPre pr;
   const int tid = threadIdx.x;
@@ -97,7 +97,7 @@ __device__ __forceinline__ DecPre dec_preload(const MoeArgs& a, const DecPublish
   const int n = SRC == kSrcIds ? a.T * a.k : a.E + 1;
 #pragma unroll
   for (int m = 0; m < kDecPre; m++) {
-    int i = tid + m * kDecThreads;
+    int i = tid + m * NT;
     i = i < n ? i : n - 1;
     pr.v[m] = SRC == kSrcIds ? a.ids[i] : a.offsets[i];
   }
@@ -105,40 +105,43 @@ __device__ __forceinline__ DecPre dec_preload(const MoeArgs& a, const DecPublish
 }
 
 // Every token row of x (T <= kDecTok, H <= kDecKC) into the staging rows, indexed by
-// token: all loads in flight at once, then the stores.
+// token: all loads in flight at once, then the stores. Pieces past the last row load and
+// store the last row's piece again (the same value to the same place), so that no load
+// sits under a branch, where it would be waited for one at a time.
+template <int NT>
 __device__ __forceinline__ void dec_prestage_x(const MoeArgs& a, DecLDS& L) {
-  constexpr int SQ = kDecTok * (kDecKC / 8) / kDecThreads;
+  constexpr int SQ = kDecTok * (kDecKC / 8) / NT;
   const int tid = threadIdx.x;
   const int cw8 = a.H / 8;
   uint4 v[SQ];
+  int dst[SQ];
 #pragma unroll
   for (int m = 0; m < SQ; m++) {
-    const int q = tid + m * kDecThreads;
+    const int q = tid + m * NT;
     int r = q / cw8;
     const int c8 = q - r * cw8;
     r = r < a.T ? r : a.T - 1;
     v[m] = *reinterpret_cast<const uint4*>(a.x + (size_t)r * a.H + c8 * 8);
+    dst[m] = r * kDecXS + c8 * 8;
   }
 #pragma unroll
-  for (int m = 0; m < SQ; m++) {
-    const int q = tid + m * kDecThreads;
-    const int r = q / cw8, c8 = q - r * cw8;
-    if (r < a.T) *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) = v[m];
-  }
+  for (int m = 0; m < SQ; m++) *reinterpret_cast<uint4*>(L.xs + dst[m]) = v[m];
 }
 
 // Publisher of a table-routed launch (the grid's last workgroup): stable grouping of the
 // ids the routing kernel wrote, into the caller's offsets / sorted_flat / flat_to_sorted.
+template <int NT>
 __device__ void dec_publish(const MoeArgs& a, DecLDS& L, const DecPublish& pub) {
   int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);
-  auto& gs = *reinterpret_cast<GroupSharedT<kDecThreads>*>(L.xs + 2 * kDecMaxRows);
+  auto& gs = *reinterpret_cast<GroupSharedT<NT>*>(L.xs + 2 * kDecMaxRows);
+  static_assert(2 * kDecMaxRows * 2 + sizeof(GroupSharedT<NT>) <= sizeof(L.xs), "publisher scratch exceeds the staging rows");
   const int TK = a.T * a.k;
-  for (int f = threadIdx.x; f < TK; f += kDecThreads) ids_l[f] = a.ids[f];
+  for (int f = threadIdx.x; f < TK; f += NT) ids_l[f] = a.ids[f];
   __syncthreads();
-  group_block<kDecThreads>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
+  group_block<NT>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
 }
 
-template <int SRC, bool ALL>
+template <int SRC, bool ALL, int NT>
 __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, const DecPre& pr, int fixed_expert,
                           int aidx, bool first_of_expert, int slot_known, DecExpert& ex) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -158,13 +161,13 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
   } else if (SRC == kSrcIds) {
 #pragma unroll
     for (int m = 0; m < kDecPre; m++)
-      if (tid + m * kDecThreads < TK) ids_l[tid + m * kDecThreads] = pr.v[m];
+      if (tid + m * NT < TK) ids_l[tid + m * NT] = pr.v[m];
   }
   if (SRC != kSrcGiven) {
     if (SRC == kSrcIds) {
-      for (int i = tid; i < a.E; i += kDecThreads) L.cnt[i] = 0;
+      for (int i = tid; i < a.E; i += NT) L.cnt[i] = 0;
       __syncthreads();
-      for (int f = tid; f < TK; f += kDecThreads) {
+      for (int f = tid; f < TK; f += NT) {
         const int e = ids_l[f];
         if ((unsigned)e < (unsigned)a.E) atomicAdd(&L.cnt[e], 1);
       }
@@ -236,14 +239,14 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
     }
     __syncthreads();
     if (first_of_expert) {
-      for (int r = tid; r < ex.cnt; r += kDecThreads) {
+      for (int r = tid; r < ex.cnt; r += NT) {
         const int f = L.rows[r];
         pub.sorted_flat[ex.seg0 + r] = f;
         pub.flat_to_sorted[f] = ex.seg0 + r;
       }
     }
     if (blockIdx.x == 0)
-      for (int i = tid; i <= a.E; i += kDecThreads) pub.offsets[i] = L.off[i];
+      for (int i = tid; i <= a.E; i += NT) pub.offsets[i] = L.off[i];
   }
   if (ex.cnt <= 0) return false;
   const int slot = ALL ? slot_known : a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[ex.e]) : ex.e;
@@ -331,12 +334,22 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
   if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
 
-  const DecPre pre = dec_preload<SRC>(a, pub);
+  // all-experts launch: the expert's slot, loaded first so that its latency overlaps the
+  // activation loads (the publisher's index is clamped; it returns before using it)
+  // (a vector load: a scalar one would be waited for with the kernel arguments)
+  int slot = 0;
+  if (ALL) {
+    const __amdgpu_buffer_rsrc_t er =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
+    slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * (aidx < a.E ? aidx : a.E - 1), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
+  }
+  const DecPre pre = dec_preload<SRC, kDecThreads>(a, pub);
   if (GATEUP && SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
-    dec_publish(a, L, pub);
+    dec_publish<kDecThreads>(a, L, pub);
     return;
   }
-  if (GATEUP && SRC == kSrcSel) dec_prestage_x(a, L);
+  if (GATEUP && SRC == kSrcSel) dec_prestage_x<kDecThreads>(a, L);
   // ALL: the grid covers every expert, so the expert (hence its weights) is known at once:
   // the first ring of weight loads goes out right behind the routing inputs and arrives
   // while the routing is worked out. Loads through a resource of zero length (expert
@@ -344,16 +357,15 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   // anyway keeps every wave's load count fixed, so the waits stay exact.
   WSlot2 W[kDecRing];
   __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
-  int slot = 0;
   if (ALL) {
-    slot = a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[aidx]) : aidx;
+    slot = a.e2s ? __builtin_amdgcn_readfirstlane(slot) : aidx;
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
                                              slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
   DecExpert ex;
-  if (!dec_setup<SRC, ALL>(a, L, pub, pre, fixed_expert, aidx, chunk == 0, slot, ex)) return;
+  if (!dec_setup<SRC, ALL, kDecThreads>(a, L, pub, pre, fixed_expert, aidx, chunk == 0, slot, ex)) return;
   if (!ALL) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
 #pragma unroll
@@ -487,34 +499,43 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
 }
 
 // ------------------------------------------------------------------------------------
-// Fused gate/up + down. Workgroup = (expert, slice c of 128 rows of I); wave w owns row
-// block 8c + w of I. Phase 1 computes h for the slice (gate and up tiles, reduction over
-// H) into LDS; phase 2 applies the slice's 128 columns of W_down, which are exactly input
-// group c of every down tile, to all H outputs: each wave streams the tiles (row block
-// rbd, group c) of its share of H. The result goes to part[c][f][H]; the combine adds the
-// slices and applies the routing weight. h never leaves the chip, and one kernel
-// boundary (its ramp, set-up and tail) disappears. One weight ring runs through both
-// phases: slots 0 .. S1-1 hold gate/up groups, then pairs of down tiles.
+// Fused gate/up + down, NW = 8 or 16 waves. Workgroup = (expert, slice c of RS = 16 NW
+// rows of I); wave w owns row block NW c + w of I. Phase 1 computes h for the slice (gate
+// and up tiles, reduction over H) into LDS; phase 2 applies the slice's RS columns of
+// W_down, which are exactly input groups NCG c .. NCG c + NCG - 1 (NCG = NW / 8) of every
+// down tile row, to all H outputs: each wave streams those tiles for its share of the H
+// row blocks. The result goes to part[c][f][H]; the combine adds the slices and applies
+// the routing weight. h never leaves the chip, and one kernel boundary (its ramp, set-up
+// and tail) disappears. One weight ring runs through both phases: slots 0 .. S1-1 hold
+// gate/up groups, then two down tiles each (two row blocks at NW = 8, the slice's two
+// groups of one row block at NW = 16).
+// With 16 waves one workgroup fills a compute unit: two 8-wave workgroups sharing one do
+// not stream evenly (the older one's waves win the issue arbitration and the younger one
+// ends far later), while the waves of one workgroup meet at its barriers; the token rows
+// are also staged once per compute unit instead of twice, and the slices are twice as
+// wide, which halves the partial outputs the combine reads.
 // ------------------------------------------------------------------------------------
-template <int SRC, bool ALL>
-__global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a, DecPublish pub, int fixed_expert) {
+template <int SRC, bool ALL, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPublish pub, int fixed_expert) {
+  static_assert(NW == 8 || NW == 16, "8 or 16 waves");
+  constexpr int NT = 64 * NW, RS = kTileRows * NW, NCG = NW / 8;
   __shared__ DecLDS L;
-  __shared__ float s_hseed[kDecTok];
+  __shared__ float s_hseed[NCG][kDecTok];
   const int lane = (int)lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x;
-  const int nslice = a.I / kGroup;
+  const int nslice = a.I / RS;
   const int aidx = blockIdx.x / nslice, cs = blockIdx.x % nslice;
 
   const int G = a.H / kGroup;                  // gate/up groups
   const int nK = (a.H + kDecKC - 1) / kDecKC;  // staged chunks of x
   const int S1 = nK * kDecKG;                  // phase-1 ring positions
   const int nrbd = a.H / kTileRows;            // down row blocks
-  const int per_w = (nrbd + kDecWaves - 1) / kDecWaves;     // down row blocks per wave
-  const int npair = (per_w + 1) / 2;
-  const int S2 = (npair + kDecRing - 1) / kDecRing * kDecRing;   // phase-2 ring positions
+  const int per_w = (nrbd + NW - 1) / NW;      // down row blocks per wave
+  const int npos2 = NCG == 1 ? (per_w + 1) / 2 : per_w;          // phase-2 positions in use
+  const int S2 = (npos2 + kDecRing - 1) / kDecRing * kDecRing;   // phase-2 ring positions
   const int ST = S1 + S2;
-  const int rb = cs * kDecWaves + wave;        // gate/up row block of this wave
+  const int rb = cs * NW + wave;               // gate/up row block of this wave
   const int rbd_base = wave * per_w;
   const int Gd = a.I / kGroup;
   const uint32_t sc_base = (uint32_t)(n_tiles(a.H, a.I) * kTileBytes);
@@ -522,7 +543,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
   const int nbytes = (int)packed_bytes(a.H, a.I);
   const uint32_t lo_t = (uint32_t)lane * 16u, lo_s = (uint32_t)(lane >> 4) * 8u;
   const uint32_t tg0 = (uint32_t)(rb * 2) * G, tg1 = (uint32_t)(rb * 2 + 1) * G;
-  // tile indices of ring position s (uniform): gate/up group, or a pair of down tiles
+  // tile indices of ring position s (uniform): gate/up group, or two down tiles
   auto tiles_of = [&](int s, uint32_t& ta, uint32_t& tb) {
     if (s < S1) {
       const int c = s / kDecKG, i = s % kDecKG;
@@ -532,12 +553,19 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
       tb = tg1 + g;
     } else {
       const int pi = s - S1;
-      int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
       const int rmax = rbd_base + per_w - 1 < nrbd - 1 ? rbd_base + per_w - 1 : nrbd - 1;
-      r0 = r0 < rmax ? r0 : rmax;
-      r1 = r1 < rmax ? r1 : rmax;
-      ta = dbase + (uint32_t)r0 * Gd + cs;
-      tb = dbase + (uint32_t)r1 * Gd + cs;
+      if (NCG == 1) {
+        int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
+        r0 = r0 < rmax ? r0 : rmax;
+        r1 = r1 < rmax ? r1 : rmax;
+        ta = dbase + (uint32_t)r0 * Gd + cs;
+        tb = dbase + (uint32_t)r1 * Gd + cs;
+      } else {
+        int r = rbd_base + pi;
+        r = r < rmax ? r : rmax;
+        ta = dbase + (uint32_t)r * Gd + 2 * cs;
+        tb = ta + 1;
+      }
     }
   };
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int s, WSlot2& w) {
@@ -549,28 +577,37 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
     w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + tb * kScaleBytes), 0));
   };
 
-  for (int i = tid; i < kDecXS / 8; i += kDecThreads)
+  for (int i = tid; i < kDecXS / 8; i += NT)
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
   if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
 
-  const DecPre pre = dec_preload<SRC>(a, pub);
-  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
-    dec_publish(a, L, pub);
-    return;
-  }
-  if (SRC == kSrcSel) dec_prestage_x(a, L);
-  WSlot2 W[kDecRing];
-  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
+  // all-experts launch: the expert's slot, loaded first so that its latency overlaps the
+  // activation loads (the publisher's index is clamped; it returns before using it)
+  // (a vector load: a scalar one would be waited for with the kernel arguments)
   int slot = 0;
   if (ALL) {
-    slot = a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[aidx]) : aidx;
+    const __amdgpu_buffer_rsrc_t er =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
+    slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * (aidx < a.E ? aidx : a.E - 1), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
+  }
+  const DecPre pre = dec_preload<SRC, NT>(a, pub);
+  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+    dec_publish<NT>(a, L, pub);
+    return;
+  }
+  if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  WSlot2 W[kDecRing];
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
+  if (ALL) {
+    slot = a.e2s ? __builtin_amdgcn_readfirstlane(slot) : aidx;
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
                                              slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
   DecExpert ex;
-  if (!dec_setup<SRC, ALL>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) return;
+  if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) return;
   if (!ALL) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
 #pragma unroll
@@ -601,7 +638,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
       __syncthreads();   // previous chunk consumed; pass row list visible
       if (SRC != kSrcSel) {   // table routing: every token row is already staged
         const int cw8 = kcw / 8;
-        for (int q = tid; q < nrow * cw8; q += kDecThreads) {
+        for (int q = tid; q < nrow * cw8; q += NT) {
           const int r = q / cw8, c8 = q - r * cw8;
           *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) = *reinterpret_cast<const uint4*>(
               a.x + (size_t)(L.pf[r] / a.k) * a.H + kc0 + c8 * 8);
@@ -609,7 +646,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
       }
       __syncthreads();
       const int nstaged = SRC == kSrcSel ? a.T : nrow;   // rows indexed by token or by slot
-      for (int q = tid; q < nstaged * ngc * 2; q += kDecThreads) {
+      for (int q = tid; q < nstaged * ngc * 2; q += NT) {
         const int r = q / (ngc * 2), gg = (q >> 1) % ngc, half = q & 1;
         const uint16_t* src = L.xs + r * kDecXS + gg * kGroup + half * 64;
         float sm = 0.f;
@@ -656,9 +693,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
         }
       }
     }
-    // ---- h of the slice into LDS (bf16, [token][128 + skew]), and its correction seeds
+    // ---- h of the slice into LDS (bf16, [token][RS + skew]), and its correction seeds
     __syncthreads();   // all waves done with the staged activations
-    constexpr int kHS = kGroup + 8;
+    constexpr int kHS = RS + 8;
     uint16_t* hs = L.xs;
     {
       // padding token slots computed from the zero row: their h is 0
@@ -671,49 +708,60 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_fused_kernel(MoeArgs a,
       *reinterpret_cast<uint2*>(hs + (lane & 15) * kHS + wave * 16 + 4 * (lane >> 4)) = pk;
     }
     __syncthreads();
-    if (wave == 0) {
-      // -136 * sum of the token's 128 h values: four quarter sums, added in a fixed order
-      const uint16_t* hr = hs + (lane & 15) * kHS + 32 * (lane >> 4);
+    if (wave < NCG) {
+      // -136 * sum of the token's 128 h values of group `wave`: four quarter sums, added
+      // in a fixed order
+      const uint16_t* hr = hs + (lane & 15) * kHS + wave * kGroup + 32 * (lane >> 4);
       float sm = 0.f;
       for (int i = 0; i < 32; i++) sm += bf16_to_f32(hr[i]);
       sm += __shfl_xor(sm, 16);
       sm += __shfl_xor(sm, 32);
-      if (lane < kDecTok) s_hseed[lane] = -136.0f * sm;
+      if (lane < kDecTok) s_hseed[wave][lane] = -136.0f * sm;
     }
     __syncthreads();
-    // ---- phase 2: the slice's down column group over all H rows of this wave's share
-    bf16x8 acth[4];
+    // ---- phase 2: the slice's down column groups over all H rows of this wave's share
+    bf16x8 acth[NCG][4];
+    float sdh[NCG];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; s4++)
-      acth[s4] = *reinterpret_cast<const bf16x8*>(hs + (lane & 15) * kHS + 32 * s4 + 8 * (lane >> 4));
-    const float sdh = s_hseed[lane & 15];
+    for (int g = 0; g < NCG; g++) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++)
+        acth[g][s4] = *reinterpret_cast<const bf16x8*>(hs + (lane & 15) * kHS + g * kGroup + 32 * s4 + 8 * (lane >> 4));
+      sdh[g] = s_hseed[g][lane & 15];
+    }
     const int f = L.pf[lane & 15];
     float* prow = a.part + ((size_t)cs * a.T * a.k + (f >= 0 ? f : 0)) * a.H + 4 * (lane >> 4);
+    const int lim = rbd_base + per_w < nrbd ? rbd_base + per_w : nrbd;
 #pragma unroll
     for (int i0 = 0; i0 < S2; i0 += kDecRing) {
 #pragma unroll
       for (int j = 0; j < kDecRing; j++) {
         const int pi = i0 + j;
-        if (pi < npair) {
-          const int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
-          const int lim = rbd_base + per_w < nrbd ? rbd_base + per_w : nrbd;
-          f32x4 c0 = {sdh, sdh, sdh, sdh}, c1 = c0;
-          c0 = mfma16(dequant_word(W[j].w[0].x), acth[0], c0);
-          c1 = mfma16(dequant_word(W[j].w[1].x), acth[0], c1);
-          c0 = mfma16(dequant_word(W[j].w[0].y), acth[1], c0);
-          c1 = mfma16(dequant_word(W[j].w[1].y), acth[1], c1);
-          c0 = mfma16(dequant_word(W[j].w[0].z), acth[2], c0);
-          c1 = mfma16(dequant_word(W[j].w[1].z), acth[2], c1);
-          c0 = mfma16(dequant_word(W[j].w[0].w), acth[3], c0);
-          c1 = mfma16(dequant_word(W[j].w[1].w), acth[3], c1);
-          f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
-          scale_accum(o0, c0, W[j].s[0]);
-          scale_accum(o1, c1, W[j].s[1]);
+        if (pi < npos2) {
+          // NW = 8: tiles of row blocks r0, r0 + 1, one group each; NW = 16: the two
+          // groups of row block r0, summed into one output
+          const bf16x8* o1 = acth[NCG - 1];
+          f32x4 c0 = {sdh[0], sdh[0], sdh[0], sdh[0]}, c1 = {sdh[NCG - 1], sdh[NCG - 1], sdh[NCG - 1], sdh[NCG - 1]};
+          c0 = mfma16(dequant_word(W[j].w[0].x), acth[0][0], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].x), o1[0], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].y), acth[0][1], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].y), o1[1], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].z), acth[0][2], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].z), o1[2], c1);
+          c0 = mfma16(dequant_word(W[j].w[0].w), acth[0][3], c0);
+          c1 = mfma16(dequant_word(W[j].w[1].w), o1[3], c1);
+          f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = oa;
+          scale_accum(oa, c0, W[j].s[0]);
+          scale_accum(NCG == 1 ? ob : oa, c1, W[j].s[1]);
           if (f >= 0) {
-            if (r0 < lim)
-              *reinterpret_cast<float4*>(prow + r0 * 16) = make_float4(o0[0], o0[1], o0[2], o0[3]);
-            if (r1 < lim)
-              *reinterpret_cast<float4*>(prow + r1 * 16) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+            if (NCG == 1) {
+              const int r0 = rbd_base + 2 * pi, r1 = r0 + 1;
+              if (r0 < lim) *reinterpret_cast<float4*>(prow + r0 * 16) = make_float4(oa[0], oa[1], oa[2], oa[3]);
+              if (r1 < lim) *reinterpret_cast<float4*>(prow + r1 * 16) = make_float4(ob[0], ob[1], ob[2], ob[3]);
+            } else {
+              const int r0 = rbd_base + pi;
+              if (r0 < lim) *reinterpret_cast<float4*>(prow + r0 * 16) = make_float4(oa[0], oa[1], oa[2], oa[3]);
+            }
           }
         }
         next_issue(S1 + i0 + j + kDecRing, W[j]);
@@ -820,9 +868,14 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
     EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
 }
 
-bool decode_fused_ok(int T, int I, int E, int k) {
-  const long long ny = E < (long long)T * k ? E : (long long)T * k;
-  return I / kGroup <= 16 && ny * (I / kGroup) >= 256;
+int decode_fused_waves(int T, int I, int E, int k) {
+  const long long tk = (long long)T * k;
+  const long long ny = E < tk ? E : tk;
+  // most experts active and one 16-wave workgroup per compute unit or more: 16 waves
+  if (tk >= 2LL * E && I % (2 * kGroup) == 0 && I / (2 * kGroup) <= 8 && (long long)E * (I / (2 * kGroup)) >= 256)
+    return 16;
+  if (I / kGroup <= 16 && ny * (I / kGroup) >= 256) return 8;
+  return 0;
 }
 
 static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub, int fixed_expert, int ny,
@@ -830,14 +883,19 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
   if (a.nparts > 0 && fixed_expert < 0) {
     ProfScope prof("decode_fused", s);
     const bool all = (long long)a.T * a.k >= 2LL * a.E;
-    const int nslice = a.I / kGroup;
-    const int extra = pub && pub->sel ? 1 : 0;   // the publisher workgroup
-    const dim3 grid((all ? a.E : ny) * nslice + extra), block(kDecThreads);
+    const int nw = a.I / (kTileRows * a.nparts);   // the workspace layout chose the width
+    const int extra = pub && pub->sel ? 1 : 0;     // the publisher workgroup
     const DecPublish none{};
-#define EXMOE_FUSED(SRC, P)                                                                                   \
-  do {                                                                                                       \
-    if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true>), grid, block, 0, s, a, P, fixed_expert);    \
-    else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false>), grid, block, 0, s, a, P, fixed_expert);       \
+#define EXMOE_FUSED(SRC, P)                                                                                      \
+  do {                                                                                                          \
+    const dim3 grid((all ? a.E : ny) * a.nparts + extra);                                                       \
+    if (nw == 16) {                                                                                             \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, a, P, fixed_expert); \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, a, P, fixed_expert);    \
+    } else {                                                                                                    \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, a, P, fixed_expert);   \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, a, P, fixed_expert);      \
+    }                                                                                                           \
   } while (0)
     if (!pub) EXMOE_FUSED(kSrcGiven, none);
     else if (pub->sel) EXMOE_FUSED(kSrcSel, *pub);
