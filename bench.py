@@ -93,7 +93,13 @@ def bytes_per_call(exm, torch, lay_syn, shape, wr, xs_dev, T, bias=None):
     return np.array(D)
 
 
-def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0):
+SPAN_KERNELS = ("decode_gateup", "decode_down", "decode_fused", "combine", "prefill_gateup", "prefill_down")
+
+
+def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0, spans=None):
+    """Milliseconds per layer call over `steps` calls (one graph replay, or eager calls).
+    With a dict in `spans`, the expert-layer kernels of those same timed calls stamp their
+    launch spans in-kernel, and spans[name] = (average microseconds, launches)."""
     shape = wl.shape
     bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k, flags)
     wr = wl.layer["wr"]
@@ -105,6 +111,8 @@ def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    if spans is not None:
+        exm.span_enable(steps * 8)   # slots for the launches below (captured or eager)
     graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
@@ -120,6 +128,8 @@ def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if spans is not None:
+        exm.span_clear()
     e0.record()
     if graph is not None:
         graph.replay()
@@ -129,16 +139,28 @@ def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    if spans is not None:
+        for n in SPAN_KERNELS:
+            us, cnt = exm.span_read(n)
+            if cnt:
+                spans[n] = (us / cnt, cnt)
+        exm.span_enable(0)
     return ms / steps
 
 
 def kernel_times(exm, torch, wl, steps, names):
-    """Average launch time of each named kernel: HIP events around every launch."""
+    """Average launch time of each named kernel: HIP events around every launch. The GPU
+    first spins for a while on the same stream, so that the host has queued the launches
+    before they run and they execute back to back, as in the timed graph replay (a start
+    event recorded while the GPU waits for the host would count that wait)."""
     shape = wl.shape
     bufs = exm.LayerBuffers(wl.T, shape.H, shape.I, shape.E, shape.k)
     wr = wl.layer["wr"]
+    exm.moe_layer(wl.xs[0], wr, wl.banks[0], shape.I, shape.k, bias=wl.bias, buffers=bufs)   # warm
+    torch.cuda.synchronize()
     exm.profile_reset()
     exm.profile_enable(True)
+    torch.cuda._sleep(int(2.0e9 * 0.05))   # ~50 ms of spinning at ~2 GHz
     for i in range(steps):
         exm.moe_layer(wl.xs[i % len(wl.xs)], wr, wl.banks[i % len(wl.banks)], shape.I, shape.k, bias=wl.bias,
                       buffers=bufs)
@@ -224,23 +246,28 @@ def main():
         xs = [to_dev_bf16(olmoe_syn.x(T, stream=s)) for s in range(64)]
         wl = Workload(f"olmoe_decode_T{T}", OLMOE, T, {"wr": wr}, banks, xs)
         D = bytes_per_call(exm, torch, olmoe_syn, OLMOE, wr, xs, T)
-        ms = time_layer(exm, torch, wl, steps, warmup, use_graph)
+        spans = {}
+        ms = time_layer(exm, torch, wl, steps, warmup, use_graph, spans=spans)
         layer_bytes = D.mean() * expert_bytes + E * H * 2 + 2 * T * H * 2 + T * k * 8
         rec = {"T": T, "tokens_per_s": T / (ms * 1e-3), "us_per_layer": ms * 1e3,
                "distinct_experts_mean": float(D.mean()),
                "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if want_kernels:
-            kt = kernel_times(exm, torch, wl, min(steps, 256),
-                              ["route_logits", "route_token", "topk", "group", "topk_group", "decode_gateup", "decode_down", "decode_fused", "combine"])
+            kt = kernel_times(exm, torch, wl, min(steps, 128),
+                              ["route_logits", "route_token", "route_sel", "topk", "group", "topk_group", "decode_gateup", "decode_down",
+                               "decode_fused", "combine"])
             rec["kernel_us"] = {n: v[0] * 1e3 for n, v in kt.items()}
-            if "decode_fused" in kt:
+            rec["kernel_span_us"] = {n: v[0] for n, v in spans.items()}
+            # the roofline's kernel duration: in-kernel span stamps of the timed calls
+            if "decode_fused" in spans:
                 # gate/up and down in one kernel: weights of every active expert, x in,
-                # one fp32 output row per routed row
-                kname, ms_k = "decode_fused_kernel", kt["decode_fused"][0]
+                # one fp32 output row per routed row (the kernel writes one per slice of I:
+                # traffic above this minimum)
+                kname, ms_k = "decode_fused_kernel", spans["decode_fused"][0] * 1e-3
                 alg = D.mean() * expert_bytes + T * H * 2 + T * k * H * 4
             else:
-                kname, ms_k = "decode_expert_kernel", kt["decode_gateup"][0]   # its gate/up instance
+                kname, ms_k = "decode_expert_kernel", spans["decode_gateup"][0] * 1e-3   # its gate/up instance
                 alg = D.mean() * gu_bytes + T * H * 2 + T * k * I * 2
             tr = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{kname.replace('_kernel', '')}_olmoe_decode_T{T}.txt"),
                               kname)
@@ -250,8 +277,8 @@ def main():
                                "algorithmic_bytes_per_launch": alg, "avg_launch_us": ms_k * 1e3}
             if tr is not None:
                 rec["roofline"]["traffic_over_algorithmic"] = tr["bytes"] / alg
-            if "decode_down" in kt:
-                ms_d = kt["decode_down"][0]
+            if "decode_down" in spans:
+                ms_d = spans["decode_down"][0] * 1e-3
                 d_alg = D.mean() * down_bytes + T * k * I * 2 + T * k * H * 4 + T * k * 4
                 rec["down_kernel"] = {"achieved_gbs": d_alg / (ms_d * 1e-3) / 1e9, "avg_launch_us": ms_d * 1e3,
                                       "algorithmic_bytes_per_launch": d_alg}
@@ -360,21 +387,23 @@ def main():
         xs = [to_dev_bf16(syn.x(T, stream=s)) for s in range(4)]
         bias_t = None if bias is None else torch.from_numpy(bias).cuda()
         wl = Workload(name, shape, T, {"wr": wr_p}, banks_p, xs, bias_t)
-        ms = time_layer(exm, torch, wl, steps, warmup, use_graph)
+        spans = {}
+        ms = time_layer(exm, torch, wl, steps, warmup, use_graph, spans=spans)
         flops = 6.0 * T * shape.k * shape.H * shape.I
         kt = kernel_times(exm, torch, wl, min(steps, 8), ["prefill_gateup", "prefill_down", "xsum", "combine",
                                                           "route_logits", "topk", "group", "decode_gateup",
                                                           "decode_down"])
         rec = {"T": T, "tokens_per_s": T / (ms * 1e-3), "ms_per_layer": ms, "layer_tflops": flops / (ms * 1e-3) / 1e12,
                "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-               "kernel_us": {n: v[0] * 1e3 for n, v in kt.items()}}
-        if "prefill_gateup" in kt:
+               "kernel_us": {n: v[0] * 1e3 for n, v in kt.items()},
+               "kernel_span_us": {n: v[0] for n, v in spans.items()}}
+        if "prefill_gateup" in spans:
             gu_fl = 4.0 * T * shape.k * shape.H * shape.I
-            rec["gateup_tflops"] = gu_fl / (kt["prefill_gateup"][0] * 1e-3) / 1e12
+            rec["gateup_tflops"] = gu_fl / (spans["prefill_gateup"][0] * 1e-6) / 1e12
             rec["gateup_mfma_frac"] = rec["gateup_tflops"] / BF16_PEAK_TFLOPS
-        if "prefill_down" in kt:
+        if "prefill_down" in spans:
             d_fl = 2.0 * T * shape.k * shape.H * shape.I
-            rec["down_tflops"] = d_fl / (kt["prefill_down"][0] * 1e-3) / 1e12
+            rec["down_tflops"] = d_fl / (spans["prefill_down"][0] * 1e-6) / 1e12
         log(f"{name}: {rec['tokens_per_s']:.0f} tok/s, {ms:.3f} ms/layer, {rec['layer_tflops']:.1f} TFLOP/s "
             f"({rec['layer_mfma_frac'] * 100:.1f}% of bf16 MFMA)")
         return rec

@@ -241,12 +241,29 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
  * own start and end on its launch stream (hipExtLaunchKernelGGL; skipped on a stream that
  * is being captured into a graph). exmoe_profile_read
  * synchronizes the recorded events and returns the accumulated milliseconds and launch
- * count of one kernel by name: "route_logits", "topk", "group", "decode_gateup",
- * "decode_down", "combine", "xsum", "prefill_gateup", "prefill_down". Process-global.
+ * count of one kernel by name: "route_logits", "route_token", "route_sel", "topk",
+ * "group", "decode_gateup", "decode_down", "decode_fused", "combine", "xsum",
+ * "prefill_gateup", "prefill_down". Process-global. The events bracket the launch as the
+ * stream processes it, so a launch that waits for the host is counted with that wait.
  * ---------------------------------------------------------------------------------- */
 int exmoe_profile_enable(int on);
 int exmoe_profile_reset(void);
 int exmoe_profile_read(const char* kernel_name, double* total_ms, uint64_t* launches);
+
+/* Launch span stamps (benchmark timing; not part of the layer's semantics). After
+ * exmoe_span_enable(n) (n > 0; allocates 1 KiB of device memory per slot, n = 0 frees them),
+ * each of the next n launches of the expert-layer kernels ("decode_gateup", "decode_down",
+ * "decode_fused", "combine", "prefill_gateup", "prefill_down") takes one slot, also while
+ * its stream is captured into a graph: its workgroups stamp the GPU's constant-rate clock
+ * at their start (minimum) and after their last memory operation (maximum).
+ * exmoe_span_read synchronizes the device and returns, for one kernel name, the summed
+ * durations in microseconds and the number of slots that ran since the last
+ * exmoe_span_clear (which resets the stamps and keeps the slots' assignment, so that a
+ * captured graph can be replayed and measured again). Process-global; not thread-safe
+ * against concurrent layer calls that take slots. */
+int exmoe_span_enable(int max_launches);
+int exmoe_span_clear(void);
+int exmoe_span_read(const char* kernel_name, double* total_us, uint64_t* launches);
 
 /* Plain device copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned),
  * one pass of 16-byte loads and stores, asynchronous on `stream`. Not part of the layer:

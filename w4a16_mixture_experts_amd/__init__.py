@@ -86,6 +86,9 @@ _SIGS = {
     "exmoe_profile_enable": (_i, [_i]),
     "exmoe_profile_reset": (_i, []),
     "exmoe_profile_read": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]),
+    "exmoe_span_enable": (_i, [_i]),
+    "exmoe_span_clear": (_i, []),
+    "exmoe_span_read": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]),
     "exmoe_device_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -370,6 +373,24 @@ def profile_read(kernel: str):
     n = ctypes.c_uint64(0)
     _check(_lib.exmoe_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def span_enable(max_launches: int):
+    """Launch span stamps for the next `max_launches` expert-layer kernel launches (0: off)."""
+    _check(_lib.exmoe_span_enable(int(max_launches)))
+
+
+def span_clear():
+    """Reset the span stamps, keeping the slots' assignment (replay a graph, then read)."""
+    _check(_lib.exmoe_span_clear())
+
+
+def span_read(kernel: str):
+    """(total microseconds, launches) of one kernel's spans since the last clear."""
+    us = ctypes.c_double(0.0)
+    n = ctypes.c_uint64(0)
+    _check(_lib.exmoe_span_read(kernel.encode(), ctypes.byref(us), ctypes.byref(n)))
+    return us.value, n.value
 
 
 def device_copy(dst, src):

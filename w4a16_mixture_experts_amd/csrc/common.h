@@ -17,6 +17,7 @@ constexpr int kTileBytes = 1024; // 16 rows x 128 inputs x 4 bits
 constexpr int kScaleBytes = 32;  // 16 bf16 scales per tile
 constexpr int kMaxExperts = 256;
 constexpr int kMaxK = 64;
+constexpr int kSpanSub = 64;     // sub-slots of a launch span slot (by workgroup index)
 constexpr int kMaxDim = 16384;   // largest hidden / intermediate size (zero-row length)
 
 __host__ __device__ inline size_t n_tiles(int H, int I) {
@@ -50,6 +51,9 @@ class ProfScope {
   hipEvent_t start() const { return a_; }
   hipEvent_t stop() const { return b_; }
   void used() { used_ = true; }
+  // Next launch span slot while span stamps are enabled (also under stream capture), else
+  // null. The slot is tagged with this scope's kernel name.
+  unsigned long long* span();
 
  private:
   const char* name_;
@@ -70,6 +74,7 @@ class ProfScope {
   } while (0)
 
 // ---- kernel launchers (defined in the .hip files); each returns a HIP error code
+hipError_t span_fill(unsigned long long* p, int n, hipStream_t s);
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
@@ -102,6 +107,7 @@ struct MoeArgs {
   uint8_t* sel;       // u8 [E][16]: decode expert table, sel[e][t] = slot + 1 of token t (0: not routed)
   uint32_t* counters; // arrival counters of the routing kernel (zero between launches)
   uint32_t* debug;    // debug word(s)
+  unsigned long long* span;   // launch span slot (benchmark timing) or null
 };
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "common.h"
+
 namespace exmoe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
@@ -62,6 +64,25 @@ __device__ __forceinline__ void scale_accum(f32x4& acc, const f32x4& c, uint2 sc
   acc[1] += __uint_as_float(sc.x & 0xFFFF0000u) * c[1];
   acc[2] += __uint_as_float(sc.y << 16) * c[2];
   acc[3] += __uint_as_float(sc.y & 0xFFFF0000u) * c[3];
+}
+
+// Launch span stamps (benchmark timing, off when sp is null): the first thread of every
+// workgroup folds the GPU's constant-rate clock into its sub-slot of the launch's slot
+// (kSpanSub sub-slots, by workgroup index, so that few workgroups share an address):
+// minimum at its start, maximum after all of its waves' memory operations have completed.
+// The launch's duration is the largest end minus the smallest start, inside a replayed
+// graph too.
+__device__ __forceinline__ void span_begin(unsigned long long* sp) {
+  if (sp && threadIdx.x == 0)
+    atomicMin(sp + 2 * (blockIdx.x % kSpanSub), (unsigned long long)__builtin_amdgcn_s_memrealtime());
+}
+__device__ __forceinline__ void span_end(unsigned long long* sp) {
+  if (sp) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      atomicMax(sp + 2 * (blockIdx.x % kSpanSub) + 1, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+  }
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

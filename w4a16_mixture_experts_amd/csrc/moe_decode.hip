@@ -277,6 +277,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   __shared__ DecLDS L;
   const int lane = (int)lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  span_begin(a.span);
   const int tid = threadIdx.x;
   const int aidx = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
 
@@ -496,6 +497,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
     }
     __syncthreads();   // pass row list and reduction space free for the next pass
   }
+  span_end(a.span);
 }
 
 // ------------------------------------------------------------------------------------
@@ -520,9 +522,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   static_assert(NW == 8 || NW == 16, "8 or 16 waves");
   constexpr int NT = 64 * NW, RS = kTileRows * NW, NCG = NW / 8;
   __shared__ DecLDS L;
-  __shared__ float s_hseed[NCG][kDecTok];
   const int lane = (int)lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  span_begin(a.span);
   const int tid = threadIdx.x;
   const int nslice = a.I / RS;
   const int aidx = blockIdx.x / nslice, cs = blockIdx.x % nslice;
@@ -543,6 +545,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   const int nbytes = (int)packed_bytes(a.H, a.I);
   const uint32_t lo_t = (uint32_t)lane * 16u, lo_s = (uint32_t)(lane >> 4) * 8u;
   const uint32_t tg0 = (uint32_t)(rb * 2) * G, tg1 = (uint32_t)(rb * 2 + 1) * G;
+  const bf16x8 n136 = neg136_operand();
   // tile indices of ring position s (uniform): gate/up group, or two down tiles
   auto tiles_of = [&](int s, uint32_t& ta, uint32_t& tb) {
     if (s < S1) {
@@ -579,7 +582,6 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 
   for (int i = tid; i < kDecXS / 8; i += NT)
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < kDecKG) L.seed[kDecTok * kDecKG + tid] = 0.f;
 
   // all-experts launch: the expert's slot, loaded first so that its latency overlaps the
   // activation loads (the publisher's index is clamped; it returns before using it)
@@ -591,7 +593,17 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * (aidx < a.E ? aidx : a.E - 1), 0, 0);
     __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
   }
-  const DecPre pre = dec_preload<SRC, NT>(a, pub);
+  // table routing with every expert launched: this expert's 16-byte table row in every
+  // lane (a vector load, like the slot's)
+  constexpr bool kSelAll = SRC == kSrcSel && ALL;
+  uint4 selrow = make_uint4(0u, 0u, 0u, 0u);
+  DecPre pre;
+  if (kSelAll) {
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.sel, (short)0, a.E * kSelStride, 0x00020000);
+    selrow = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, (aidx < a.E ? aidx : a.E - 1) * kSelStride, 0, 0));
+  } else {
+    pre = dec_preload<SRC, NT>(a, pub);
+  }
   if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
     dec_publish<NT>(a, L, pub);
     return;
@@ -607,7 +619,26 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
   DecExpert ex;
-  if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) return;
+  if (kSelAll) {
+    // the expert's tokens, ascending, straight from its table row: no grouping needed
+    const uint32_t wd = (lane & 15) < 4 ? selrow.x : (lane & 15) < 8 ? selrow.y : (lane & 15) < 12 ? selrow.z : selrow.w;
+    const int sb = lane < a.T ? (int)((wd >> (8 * (lane & 3))) & 0xFFu) : 0;
+    const uint64_t m = __ballot(sb > 0);
+    if (wave == 0 && sb > 0) L.srows[__popcll(m & ((1ull << lane) - 1ull))] = lane * a.k + sb - 1;
+    ex.e = aidx;
+    ex.seg0 = 0;
+    ex.cnt = __popcll(m);
+    __syncthreads();   // token list and activation rows visible
+    if (ex.cnt == 0) return;
+    if (slot < 0) {
+      if (tid == 0) atomicOr(a.debug, 1u);   // routed expert without a slot
+      return;
+    }
+    ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
+    ex.scales = nullptr;
+  } else if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) {
+    return;
+  }
   if (!ALL) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
 #pragma unroll
@@ -645,28 +676,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
         }
       }
       __syncthreads();
-      const int nstaged = SRC == kSrcSel ? a.T : nrow;   // rows indexed by token or by slot
-      for (int q = tid; q < nstaged * ngc * 2; q += NT) {
-        const int r = q / (ngc * 2), gg = (q >> 1) % ngc, half = q & 1;
-        const uint16_t* src = L.xs + r * kDecXS + gg * kGroup + half * 64;
-        float sm = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * i);
-          const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            sm += __uint_as_float(q4[m] << 16);
-            sm += __uint_as_float(q4[m] & 0xFFFF0000u);
-          }
-        }
-        const float o = __shfl_xor(sm, 1);
-        if (!half) L.seed[r * kDecKG + gg] = -136.0f * (sm + o);
-      }
-      __syncthreads();
       const int myrow = (lane & 15) < nrow ? (SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
       const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
-      const float* srow = L.seed + myrow * kDecKG;
 #pragma unroll
       for (int i0 = 0; i0 < kDecKG; i0 += kDecRing) {
 #pragma unroll
@@ -676,8 +687,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
             bf16x8 act[4];
 #pragma unroll
             for (int s4 = 0; s4 < 4; s4++) act[s4] = *reinterpret_cast<const bf16x8*>(xrow + gl * kGroup + 32 * s4);
-            const float sd = srow[gl];
-            f32x4 c0 = {sd, sd, sd, sd}, c1 = c0;
+            // seed: -136 * (sum of the group's activations of the token), by MFMA
+            f32x4 sd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; s4++) sd = mfma16(n136, act[s4], sd);
+            f32x4 c0 = sd, c1 = sd;
             c0 = mfma16(dequant_word(W[j].w[0].x), act[0], c0);
             c1 = mfma16(dequant_word(W[j].w[1].x), act[0], c1);
             c0 = mfma16(dequant_word(W[j].w[0].y), act[1], c0);
@@ -708,26 +722,18 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
       *reinterpret_cast<uint2*>(hs + (lane & 15) * kHS + wave * 16 + 4 * (lane >> 4)) = pk;
     }
     __syncthreads();
-    if (wave < NCG) {
-      // -136 * sum of the token's 128 h values of group `wave`: four quarter sums, added
-      // in a fixed order
-      const uint16_t* hr = hs + (lane & 15) * kHS + wave * kGroup + 32 * (lane >> 4);
-      float sm = 0.f;
-      for (int i = 0; i < 32; i++) sm += bf16_to_f32(hr[i]);
-      sm += __shfl_xor(sm, 16);
-      sm += __shfl_xor(sm, 32);
-      if (lane < kDecTok) s_hseed[wave][lane] = -136.0f * sm;
-    }
-    __syncthreads();
-    // ---- phase 2: the slice's down column groups over all H rows of this wave's share
+    // ---- phase 2: the slice's down column groups over all H rows of this wave's share;
+    // the seeds -136 * (sum of h over each group) come from the same MFMA against -136
     bf16x8 acth[NCG][4];
-    float sdh[NCG];
+    f32x4 sdh[NCG];
 #pragma unroll
     for (int g = 0; g < NCG; g++) {
+      sdh[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s4 = 0; s4 < 4; s4++)
+      for (int s4 = 0; s4 < 4; s4++) {
         acth[g][s4] = *reinterpret_cast<const bf16x8*>(hs + (lane & 15) * kHS + g * kGroup + 32 * s4 + 8 * (lane >> 4));
-      sdh[g] = s_hseed[g][lane & 15];
+        sdh[g] = mfma16(n136, acth[g][s4], sdh[g]);
+      }
     }
     const int f = L.pf[lane & 15];
     float* prow = a.part + ((size_t)cs * a.T * a.k + (f >= 0 ? f : 0)) * a.H + 4 * (lane >> 4);
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
           // NW = 8: tiles of row blocks r0, r0 + 1, one group each; NW = 16: the two
           // groups of row block r0, summed into one output
           const bf16x8* o1 = acth[NCG - 1];
-          f32x4 c0 = {sdh[0], sdh[0], sdh[0], sdh[0]}, c1 = {sdh[NCG - 1], sdh[NCG - 1], sdh[NCG - 1], sdh[NCG - 1]};
+          f32x4 c0 = sdh[0], c1 = sdh[NCG - 1];
           c0 = mfma16(dequant_word(W[j].w[0].x), acth[0][0], c0);
           c1 = mfma16(dequant_word(W[j].w[1].x), o1[0], c1);
           c0 = mfma16(dequant_word(W[j].w[0].y), acth[0][1], c0);
@@ -769,6 +775,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     }
     __syncthreads();   // pass row list and LDS free for the next pass
   }
+  span_end(a.span);
 }
 
 // ------------------------------------------------------------------------------------
@@ -776,6 +783,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 // ------------------------------------------------------------------------------------
 constexpr int kCombineTok = 16;
 __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
+  span_begin(a.span);
   const int t0 = blockIdx.y * kCombineTok;
   const int t1 = t0 + kCombineTok < a.T ? t0 + kCombineTok : a.T;
   const int row0 = blockIdx.x * 64;
@@ -791,6 +799,7 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
     pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
     *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
   }
+  span_end(a.span);
 }
 
 // combine of the fused decode: y[t] = bf16(sum over slots j in order of w[t k + j] times
@@ -799,6 +808,7 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 constexpr int kCombCols = 128;
 __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
   __shared__ float4 red[kMaxK][kCombCols / 4];
+  span_begin(a.span);
   const int t = blockIdx.y;
   const int col0 = blockIdx.x * kCombCols;
   const size_t slice = (size_t)a.T * a.k * a.H;
@@ -832,6 +842,7 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
       *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
     }
   }
+  span_end(a.span);
 }
 
 // ------------------------------------------------------------------------------------
@@ -851,9 +862,11 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
   const int per1 = GATEUP ? a.I / (kTileRows * kDecWaves) : (a.H / kTileRows + 2 * kDecWaves - 1) / (2 * kDecWaves);
   const dim3 block(kDecThreads);
   const int extra = GATEUP && SRC == kSrcSel ? 1 : 0;   // the publisher workgroup
+  MoeArgs as = a;
+  as.span = prof.span();
   if (fixed_expert < 0 && (long long)a.T * a.k >= 2LL * a.E) {
     // most experts active: one row of workgroups per expert (no active-expert list)
-    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, true>), dim3(a.E * per1 + extra), block, 0, s, a, pub,
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, true>), dim3(a.E * per1 + extra), block, 0, s, as, pub,
                  fixed_expert, per1);
     return;
   }
@@ -861,11 +874,11 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
   const int nchunk = per1 * ks;
   const dim3 grid(ny * nchunk + extra);
   if (ks == 1)
-    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 1, false>), grid, block, 0, s, as, pub, fixed_expert, nchunk);
   else if (ks == 2)
-    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 2, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 2, false>), grid, block, 0, s, as, pub, fixed_expert, nchunk);
   else
-    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, a, pub, fixed_expert, nchunk);
+    EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, as, pub, fixed_expert, nchunk);
 }
 
 int decode_fused_waves(int T, int I, int E, int k) {
@@ -886,15 +899,17 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
     const int nw = a.I / (kTileRows * a.nparts);   // the workspace layout chose the width
     const int extra = pub && pub->sel ? 1 : 0;     // the publisher workgroup
     const DecPublish none{};
+    MoeArgs as = a;
+    as.span = prof.span();
 #define EXMOE_FUSED(SRC, P)                                                                                      \
   do {                                                                                                          \
     const dim3 grid((all ? a.E : ny) * a.nparts + extra);                                                       \
     if (nw == 16) {                                                                                             \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, a, P, fixed_expert); \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, a, P, fixed_expert);    \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert); \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert);    \
     } else {                                                                                                    \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, a, P, fixed_expert);   \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, a, P, fixed_expert);      \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert);   \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, as, P, fixed_expert);      \
     }                                                                                                           \
   } while (0)
     if (!pub) EXMOE_FUSED(kSrcGiven, none);
@@ -950,11 +965,13 @@ hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipSt
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   ProfScope prof("combine", s);
+  MoeArgs as = a;
+  as.span = prof.span();
   if (a.nparts > 0) {
-    EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, a);
+    EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, as);
     return hipGetLastError();
   }
-  EXMOE_LAUNCH(prof, combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, a);
+  EXMOE_LAUNCH(prof, combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, as);
   return hipGetLastError();
 }
 

@@ -102,6 +102,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   __shared__ int s_scan[kMaxExperts + 1];
   __shared__ float s_gsum[NW][kPfBN];
 
+  span_begin(a.span);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile addresses stay scalar
   const int rt = blockIdx.x % n_row_tiles;
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         }
       }
   }
+  span_end(a.span);
 }
 
 // Correction seeds of the gate/up kernel: xsum[g][r] = -136 * (sum over group g of the
@@ -350,13 +352,17 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
   const int rt_gu = a.I / 128;
   {
     ProfScope prof("prefill_gateup", s);
-    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, a, -1,
+    MoeArgs as = a;
+    as.span = prof.span();
+    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, as, -1,
                        rt_gu);
   }
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
   {
     ProfScope prof("prefill_down", s);
-    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, a, -1,
+    MoeArgs as = a;
+    as.span = prof.span();
+    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, as, -1,
                        rt_d);
   }
   return launch_combine(a, s);

@@ -8,6 +8,21 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+// Launch span slots back to "not run": min start = all ones, max end = 0.
+__global__ __launch_bounds__(256) void span_fill_kernel(unsigned long long* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    p[2 * i] = ~0ull;
+    p[2 * i + 1] = 0ull;
+  }
+}
+
+hipError_t span_fill(unsigned long long* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(span_fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace exmoe
 
 using namespace exmoe;
