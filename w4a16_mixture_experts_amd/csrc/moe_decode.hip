@@ -3,28 +3,27 @@
 // Every selected expert runs (ExactMoE abstract; Fig. 1). With a handful of tokens per
 // expert the layer is bound by streaming the packed int4 weights from HBM, so the expert
 // kernels are laid out for bandwidth:
-//  * a workgroup (8 waves) owns one active expert and a slice of output rows; each wave
-//    streams whole 1 KiB tiles (one wave-wide 128-bit load each), two tiles per 128-input
-//    group, kDecRing groups ahead in registers;
-//  * the expert's tokens (up to 16 per pass) are staged once per workgroup in LDS and
-//    ride in the N dimension of v_mfma_f32_16x16x32_bf16; the activation operand comes
-//    from LDS (rows skewed by 16 bytes, so the 16 token rows hit distinct banks);
-//  * when too few workgroups would exist (batch 1-4), KS waves split the reduction
-//    dimension of each row block and add their partial sums through LDS.
+//  * a workgroup owns one active expert and a slice of output rows; each wave streams
+//    whole 1 KiB tiles (one wave-wide 128-bit load each), two tiles per 128-input group,
+//    kDecRing groups ahead in registers;
+//  * the expert's tokens (up to 16 per pass) are staged in LDS and ride in the N
+//    dimension of v_mfma_f32_16x16x32_bf16; the activation operand comes from LDS (rows
+//    skewed by 16 bytes, so the 16 token rows hit distinct banks).
 // Dequantization is exact: a packed word becomes bf16 operands 128 + u (u = q + 8) with
 // two bitwise ops per pair; each group's accumulator is seeded with -136 * (sum of that
-// group's activations of the token), computed in the workgroup from the staged rows, so
-// the chain ends at sum(x * q); the bf16 row scale is applied once per group in fp32.
+// group's activations of the token), so the chain ends at sum(x * q); the bf16 row scale
+// is applied once per group in fp32.
 //
-// Kernel 1 (gate/up): h = bf16(silu(W_gate x) * (W_up x)), rows in expert-grouped order.
-//   In the whole-layer call it groups the routed rows itself from the top-k ids (a
-//   histogram, scan and ballot over at most kDecMaxRows rows in LDS) and publishes the
-//   grouping: the first workgroup of each expert writes its segment of the permutation,
-//   workgroup 0 the offsets.
-// Kernel 2 (down): o = W_down h, times the routing weight, into y_perm (flat order, fp32).
-// Kernel 3 (combine): y[t] = bf16(sum over slots j in order of y_perm[t k + j]).
-// Workgroups never wait on each other: a device-scope release costs a serialized L2
-// write-back on this chip, more than a kernel boundary inside a graph.
+// decode_fused_kernel (most batches): gate/up, SiLU * up and down in one kernel; the
+//   workgroup keeps h of its slice of I in LDS and writes fp32 down outputs per slice,
+//   which combine_parts_kernel adds in a fixed order with the routing weights.
+// decode_expert_kernel (one token, too few workgroups to fuse): gate/up into h, then
+//   down into y_perm (already weighted), then combine_kernel.
+// Routing sources: the caller's grouping, the top-k ids (grouped here: histogram, scan
+// and ballot over at most kDecMaxRows rows in LDS, and published by the first workgroup
+// of each expert), or the routing kernel's per-expert token table (no grouping here; a
+// publisher workgroup writes the caller's grouping outputs).
+// Workgroups of these kernels never wait on each other.
 #include "common.h"
 #include "device.h"
 #include "group_block.h"
