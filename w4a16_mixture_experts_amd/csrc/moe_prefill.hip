@@ -25,7 +25,7 @@ namespace exmoe {
 constexpr int kPfBN = 128;                 // tokens per workgroup tile
 constexpr int kPfWaves = 8;                // waves per workgroup (2 row subtiles each)
 constexpr int kPfRows = 256;               // output rows per workgroup tile
-constexpr int kLdsStride = kGroup + 8;     // bf16 elements per LDS row (272 B)
+constexpr int kLdsStride = kGroup;         // bf16 elements per LDS row (256 B; 16-byte chunks swizzled)
 
 // All-zero row read for rows past a segment's end (device globals start zeroed; never
 // written).
@@ -87,6 +87,15 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
   return t.tok0 < t.cnt;
 }
 
+// One wave-wide global -> LDS copy (global_load_lds): lane l reads 16 (or 4) bytes at its
+// own address; they land at dst + 16 l (or 4 l). Completion is counted like a load.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
 // NW waves per workgroup; each wave owns NA = 16 / NW row subtiles (of 16 rows) and all
 // 8 token subtiles of the 256 x 128 tile. Tokens are the M operand of the MFMA and weight
 // rows the N operand, so a lane's 4 accumulator values belong to one weight row (one
@@ -96,9 +105,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
                                                            int n_row_tiles) {
   constexpr int NT = NW * 64;            // threads
   constexpr int NA = 16 / NW;            // row subtiles per wave
-  constexpr int NST = kPfBN * 16 / NT;   // 16-byte staging chunks per thread and group
-  __shared__ __attribute__((aligned(16))) uint16_t s_act[2][kPfBN * kLdsStride];
-  __shared__ __attribute__((aligned(16))) float s_seed[2][kPfBN];
+  // two buffers as separate arrays: the compiler then sees that reading one does not wait
+  // for the copies into the other
+  __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) float s_seed0[kPfBN], s_seed1[kPfBN];
   __shared__ int s_scan[kMaxExperts + 1];
   __shared__ float s_gsum[NW][kPfBN];
 
@@ -140,30 +150,32 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     }
   }
 
-  // ---- staging of the activation tile (and the group's correction seeds)
-  constexpr int TPR = NT / kPfBN;        // threads per row
-  const int st_row = tid / TPR, st_c = tid % TPR;
-  const bool st_valid = pt.tok0 + st_row < pt.cnt;
-  // Rows past the segment read the zero row: loads stay unconditional, so the compiler
-  // counts them exactly and the prefetch stays in flight.
-  const uint16_t* st_src = g_zero_row_pf;
-  if (st_valid) {
-    if (GATEUP)
-      st_src = a.x + (size_t)(a.sorted_flat[pt.seg0 + pt.tok0 + st_row] / a.k) * a.H;
-    else
-      st_src = a.h + (size_t)(pt.seg0 + pt.tok0 + st_row) * a.I;
+  // ---- staging of the activation tile (and the group's correction seeds), straight from
+  // memory into LDS (global_load_lds, 16 bytes per lane): each wave moves kDmaPerWave
+  // pieces of 4 rows x 256 bytes per group. Chunk c (16 bytes) of row r lands at position
+  // c ^ (r mod 16) of the row, so that the 16 rows of a fragment read hit distinct banks.
+  // Rows past the segment read the zero row.
+  constexpr int kDmaPerWave = kPfBN / 4 / NW;
+  const uint16_t* drow[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; i++) {
+    const int r = (wave * kDmaPerWave + i) * 4 + (lane >> 4);
+    const uint16_t* src = g_zero_row_pf;
+    if (pt.tok0 + r < pt.cnt) {
+      if (GATEUP)
+        src = a.x + (size_t)(a.sorted_flat[pt.seg0 + pt.tok0 + r] / a.k) * a.H;
+      else
+        src = a.h + (size_t)(pt.seg0 + pt.tok0 + r) * a.I;
+    }
+    drow[i] = src + (((lane & 15) ^ (r & 15)) * 8);
   }
-  const float* seed_src = seeds + pt.seg0 + pt.tok0 + st_row;   // + g * rows_pad; padded rows exist
-  uint4 st_reg[NST];
-  float st_seed;
-#define EXMOE_STAGE_LOAD(g_)                                                                     \
-  _Pragma("unroll") for (int i = 0; i < NST; i++)                                               \
-      st_reg[i] = *reinterpret_cast<const uint4*>(st_src + (g_) * kGroup + (st_c + TPR * i) * 8); \
-  st_seed = seed_src[(size_t)(g_) * rows_pad]
-#define EXMOE_STAGE_STORE(buf_)                                                                  \
-  _Pragma("unroll") for (int i = 0; i < NST; i++)                                               \
-      *reinterpret_cast<uint4*>(&s_act[(buf_)][st_row * kLdsStride + (st_c + TPR * i) * 8]) = st_reg[i]; \
-  if (st_c == 0) s_seed[(buf_)][st_row] = st_seed
+  const float* seed_src = seeds + pt.seg0 + pt.tok0 + (wave & 1) * 64 + lane;   // padded rows exist
+#define EXMOE_STAGE(g_, ACT, SEED)                                                                      \
+  do {                                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < kDmaPerWave; i++)                                             \
+        dma16(drow[i] + (g_) * kGroup, &ACT[(wave * kDmaPerWave + i) * 4 * kLdsStride]);                \
+    if (wave < 2) dma4(seed_src + (size_t)(g_) * rows_pad, &SEED[wave * 64]);                           \
+  } while (0)
 
   f32x4 acc[NA][8];
 #pragma unroll
@@ -179,20 +191,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     wcur[ai] = tiles[t * 64 + lane];
     scur[ai] = scales[t * 16 + (lane & 15)];
   }
-  EXMOE_STAGE_LOAD(0);
-  EXMOE_STAGE_STORE(0);
+  EXMOE_STAGE(0, s_act0, s_seed0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int g = 0; g < G; g++) {
-    const int buf = g & 1;
-    const int gn = g + 1 < G ? g + 1 : g;         // the last prefetch repeats a group, harmlessly
-    EXMOE_STAGE_LOAD(gn);
+  // One group: compute it from (cact, cseed) while the next one lands in (nact, nseed).
+  auto group = [&](int g_, const uint16_t* cact, const float* cseed, uint16_t* nact, float* nseed) {
+    const int gn = g_ + 1 < G ? g_ + 1 : g_;   // the last prefetch repeats a group, harmlessly
+    // the next group's activations and seeds into the other buffer, its weights into
+    // registers; everything is waited for once, at the end of this group
+    EXMOE_STAGE(gn, nact, nseed);
 #pragma unroll
     for (int ai = 0; ai < NA; ai++) {
       const size_t t = tbase[ai] + gn;
       wnext[ai] = tiles[t * 64 + lane];
       snext[ai] = scales[t * 16 + (lane & 15)];
     }
+    __builtin_amdgcn_sched_barrier(0);
     // weight fragments of the group, dequantized once: [row subtile][K step]
     bf16x8 wfr[NA][4];
 #pragma unroll
@@ -215,12 +230,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         const int row = (2 * p + j) * 16 + (lane & 15);
 #pragma unroll
         for (int s4 = 0; s4 < 4; s4++) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&s_act[buf][row * kLdsStride + 32 * s4 + 8 * (lane >> 4)]);
+          const uint4 v = *reinterpret_cast<const uint4*>(
+              &cact[row * kLdsStride + (((4 * s4 + (lane >> 4)) ^ (row & 15)) * 8)]);
           i32x4 iv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
           xfr[j][s4] = __builtin_bit_cast(bf16x8, iv);
         }
         // seeds of tokens 4(l/16)+0..3 of the subtile: -136 * group sum of their activations
-        seed[j] = *reinterpret_cast<const f32x4*>(&s_seed[buf][(2 * p + j) * 16 + 4 * (lane >> 4)]);
+        seed[j] = *reinterpret_cast<const f32x4*>(&cseed[(2 * p + j) * 16 + 4 * (lane >> 4)]);
       }
 #pragma unroll
       for (int j = 0; j < 2; j++) {
@@ -236,16 +252,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         }
       }
     }
-    EXMOE_STAGE_STORE(buf ^ 1);
+    // the next group has landed (LDS and registers) and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int ai = 0; ai < NA; ai++) {
       wcur[ai] = wnext[ai];
       scur[ai] = snext[ai];
     }
-    __syncthreads();
+  };
+  for (int g = 0; g < G; g += 2) {
+    group(g, s_act0, s_seed0, s_act1, s_seed1);
+    if (g + 1 < G) group(g + 1, s_act1, s_seed1, s_act0, s_seed0);
   }
-#undef EXMOE_STAGE_LOAD
-#undef EXMOE_STAGE_STORE
+#undef EXMOE_STAGE
 
   // ---- epilogue: lane l holds weight row (l % 16) of each row subtile and tokens
   // bj*16 + 4(l/16) + i of each token subtile
