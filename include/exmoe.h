@@ -235,6 +235,25 @@ int exmoe_slot_cache_reset_stats(exmoe_slot_cache* cache);
 /* Waits for outstanding copies, frees everything. NULL is a no-op. */
 int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 
+/* Expert layer through the slot cache in cache-sized waves (Fig. 1: waves of experts that
+ * fit the cache). The distinct active experts (host list, every routed expert of the call,
+ * e.g. from exmoe_active_experts) are taken in ascending id, in waves of at most
+ * slots_per_layer; each wave is acquired (exmoe_slot_cache_acquire: misses copied, the
+ * compute stream waits for them), then the expert kernels run for that wave's experts
+ * only. The combine runs once after the last wave, so y equals exmoe_moe_forward's on a
+ * resident bank bit for bit. Each wave's acquire is a layer-step of the cache's policy
+ * and counters. Arguments as exmoe_moe_forward, with the bank replaced by (cache, layer);
+ * the cache must hold E experts per layer and not be a dry-run cache;
+ * EXMOE_PATH_SEQUENTIAL -> EXMOE_ERR_UNSUPPORTED. The workspace size is
+ * exmoe_moe_workspace_bytes. Host-synchronous only where the cache copies from pageable
+ * memory (the per-wave table upload). */
+int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
+                             const int32_t* expert_offsets, const int32_t* sorted_flat,
+                             const int32_t* flat_to_sorted, exmoe_slot_cache* cache, int layer,
+                             const int32_t* active_ids_host, int n_active, int T, int H, int I, int E,
+                             int k, int flags, exmoe_bf16* y, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Per-kernel timing for benchmarks (not part of the layer's semantics). While enabled,
  * each kernel of the library is launched with a hipEvent pair that stamps that kernel's

@@ -9,7 +9,10 @@ state the eviction policy. Reading (least-recently-used, per layer):
   * a miss copies one packed expert (bytes += expert_bytes) into the lowest free slot,
     else evicts the resident expert with the smallest stamp that is not in the current
     active set;
-  * more active experts than slots is an error (the caller must split into waves);
+  * more active experts than slots is an error for one lookup; a forward splits them into
+    cache-sized waves (Fig. 1 caption: active experts run in waves that fit the cache).
+    Reading: the distinct active experts in ascending id, cut into consecutive waves of at
+    most `slots`; each wave is one layer-step of the policy above (acquire_waves);
   * slots == experts is full residency: everything is preloaded, lookups are bypassed and
     the counters stay at zero (Fig. 2 caption: accounting bypassed when resident).
 """
@@ -69,3 +72,13 @@ class LRUSlotCacheSim:
         for e, s in self.slot_of[layer].items():
             table[e] = s
         return table
+
+    def acquire_waves(self, layer: int, active):
+        """The waves of one cached forward: [(wave expert ids, table after its acquire)]."""
+        A = sorted(set(int(e) for e in active))
+        out = []
+        for w0 in range(0, len(A), self.S):
+            wave = A[w0:w0 + self.S]
+            out.append((wave, self.acquire(layer, wave)))
+        return out
+

@@ -251,3 +251,66 @@ def test_slot_cache_outputs_equal_resident(exm):
     assert (st["lookups"], st["hits"], st["misses"], st["evictions"], st["h2d_bytes"]) == \
         (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes)
     cache.close()
+
+
+# ------------------------------------------------------------------ cache-sized waves
+def _cached_vs_resident(exm, lay, cache, sim, x, path, bias=None):
+    import torch
+    shape = lay.shape
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
+    logits, ids, w = exm.route_topk(x, lay.wr, shape.k, bias=b)
+    off, sf, fs = exm.group_tokens(ids, shape.E)
+    active = exm.active_experts(off)
+    y_c = exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, 0, active, shape.I, flags=path)
+    waves = sim.acquire_waves(0, active)
+    y_r = exm.moe_forward(x, ids, w, off, sf, fs, lay.bank, shape.I, flags=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y_c.view(torch.int16), y_r.view(torch.int16)), f"cached output differs (path {path})"
+    return len(active), len(waves)
+
+
+def _same_counters(cache, sim):
+    st = cache.stats()
+    assert (st["lookups"], st["hits"], st["misses"], st["evictions"], st["h2d_bytes"]) == \
+        (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_forward_cached_waves_equal_resident(exm, path):
+    """Calls routed to more experts than a 5-slot cache holds run in waves; the output is
+    bitwise the resident bank's on the same path and the counters are the oracle's wave
+    simulation (ragged T included)."""
+    log(f"cached waves, 16 experts, 5 slots, path {path}")
+    shape = LayerShape(H=256, I=256, E=16, k=4)
+    lay = Layer(shape, seed=21, oracle_experts=False)
+    nb = exm.packed_expert_bytes(shape.H, shape.I)
+    S = 5
+    cache = exm.SlotCache(1, shape.E, S, nb)
+    for e in range(shape.E):
+        cache.fill(0, e, lay.blobs[e])
+    sim = oracle.LRUSlotCacheSim(1, shape.E, S, nb)
+    for T, stream in ((16, 1), (37, 2), (5, 3), (16, 1)):
+        n_act, n_waves = _cached_vs_resident(exm, lay, cache, sim, to_dev_bf16(lay.syn.x(T, stream=stream)), path)
+        assert n_waves == -(-n_act // S)
+    _same_counters(cache, sim)
+    cache.close()
+
+
+def test_olmoe_cached_waves(exm, olmoe):
+    """OLMoE-shaped decode (16 tokens, fused expert kernel) and Zipf-biased prefill (128
+    tokens) through a 16-slot cache: bitwise equal to the resident bank."""
+    log("olmoe through a 16-slot cache in waves")
+    nb = exm.packed_expert_bytes(OLMOE.H, OLMOE.I)
+    cache = exm.SlotCache(1, OLMOE.E, 16, nb)
+    for e in range(OLMOE.E):
+        cache.fill(0, e, olmoe.blobs[e])
+    sim = oracle.LRUSlotCacheSim(1, OLMOE.E, 16, nb)
+    n_act, n_waves = _cached_vs_resident(exm, olmoe, cache, sim, to_dev_bf16(olmoe.syn.x(16, stream=5)), 0)
+    log(f"  decode: {n_act} active experts in {n_waves} waves")
+    assert n_waves > 1
+    n_act, n_waves = _cached_vs_resident(exm, olmoe, cache, sim, to_dev_bf16(olmoe.syn.x(128, stream=6)), 0,
+                                         bias=olmoe.syn.zipf_bias())
+    log(f"  prefill: {n_act} active experts in {n_waves} waves")
+    assert n_waves > 1
+    _same_counters(cache, sim)
+    cache.close()

@@ -405,3 +405,39 @@ def test_lru_closed_forms():
     assert list(sim.acquire(0, [2, 0])) == [0, 1, 2] and sim.lookups == 0
     with pytest.raises(ValueError):
         oracle.LRUSlotCacheSim(layers=1, E=4, slots=2, expert_bytes=1).acquire(0, [0, 1, 2])
+
+
+def test_lru_waves_closed_forms_and_reference():
+    """Cache-sized waves (Fig. 1 caption): distinct active experts in ascending id, cut into
+    waves of at most S, each one layer-step of the policy."""
+    S, n = 4, 6
+    r = n - S
+    sim = oracle.LRUSlotCacheSim(layers=1, E=12, slots=S, expert_bytes=3)
+    waves = sim.acquire_waves(0, [5, 3, 1, 0, 2, 4, 3])         # duplicates and order ignored
+    assert [w for w, _ in waves] == [[0, 1, 2, 3], [4, 5]]
+    assert (sim.misses, sim.hits, sim.evictions, sim.h2d_bytes) == (n, 0, r, 3 * n)
+    # every expert of a wave is resident right after its acquire
+    for w, table in waves:
+        assert all(table[e] >= 0 for e in w)
+    # the same forward again: the r oldest of wave 1 were evicted by wave 2, and wave 1
+    # evicts wave 2 in turn -> 2r misses, S - r hits
+    sim.reset_stats()
+    sim.acquire_waves(0, range(n))
+    assert (sim.misses, sim.hits) == (2 * r, S - r)
+    # the waves as layer-steps of the independent reference
+    trace = []
+    for active in ([3, 9, 1, 7, 11, 0], [2, 3, 4], list(range(12)), [11, 10]):
+        A = sorted(set(active))
+        trace += [A[i:i + S] for i in range(0, len(A), S)]
+    sim = oracle.LRUSlotCacheSim(layers=1, E=12, slots=S, expert_bytes=5)
+    for active in ([3, 9, 1, 7, 11, 0], [2, 3, 4], list(range(12)), [11, 10]):
+        sim.acquire_waves(0, active)
+    width = max(len(w) for w in trace)
+    arr = np.full((len(trace), 1, width), -1, dtype=np.int64)
+    for i, w in enumerate(trace):
+        arr[i, 0, :len(w)] = w
+        arr[i, 0, len(w):] = w[0]                                # padding repeats an id (deduplicated)
+    ref, slots = _lru_reference(arr, 12, S, 5)
+    assert (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes) == \
+        (ref["lookups"], ref["hits"], ref["misses"], ref["evictions"], ref["bytes"])
+    assert sim.slot_of[0] == slots[0]

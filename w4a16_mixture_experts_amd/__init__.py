@@ -72,6 +72,8 @@ _SIGS = {
     "exmoe_moe_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "exmoe_moe_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _sz, _vp]),
+    "exmoe_moe_forward_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                      _vp, _vp, _sz, _vp]),
     "exmoe_moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "exmoe_moe_layer": (_i, [_vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i, _i,
                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -304,6 +306,24 @@ def moe_layer(x, w_router, bank: ExpertBank, I: int, k: int, bias=None, renormal
 
 
 # ----------------------------------------------------------------------------- slot cache
+def moe_forward_cached(x, ids, weights, offsets, sorted_flat, flat_to_sorted, cache: "SlotCache", layer: int,
+                       active, I: int, flags: int = PATH_AUTO, y=None, workspace=None):
+    """Expert layer through a slot cache in cache-sized waves (active: every routed expert id)."""
+    torch = _torch()
+    T, H = x.shape
+    k = ids.shape[1]
+    E = offsets.numel() - 1
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if y is None else y
+    need = moe_workspace_bytes(T, H, I, E, k, flags)
+    workspace = alloc_workspace(need, x.device) if workspace is None else workspace
+    arr = (ctypes.c_int32 * max(len(active), 1))(*[int(e) for e in active])
+    _check(_lib.exmoe_moe_forward_cached(_ptr(x), _ptr(ids), _ptr(weights), _ptr(offsets), _ptr(sorted_flat),
+                                         _ptr(flat_to_sorted), cache._h, layer, ctypes.cast(arr, _vp), len(active),
+                                         T, H, I, E, k, flags, _ptr(y), _ptr(workspace), workspace.numel(),
+                                         _stream()))
+    return y
+
+
 class SlotCache:
     """GPU slot cache over a pinned host pool (policy in C++, copies on a side stream)."""
 

@@ -367,9 +367,11 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   const int nparts = fused_waves ? I / (kTileRows * fused_waves) : 0;
   const size_t o_pt = take((size_t)nparts * rows * H * 4);
   const size_t o_sel = take((size_t)E * 16);
+  const size_t o_wt = take((size_t)E * 4);
   if (a && ws) {
     uint8_t* b = static_cast<uint8_t*>(ws);
     a->sel = b + o_sel;
+    a->wave_table = reinterpret_cast<int32_t*>(b + o_wt);
     a->h = reinterpret_cast<uint16_t*>(b + o_h);
     a->y_perm = reinterpret_cast<float*>(b + o_yp);
     a->gsum = reinterpret_cast<float*>(b + o_gs);
@@ -455,6 +457,72 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
                           k, flags, y, workspace, ws_bytes, stream);
+}
+
+int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
+                             const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
+                             exmoe_slot_cache* cache, int layer, const int32_t* active_ids_host, int n_active, int T,
+                             int H, int I, int E, int k, int flags, exmoe_bf16* y, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  int st = check_shape(T, H, I, E, k);
+  if (st) return st;
+  const int pflag = flags & EXMOE_PATH_MASK;
+  if (pflag > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", pflag);
+  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if (!cache) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache must not be NULL");
+  int cE = 0, cS = 0, dry = 0;
+  slot_cache_shape(cache, &cE, &cS, &dry);
+  if (dry) return set_error(EXMOE_ERR_CACHE, "a dry-run cache holds no weights");
+  if (cE != E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache has %d experts per layer, the layer %d", cE, E);
+  if (n_active < 0 || (n_active > 0 && !active_ids_host))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bad active list");
+  std::vector<int32_t> A(active_ids_host, active_ids_host + n_active);
+  for (int e : A)
+    if (e < 0 || e >= E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
+  std::sort(A.begin(), A.end());
+  A.erase(std::unique(A.begin(), A.end()), A.end());
+  const int path = choose_path(T, E, k, flags);
+  if (path == EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_UNSUPPORTED, "the sequential path does not run in waves");
+  if (T == 0) return EXMOE_OK;
+  CHECK_PTR(x);
+  CHECK_PTR(y);
+  CHECK_PTR4(topk_ids);
+  CHECK_PTR4(topk_weights);
+  CHECK_PTR4(expert_offsets);
+  CHECK_PTR4(sorted_flat);
+  CHECK_PTR4(flat_to_sorted);
+  const size_t need = moe_workspace_layout(T, H, I, E, k, path, nullptr, nullptr);
+  if (!workspace || ws_bytes < need)
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  MoeArgs a{};
+  a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
+  a.flat_to_sorted = flat_to_sorted; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
+  moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
+  if (path == EXMOE_PATH_PREFILL) EXMOE_HIP(launch_moe_prefill_xsum(a, stream));
+  // Waves of at most S experts in ascending id: acquire (misses copied), then the expert
+  // kernels with a table that maps only this wave's experts; the rows of the other
+  // experts are left alone (skipped silently) and written by their own wave.
+  std::vector<int32_t> tbl(E), wave_tbl(E);
+  for (size_t w0 = 0; w0 < A.size(); w0 += (size_t)cS) {
+    const int n = (int)std::min(A.size() - w0, (size_t)cS);
+    exmoe_expert_bank bank{};
+    if ((st = exmoe_slot_cache_acquire(cache, layer, A.data() + w0, n, stream, &bank))) return st;
+    if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
+    std::fill(wave_tbl.begin(), wave_tbl.end(), -1);
+    for (int i = 0; i < n; i++) wave_tbl[A[w0 + i]] = tbl[A[w0 + i]];
+    // pageable source: the runtime stages it before returning, so wave_tbl can be reused;
+    // the upload is ordered after the previous wave's kernels on the same stream
+    EXMOE_HIP(hipMemcpyAsync(a.wave_table, wave_tbl.data(), sizeof(int32_t) * E, hipMemcpyHostToDevice, stream));
+    a.base = static_cast<const uint8_t*>(bank.base);
+    a.stride = bank.stride;
+    a.e2s = a.wave_table;
+    a.skip_absent = 1;
+    if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_moe_decode_experts(a, stream));
+    else EXMOE_HIP(launch_moe_prefill_experts(a, stream));
+  }
+  EXMOE_HIP(launch_combine(a, stream));
+  return EXMOE_OK;
 }
 
 size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags) {

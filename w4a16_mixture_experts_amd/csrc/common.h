@@ -108,6 +108,8 @@ struct MoeArgs {
   uint32_t* counters; // arrival counters of the routing kernel (zero between launches)
   uint32_t* debug;    // debug word(s)
   unsigned long long* span;   // launch span slot (benchmark timing) or null
+  int skip_absent;    // experts without a slot are skipped silently (one wave of a cached forward)
+  int32_t* wave_table;  // int32 [E] workspace: the expert->slot table of one wave
 };
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);
@@ -138,6 +140,13 @@ bool decode_table_routing_ok(int T, int H, int E, int k);
 hipError_t launch_moe_decode_routed(const MoeArgs& a, const uint8_t* sel, int32_t* offsets, int32_t* sorted_flat,
                                     int32_t* flat_to_sorted, hipStream_t s);
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
+// The same paths in parts (a forward in waves runs the expert kernels once per wave and
+// the correction sums and the combine once): decode experts; prefill sums, experts.
+hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s);
+// Experts per layer, slots per layer and dry-run flag of a slot cache.
+void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry);
+hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);
 

@@ -250,7 +250,7 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
   if (ex.cnt <= 0) return false;
   const int slot = ALL ? slot_known : a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[ex.e]) : ex.e;
   if (slot < 0) {
-    if (tid == 0) atomicOr(a.debug, 1u);   // routed expert without a slot
+    if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
     return false;
   }
   const uint8_t* blob = a.base + a.stride * (size_t)slot;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     __syncthreads();   // token list and activation rows visible
     if (ex.cnt == 0) return;
     if (slot < 0) {
-      if (tid == 0) atomicOr(a.debug, 1u);   // routed expert without a slot
+      if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
       return;
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
@@ -935,9 +935,13 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
   return hipGetLastError();
 }
 
-hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s) {
+hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
-  hipError_t e = launch_decode_experts(a, nullptr, -1, ny, s);
+  return launch_decode_experts(a, nullptr, -1, ny, s);
+}
+
+hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s) {
+  hipError_t e = launch_moe_decode_experts(a, s);
   if (e != hipSuccess) return e;
   return launch_combine(a, s);
 }

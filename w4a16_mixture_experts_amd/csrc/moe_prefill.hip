@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_scan)) return;
   const int slot = a.e2s ? a.e2s[pt.e] : pt.e;
   if (slot < 0) {
-    if (tid == 0) atomicOr(a.debug, 1u);
+    if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
     return;
   }
   const uint8_t* blob = a.base + a.stride * (size_t)slot;
@@ -359,16 +359,19 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
   xsum[i] = -136.0f * s;
 }
 
-hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
+hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s) {
   const int TK = a.T * a.k;
-  const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
   const int G = a.H / kGroup;
   const int rows_pad = TK + kPfBN;
-  {
-    ProfScope prof("xsum", s);
-    EXMOE_LAUNCH(prof, xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
-                       a.H, rows_pad, a.xsum);
-  }
+  ProfScope prof("xsum", s);
+  EXMOE_LAUNCH(prof, xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
+               a.H, rows_pad, a.xsum);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) {
+  const int TK = a.T * a.k;
+  const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
   const int rt_gu = a.I / 128;
   {
     ProfScope prof("prefill_gateup", s);
@@ -377,6 +380,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
     EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, as, -1,
                        rt_gu);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
   {
     ProfScope prof("prefill_down", s);
@@ -385,7 +390,14 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
     EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, as, -1,
                        rt_d);
   }
-  return launch_combine(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
+  hipError_t e = launch_moe_prefill_xsum(a, s);
+  if (e == hipSuccess) e = launch_moe_prefill_experts(a, s);
+  if (e == hipSuccess) e = launch_combine(a, s);
+  return e;
 }
 
 }  // namespace exmoe

@@ -46,6 +46,14 @@ static void cache_free(exmoe_slot_cache* c) {
   delete c;
 }
 
+namespace exmoe {
+void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry) {
+  *E = c->E;
+  *S = c->S;
+  *dry = c->dry ? 1 : 0;
+}
+}  // namespace exmoe
+
 extern "C" {
 
 int exmoe_slot_cache_create(int layers, int E, int slots_per_layer, size_t expert_bytes, int flags,

@@ -1,6 +1,6 @@
 // Top-k selection and routing weights of one token by one wave (shared by the routing
-// kernels and the decode expert kernel, which recomputes the routing of its few tokens
-// instead of waiting for another launch).
+// kernels: the prefill top-k, the per-token decode routing and the last arriver of the
+// few-token routing kernel).
 #pragma once
 
 #include "common.h"
@@ -115,30 +115,6 @@ __device__ __forceinline__ void topk_rank_token(const uint16_t* __restrict__ lro
   }
   if (lane < k) my_sel = bf16_to_f32(lrow[my_id]);
   my_w = topk_weight(my_sel, lv, 1, E, k, renormalize);
-}
-
-// The k-th largest selection key of one token (one wave; E <= 256, up to 4 per lane).
-// Keys are distinct, so the selected experts are exactly those whose key is at least
-// this one. Radix selection from the top bit: 32 ballots, no reductions.
-__device__ __forceinline__ uint32_t kth_largest_key(const uint16_t* __restrict__ lrow, int E, int k) {
-  const int lane = (int)lane_id();
-  uint32_t key[4];
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int e = lane + 64 * q;
-    key[q] = e < E ? order_key(lrow[e], e) : 0u;
-  }
-  const int nq = (E + 63) / 64;
-  uint32_t prefix = 0;
-  for (int b = 31; b >= 0; b--) {
-    const uint32_t cand = prefix | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-      if (q < nq) cnt += __popcll(__ballot(key[q] >= cand));
-    if (cnt >= k) prefix = cand;
-  }
-  return prefix;
 }
 
 }  // namespace exmoe
