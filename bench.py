@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache"], default=None,
                     help="run a single workload (for profiling)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (traffic-counter calibration)")
@@ -237,7 +237,7 @@ def main():
         log(f"calibration copy: 3 x {nb} bytes")
         del src, dst
 
-    if args.only in (None, "decode", "prefill", "cache"):
+    if args.only in (None, "decode", "prefill", "cache", "prefill_cache"):
         olmoe_syn, banks, olmoe_blobs = build_olmoe(exm, torch, args.rotate)
         wr = to_dev_bf16(olmoe_syn.router())
 
@@ -381,6 +381,84 @@ def main():
 
     if not args.no_secondary and args.only in (None, "cache"):
         secondary.update(run_slot_cache([8, 16, 32, 64]))
+
+    # ------------------------------------------------------------------ prefill through the slot cache
+    def run_prefill_cache(slots_list, T=512, layers=16, warm=2, timed=5):
+        """Time-to-first-token analogue: a T-token prompt through the expert layers of a
+        `layers`-deep OLMoE-shaped stack whose experts sit in the pinned host pool behind
+        `slots` GPU slots per layer. Each layer has its own seeded router and Zipf(1.1)
+        logit bias (so each layer routes the prompt to its own active set); the prompt's x
+        is shared by all layers; the cache is persistent-warm (the first `warm` prompts
+        are untimed). Per layer: routing, grouping, the active set read back to the host,
+        then the expert layer in cache-sized waves. Wall clock per prompt, median."""
+        per_layer = [SyntheticLayer(OLMOE, seed=0, layer=l) for l in range(layers)]
+        wrs = [to_dev_bf16(sl.router()) for sl in per_layer]
+        biases = [torch.from_numpy(sl.zipf_bias()).cuda() for sl in per_layer]
+        xs = [to_dev_bf16(olmoe_syn.x(T, stream=7000 + p)) for p in range(warm + timed)]
+        ws = exm.alloc_workspace(exm.moe_workspace_bytes(T, H, I, E, k))
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        pin = torch.empty(expert_bytes, dtype=torch.uint8).pin_memory()
+        dev = torch.empty(expert_bytes, dtype=torch.uint8, device="cuda")
+        for _ in range(4):
+            dev.copy_(pin, non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for _ in range(64):
+            dev.copy_(pin, non_blocking=True)
+        torch.cuda.synchronize()
+        h2d_gbs = 64 * expert_bytes / (time.time() - t0) / 1e9
+        del pin, dev
+        out = {}
+        for S in slots_list:
+            cache = exm.SlotCache(layers, E, S, expert_bytes)
+            for l in range(layers):
+                for e in range(E):
+                    cache.fill(l, e, olmoe_blobs[e])
+            if S == E:
+                cache.preload()
+            n_waves = 0
+            n_active = 0
+
+            def prompt(x):
+                nonlocal n_waves, n_active
+                for l in range(layers):
+                    logits, ids, w = exm.route_topk(x, wrs[l], k, bias=biases[l])
+                    off, sf, fs = exm.group_tokens(ids, E)
+                    active = exm.active_experts(off)
+                    n_active += len(active)
+                    W = S if len(active) <= S else max(S // 2, 1)   # the library's wave size
+                    n_waves += -(-len(active) // W)
+                    exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, l, active, I, y=y, workspace=ws)
+
+            for p in range(warm):
+                prompt(xs[p])
+            torch.cuda.synchronize()
+            cache.reset_stats()
+            n_waves = n_active = 0
+            times = []
+            for p in range(warm, warm + timed):
+                t0 = time.time()
+                prompt(xs[p])
+                torch.cuda.synchronize()
+                times.append(time.time() - t0)
+            st = cache.stats()
+            cache.close()
+            ms = float(np.median(times)) * 1e3
+            h2d = st["h2d_bytes"] / timed
+            rec = {"slots": S, "layers": layers, "T": T, "prompts_timed": timed, "ms_per_prompt": ms,
+                   "ms_per_prompt_min": min(times) * 1e3, "resident": bool(st["resident"]),
+                   "active_experts_per_layer": n_active / timed / layers, "waves_per_layer": n_waves / timed / layers,
+                   "hit_rate": st["hits"] / max(st["lookups"], 1), "misses_per_prompt": st["misses"] / timed,
+                   "h2d_bytes_per_prompt": h2d, "h2d_ms_at_pinned_copy_rate": h2d / (h2d_gbs * 1e9) * 1e3,
+                   "h2d_gbs_pinned_copy": h2d_gbs, "device_bytes": st["device_bytes"]}
+            log(f"prefill through the cache T={T} S={S}: {ms:.2f} ms for {layers} layers, "
+                f"{rec['waves_per_layer']:.2f} waves/layer, hit rate {rec['hit_rate'] * 100:.1f}%, "
+                f"H2D {h2d / 1e9:.2f} GB/prompt ({rec['h2d_ms_at_pinned_copy_rate']:.1f} ms at {h2d_gbs:.1f} GB/s)")
+            out[f"prefill_cache_T{T}_S{S}"] = rec
+        return out
+
+    if not args.no_secondary and args.only in (None, "prefill_cache"):
+        secondary.update(run_prefill_cache([8, 16, 32, 64]))
 
     # ------------------------------------------------------------------ prefill lines
     def run_prefill(name, shape, syn, banks_p, wr_p, T, bias, steps, warmup):

@@ -237,7 +237,8 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 
 /* Expert layer through the slot cache in cache-sized waves (Fig. 1: waves of experts that
  * fit the cache). The distinct active experts (host list, every routed expert of the call,
- * e.g. from exmoe_active_experts) are taken in ascending id, in waves of at most
+ * e.g. from exmoe_active_experts) are ordered with the ones already resident in the layer's
+ * slots first, then the others, each part in ascending id, and cut into waves of at most
  * slots_per_layer; each wave is acquired (exmoe_slot_cache_acquire: misses copied, the
  * compute stream waits for them), then the expert kernels run for that wave's experts
  * only. The combine runs once after the last wave, so y equals exmoe_moe_forward's on a

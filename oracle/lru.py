@@ -11,8 +11,15 @@ state the eviction policy. Reading (least-recently-used, per layer):
     active set;
   * more active experts than slots is an error for one lookup; a forward splits them into
     cache-sized waves (Fig. 1 caption: active experts run in waves that fit the cache).
-    Reading: the distinct active experts in ascending id, cut into consecutive waves of at
-    most `slots`; each wave is one layer-step of the policy above (acquire_waves);
+    Reading (the order of the waves is not on the pages): the distinct active experts that
+    are already resident come first, in ascending id, then the others in ascending id; an
+    active set that fits is one wave, a larger one is cut into consecutive waves of
+    slots // 2 (of 1 when slots == 1), and each wave is one layer-step of the policy above
+    (acquire_waves). Taking the resident experts first means a repeated active set larger
+    than the cache hits `slots` times instead of thrashing the LRU; half-size waves mean the
+    misses of a wave never evict an expert of the wave before it, so its copies can run
+    while that wave computes (Fig. 1: waves that fit the cache; the overlap is this
+    reading's, not the pages');
   * slots == experts is full residency: everything is preloaded, lookups are bypassed and
     the counters stay at zero (Fig. 2 caption: accounting bypassed when resident).
 """
@@ -76,9 +83,12 @@ class LRUSlotCacheSim:
     def acquire_waves(self, layer: int, active):
         """The waves of one cached forward: [(wave expert ids, table after its acquire)]."""
         A = sorted(set(int(e) for e in active))
+        resident = self.slot_of[layer]
+        A = [e for e in A if e in resident] + [e for e in A if e not in resident]
+        W = self.S // 2 if len(A) > self.S and self.S >= 2 else self.S
         out = []
-        for w0 in range(0, len(A), self.S):
-            wave = A[w0:w0 + self.S]
+        for w0 in range(0, len(A), W):
+            wave = A[w0:w0 + W]
             out.append((wave, self.acquire(layer, wave)))
         return out
 

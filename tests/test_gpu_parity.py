@@ -291,7 +291,8 @@ def test_forward_cached_waves_equal_resident(exm, path):
     sim = oracle.LRUSlotCacheSim(1, shape.E, S, nb)
     for T, stream in ((16, 1), (37, 2), (5, 3), (16, 1)):
         n_act, n_waves = _cached_vs_resident(exm, lay, cache, sim, to_dev_bf16(lay.syn.x(T, stream=stream)), path)
-        assert n_waves == -(-n_act // S)
+        W = S if n_act <= S else S // 2
+        assert n_waves == -(-n_act // W)
     _same_counters(cache, sim)
     cache.close()
 

@@ -408,36 +408,70 @@ def test_lru_closed_forms():
 
 
 def test_lru_waves_closed_forms_and_reference():
-    """Cache-sized waves (Fig. 1 caption): distinct active experts in ascending id, cut into
-    waves of at most S, each one layer-step of the policy."""
+    """Cache-sized waves (Fig. 1 caption): resident active experts first, then the others,
+    each in ascending id; one wave when the set fits, else waves of S // 2; each wave is
+    one layer-step of the policy."""
     S, n = 4, 6
-    r = n - S
     sim = oracle.LRUSlotCacheSim(layers=1, E=12, slots=S, expert_bytes=3)
     waves = sim.acquire_waves(0, [5, 3, 1, 0, 2, 4, 3])         # duplicates and order ignored
-    assert [w for w, _ in waves] == [[0, 1, 2, 3], [4, 5]]
-    assert (sim.misses, sim.hits, sim.evictions, sim.h2d_bytes) == (n, 0, r, 3 * n)
+    assert [w for w, _ in waves] == [[0, 1], [2, 3], [4, 5]]     # cold cache: plain ascending
+    assert (sim.misses, sim.hits, sim.evictions, sim.h2d_bytes) == (n, 0, n - S, 3 * n)
     # every expert of a wave is resident right after its acquire
     for w, table in waves:
         assert all(table[e] >= 0 for e in w)
-    # the same forward again: the r oldest of wave 1 were evicted by wave 2, and wave 1
-    # evicts wave 2 in turn -> 2r misses, S - r hits
+    # the last wave evicted the oldest (0, 1), so {2, 3, 4, 5} stay; the same forward again
+    # takes them first (S hits) and then misses the other n - S
     sim.reset_stats()
-    sim.acquire_waves(0, range(n))
-    assert (sim.misses, sim.hits) == (2 * r, S - r)
-    # the waves as layer-steps of the independent reference
+    waves = sim.acquire_waves(0, range(n))
+    assert [w for w, _ in waves] == [[2, 3], [4, 5], [0, 1]]
+    assert (sim.misses, sim.hits, sim.evictions) == (n - S, S, n - S)
+    # any repeated active set larger than the cache: exactly S hits per forward
+    for rep in range(3):
+        sim.reset_stats()
+        sim.acquire_waves(0, range(n))
+        assert (sim.hits, sim.misses) == (S, n - S)
+    # a set that fits is one wave; S == 1 takes waves of one
+    assert [w for w, _ in oracle.LRUSlotCacheSim(1, 12, 4, 1).acquire_waves(0, [7, 2, 9, 4])] == [[2, 4, 7, 9]]
+    assert [w for w, _ in oracle.LRUSlotCacheSim(1, 12, 1, 1).acquire_waves(0, [7, 2])] == [[2], [7]]
+    # no wave's misses evict an expert of the wave before it (its copies may overlap that
+    # wave's kernels), over random active sets, slot counts and histories
+    rng = np.random.default_rng(3)
+    for S2 in (2, 3, 4, 5, 8):
+        sim = oracle.LRUSlotCacheSim(layers=1, E=16, slots=S2, expert_bytes=1)
+        for _ in range(40):
+            A = rng.choice(16, size=int(rng.integers(1, 17)), replace=False)
+            before = None
+            waves = sim.acquire_waves(0, A)
+            for w, table in waves:
+                if before is not None and len(waves) > 1:
+                    prev_w, prev_t = before
+                    assert all(table[e] == prev_t[e] for e in prev_w), (S2, sorted(A))
+                before = (w, table)
+    # the waves as layer-steps of the independent reference, the wave split recomputed from
+    # that reference's own residency before each forward
+    forwards = ([3, 9, 1, 7, 11, 0], [2, 3, 4], list(range(12)), [11, 10], [0, 1, 2, 3, 4, 11], list(range(12)))
     trace = []
-    for active in ([3, 9, 1, 7, 11, 0], [2, 3, 4], list(range(12)), [11, 10]):
+
+    def padded(ws):
+        width = max(len(w) for w in ws)
+        arr = np.full((len(ws), 1, width), -1, dtype=np.int64)
+        for i, w in enumerate(ws):
+            arr[i, 0, :len(w)] = w
+            arr[i, 0, len(w):] = w[0]                            # padding repeats an id (deduplicated)
+        return arr
+
+    for active in forwards:
         A = sorted(set(active))
-        trace += [A[i:i + S] for i in range(0, len(A), S)]
+        res = set(_lru_reference(padded(trace), 12, S, 5)[1][0]) if trace else set()
+        order = [e for e in A if e in res] + [e for e in A if e not in res]
+        W = S if len(A) <= S else S // 2
+        trace += [order[i:i + W] for i in range(0, len(order), W)]
     sim = oracle.LRUSlotCacheSim(layers=1, E=12, slots=S, expert_bytes=5)
-    for active in ([3, 9, 1, 7, 11, 0], [2, 3, 4], list(range(12)), [11, 10]):
-        sim.acquire_waves(0, active)
-    width = max(len(w) for w in trace)
-    arr = np.full((len(trace), 1, width), -1, dtype=np.int64)
-    for i, w in enumerate(trace):
-        arr[i, 0, :len(w)] = w
-        arr[i, 0, len(w):] = w[0]                                # padding repeats an id (deduplicated)
-    ref, slots = _lru_reference(arr, 12, S, 5)
+    got = []
+    for active in forwards:
+        got += [w for w, _ in sim.acquire_waves(0, active)]
+    assert got == trace
+    ref, slots = _lru_reference(padded(trace), 12, S, 5)
     assert (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes) == \
         (ref["lookups"], ref["hits"], ref["misses"], ref["evictions"], ref["bytes"])
     assert sim.slot_of[0] == slots[0]

@@ -500,17 +500,41 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   a.flat_to_sorted = flat_to_sorted; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
   moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
   if (path == EXMOE_PATH_PREFILL) EXMOE_HIP(launch_moe_prefill_xsum(a, stream));
-  // Waves of at most S experts in ascending id: acquire (misses copied), then the expert
-  // kernels with a table that maps only this wave's experts; the rows of the other
+  // Waves: the active experts already resident first, then the others, each in ascending
+  // id (a repeated active set larger than the cache then hits S times instead of
+  // thrashing the LRU). An active set that fits is one wave; a larger one runs in waves of
+  // S/2, so the misses of wave w+1 never evict an expert of wave w (the LRU victims are the
+  // S - |wave w| - hits >= |misses| older residents) and its copies overlap wave w's
+  // kernels: they wait only for wave w-1's. Per wave: acquire (misses copied), then the
+  // expert kernels with a table that maps only this wave's experts; the rows of the other
   // experts are left alone (skipped silently) and written by their own wave.
   std::vector<int32_t> tbl(E), wave_tbl(E);
-  for (size_t w0 = 0; w0 < A.size(); w0 += (size_t)cS) {
-    const int n = (int)std::min(A.size() - w0, (size_t)cS);
+  if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
+  std::stable_partition(A.begin(), A.end(), [&](int e) { return tbl[e] >= 0; });
+  const int W = ((int)A.size() > cS && cS >= 2) ? cS / 2 : cS;
+  const int n_waves = ((int)A.size() + W - 1) / W;
+  std::vector<int32_t> prev_slots;
+  hipEvent_t mark = nullptr;
+  if (n_waves > 1) {
+    EXMOE_HIP(slot_cache_event(cache, 0, &mark));
+    EXMOE_HIP(hipEventRecord(mark, stream));   // everything before this call
+  }
+  for (int w = 0; w < n_waves; w++) {
+    const int w0 = w * W;
+    const int n = std::min((int)A.size() - w0, W);
     exmoe_expert_bank bank{};
-    if ((st = exmoe_slot_cache_acquire(cache, layer, A.data() + w0, n, stream, &bank))) return st;
+    hipEvent_t after = nullptr;   // wave 0 waits for all earlier work
+    if (w > 0) EXMOE_HIP(slot_cache_event(cache, w - 1, &after));   // done through wave w-2
+    if ((st = slot_cache_acquire_ex(cache, layer, A.data() + w0, n, stream, after, prev_slots.data(),
+                                    (int)prev_slots.size(), &bank)))
+      return st;
     if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
     std::fill(wave_tbl.begin(), wave_tbl.end(), -1);
-    for (int i = 0; i < n; i++) wave_tbl[A[w0 + i]] = tbl[A[w0 + i]];
+    prev_slots.clear();
+    for (int i = 0; i < n; i++) {
+      wave_tbl[A[w0 + i]] = tbl[A[w0 + i]];
+      prev_slots.push_back(tbl[A[w0 + i]]);
+    }
     // pageable source: the runtime stages it before returning, so wave_tbl can be reused;
     // the upload is ordered after the previous wave's kernels on the same stream
     EXMOE_HIP(hipMemcpyAsync(a.wave_table, wave_tbl.data(), sizeof(int32_t) * E, hipMemcpyHostToDevice, stream));
@@ -520,6 +544,10 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
     a.skip_absent = 1;
     if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_moe_decode_experts(a, stream));
     else EXMOE_HIP(launch_moe_prefill_experts(a, stream));
+    if (w + 2 < n_waves) {   // the mark that wave w+2's copies wait for
+      EXMOE_HIP(slot_cache_event(cache, w + 1, &mark));
+      EXMOE_HIP(hipEventRecord(mark, stream));
+    }
   }
   EXMOE_HIP(launch_combine(a, stream));
   return EXMOE_OK;

@@ -145,6 +145,14 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s);
 // Experts per layer, slots per layer and dry-run flag of a slot cache.
 void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry);
+// exmoe_slot_cache_acquire whose copies wait only for `after` (an event recorded on the
+// compute stream) unless one of them lands in a slot of protect_slots; after == NULL
+// waits for everything enqueued on the compute stream so far (the public behaviour).
+int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
+                          hipStream_t compute_stream, hipEvent_t after, const int32_t* protect_slots, int n_protect,
+                          exmoe_expert_bank* bank_out);
+// Event i of the cache's pool (created on first use, destroyed with the cache).
+hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev);
 hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path

@@ -32,6 +32,7 @@ struct exmoe_slot_cache {
   uint64_t clock = 0;
   exmoe_cache_stats st{};
   int device = 0;
+  std::vector<hipEvent_t> wave_ev;   // compute-stream marks of a forward in waves (grown on demand)
 };
 
 static void cache_free(exmoe_slot_cache* c) {
@@ -42,6 +43,7 @@ static void cache_free(exmoe_slot_cache* c) {
   if (c->d_tables) (void)hipFree(c->d_tables);
   if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  for (hipEvent_t ev : c->wave_ev) (void)hipEventDestroy(ev);
   if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
   delete c;
 }
@@ -51,6 +53,99 @@ void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry) {
   *E = c->E;
   *S = c->S;
   *dry = c->dry ? 1 : 0;
+}
+
+hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev) {
+  while ((int)c->wave_ev.size() <= i) {
+    hipEvent_t e = nullptr;
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) return r;
+    c->wave_ev.push_back(e);
+  }
+  *ev = c->wave_ev[i];
+  return hipSuccess;
+}
+
+int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
+                          hipStream_t compute_stream, hipEvent_t after, const int32_t* protect_slots, int n_protect,
+                          exmoe_expert_bank* bank_out) {
+  if (!c || !bank_out) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache and bank_out must not be NULL");
+  if (layer < 0 || layer >= c->layers) return set_error(EXMOE_ERR_CACHE, "layer %d out of range", layer);
+  if (n_active < 0 || (n_active > 0 && !active_ids_host))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bad active list");
+  std::vector<int> A(active_ids_host, active_ids_host + n_active);
+  for (int e : A)
+    if (e < 0 || e >= c->E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
+  std::sort(A.begin(), A.end());
+  A.erase(std::unique(A.begin(), A.end()), A.end());
+  if ((int)A.size() > c->S)
+    return set_error(EXMOE_ERR_CACHE, "%zu active experts exceed %d slots", A.size(), c->S);
+  int32_t* slot_of = c->slot_of.data() + (size_t)layer * c->E;
+  int32_t* owner = c->owner.data() + (size_t)layer * c->S;
+  uint64_t* stamp = c->stamp.data() + (size_t)layer * c->E;
+  std::vector<std::pair<int, int>> copies;   // (expert, slot)
+  if (!c->resident) {
+    std::vector<char> in_A(c->E, 0);
+    for (int e : A) in_A[e] = 1;
+    for (int e : A) {
+      c->st.lookups++;
+      c->clock++;
+      if (slot_of[e] >= 0) {
+        c->st.hits++;
+      } else {
+        c->st.misses++;
+        int s = -1;
+        for (int i = 0; i < c->S; i++)
+          if (owner[i] < 0) { s = i; break; }
+        if (s < 0) {
+          int victim = -1;
+          for (int x = 0; x < c->E; x++)
+            if (slot_of[x] >= 0 && !in_A[x] && (victim < 0 || stamp[x] < stamp[victim])) victim = x;
+          s = slot_of[victim];      // exists: |A| <= S and every slot is owned
+          slot_of[victim] = -1;
+          c->st.evictions++;
+        }
+        slot_of[e] = s;
+        owner[s] = e;
+        copies.emplace_back(e, s);
+        c->st.h2d_bytes += c->expert_bytes;
+        c->st.h2d_copies++;
+      }
+      stamp[e] = c->clock;
+    }
+  }
+  if (c->dry) {
+    memset(bank_out, 0, sizeof(*bank_out));
+    return EXMOE_OK;
+  }
+  uint8_t* layer_dev = c->dev + (size_t)layer * c->S * c->stride;
+  if (!copies.empty()) {
+    // The copy stream must not overwrite a slot that earlier work on the compute stream
+    // may still read: it waits for `after` when no copy lands in a protected slot, else
+    // for everything enqueued on the compute stream so far.
+    bool early = after != nullptr;
+    for (auto& es : copies)
+      for (int i = 0; i < n_protect; i++) early = early && es.second != protect_slots[i];
+    if (early) {
+      EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, after, 0));
+    } else {
+      EXMOE_HIP(hipEventRecord(c->ev_compute, compute_stream));
+      EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, c->ev_compute, 0));
+    }
+    for (auto& es : copies)
+      EXMOE_HIP(hipMemcpyAsync(layer_dev + (size_t)es.second * c->stride,
+                               c->pinned + ((size_t)layer * c->E + es.first) * c->stride, c->expert_bytes,
+                               hipMemcpyHostToDevice, c->copy_stream));
+    // Table from pageable memory: the runtime stages it before returning.
+    EXMOE_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * c->E, slot_of, sizeof(int32_t) * c->E,
+                             hipMemcpyHostToDevice, c->copy_stream));
+    EXMOE_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
+    EXMOE_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
+  }
+  bank_out->base = layer_dev;
+  bank_out->stride = c->stride;
+  bank_out->expert_to_slot = c->d_tables + (size_t)layer * c->E;
+  return EXMOE_OK;
 }
 }  // namespace exmoe
 
@@ -138,75 +233,8 @@ int exmoe_slot_cache_preload(exmoe_slot_cache* c, hipStream_t stream) {
 
 int exmoe_slot_cache_acquire(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
                              hipStream_t compute_stream, exmoe_expert_bank* bank_out) {
-  if (!c || !bank_out) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache and bank_out must not be NULL");
-  if (layer < 0 || layer >= c->layers) return set_error(EXMOE_ERR_CACHE, "layer %d out of range", layer);
-  if (n_active < 0 || (n_active > 0 && !active_ids_host))
-    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bad active list");
-  std::vector<int> A(active_ids_host, active_ids_host + n_active);
-  for (int e : A)
-    if (e < 0 || e >= c->E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
-  std::sort(A.begin(), A.end());
-  A.erase(std::unique(A.begin(), A.end()), A.end());
-  if ((int)A.size() > c->S)
-    return set_error(EXMOE_ERR_CACHE, "%zu active experts exceed %d slots", A.size(), c->S);
-  int32_t* slot_of = c->slot_of.data() + (size_t)layer * c->E;
-  int32_t* owner = c->owner.data() + (size_t)layer * c->S;
-  uint64_t* stamp = c->stamp.data() + (size_t)layer * c->E;
-  std::vector<std::pair<int, int>> copies;   // (expert, slot)
-  if (!c->resident) {
-    std::vector<char> in_A(c->E, 0);
-    for (int e : A) in_A[e] = 1;
-    for (int e : A) {
-      c->st.lookups++;
-      c->clock++;
-      if (slot_of[e] >= 0) {
-        c->st.hits++;
-      } else {
-        c->st.misses++;
-        int s = -1;
-        for (int i = 0; i < c->S; i++)
-          if (owner[i] < 0) { s = i; break; }
-        if (s < 0) {
-          int victim = -1;
-          for (int x = 0; x < c->E; x++)
-            if (slot_of[x] >= 0 && !in_A[x] && (victim < 0 || stamp[x] < stamp[victim])) victim = x;
-          s = slot_of[victim];      // exists: |A| <= S and every slot is owned
-          slot_of[victim] = -1;
-          c->st.evictions++;
-        }
-        slot_of[e] = s;
-        owner[s] = e;
-        copies.emplace_back(e, s);
-        c->st.h2d_bytes += c->expert_bytes;
-        c->st.h2d_copies++;
-      }
-      stamp[e] = c->clock;
-    }
-  }
-  if (c->dry) {
-    memset(bank_out, 0, sizeof(*bank_out));
-    return EXMOE_OK;
-  }
-  uint8_t* layer_dev = c->dev + (size_t)layer * c->S * c->stride;
-  if (!copies.empty()) {
-    // The copy stream must not overwrite a slot that earlier work on the compute stream
-    // may still read.
-    EXMOE_HIP(hipEventRecord(c->ev_compute, compute_stream));
-    EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, c->ev_compute, 0));
-    for (auto& es : copies)
-      EXMOE_HIP(hipMemcpyAsync(layer_dev + (size_t)es.second * c->stride,
-                               c->pinned + ((size_t)layer * c->E + es.first) * c->stride, c->expert_bytes,
-                               hipMemcpyHostToDevice, c->copy_stream));
-    // Table from pageable memory: the runtime stages it before returning.
-    EXMOE_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * c->E, slot_of, sizeof(int32_t) * c->E,
-                             hipMemcpyHostToDevice, c->copy_stream));
-    EXMOE_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
-    EXMOE_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
-  }
-  bank_out->base = layer_dev;
-  bank_out->stride = c->stride;
-  bank_out->expert_to_slot = c->d_tables + (size_t)layer * c->E;
-  return EXMOE_OK;
+  return exmoe::slot_cache_acquire_ex(c, layer, active_ids_host, n_active, compute_stream, nullptr, nullptr, 0,
+                                      bank_out);
 }
 
 int exmoe_slot_cache_table(const exmoe_slot_cache* c, int layer, int32_t* table_host) {
