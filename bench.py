@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16"], default=None,
                     help="run a single workload (for profiling)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (traffic-counter calibration)")
@@ -93,7 +93,8 @@ def bytes_per_call(exm, torch, lay_syn, shape, wr, xs_dev, T, bias=None):
     return np.array(D)
 
 
-SPAN_KERNELS = ("decode_gateup", "decode_down", "decode_fused", "combine", "prefill_gateup", "prefill_down")
+SPAN_KERNELS = ("decode_gateup", "decode_down", "decode_fused", "combine", "prefill_gateup", "prefill_down",
+                "bf16_decode_gateup", "bf16_decode_down", "bf16_prefill_gateup", "bf16_prefill_down")
 
 
 def time_layer(exm, torch, wl, steps, warmup, use_graph, flags=0, spans=None):
@@ -237,7 +238,7 @@ def main():
         log(f"calibration copy: 3 x {nb} bytes")
         del src, dst
 
-    if args.only in (None, "decode", "prefill", "cache", "prefill_cache"):
+    if args.only in (None, "decode", "prefill", "cache", "prefill_cache", "bf16"):
         olmoe_syn, banks, olmoe_blobs = build_olmoe(exm, torch, args.rotate)
         wr = to_dev_bf16(olmoe_syn.router())
 
@@ -382,6 +383,76 @@ def main():
     if not args.no_secondary and args.only in (None, "cache"):
         secondary.update(run_slot_cache([8, 16, 32, 64]))
 
+    # ------------------------------------------------------------------ bf16 comparator
+    bf16_banks = []
+
+    def build_bf16_banks(copies=2):
+        """The same 64 experts with bf16 weights (the comparator), 805 MB per copy."""
+        if bf16_banks:
+            return bf16_banks
+        from synthetic import f32_to_bf16_bits
+        from concurrent.futures import ThreadPoolExecutor
+        t0 = time.time()
+
+        def one(e):
+            return exm.bf16_pack(*[f32_to_bf16_bits(w) for w in olmoe_syn.expert(e)])
+
+        with ThreadPoolExecutor(8) as ex:
+            blobs = list(ex.map(one, range(E)))
+        b0 = exm.bank_from_blobs(blobs)
+        del blobs
+        bf16_banks.append(b0)
+        for _ in range(copies - 1):
+            bf16_banks.append(exm.ExpertBank(base=b0.base.clone(), stride=b0.stride))
+        torch.cuda.synchronize()
+        log(f"built the bf16 comparator bank: {copies} copies of {b0.base.numel() / 1e6:.1f} MB in {time.time() - t0:.1f}s")
+        return bf16_banks
+
+    def run_bf16_comparator(decode_T=(1, 4, 16), prefill_T=(512, 2048), steps=200, warmup=20):
+        """The layer with dense bf16 experts (same routing, grouping and combine) against the
+        int4 layer, timed the same way, back to back: the layer-level W4A16 / BF16 ratio."""
+        bb = build_bf16_banks()
+        bf16_bytes = exm.bf16_expert_bytes(H, I)
+        out = {}
+        for T in decode_T:
+            xs = [to_dev_bf16(olmoe_syn.x(T, stream=s)) for s in range(64)]
+            D = bytes_per_call(exm, torch, olmoe_syn, OLMOE, wr, xs, T).mean()
+            w4 = time_layer(exm, torch, Workload(f"olmoe_decode_T{T}", OLMOE, T, {"wr": wr}, banks, xs), steps, warmup,
+                            use_graph)
+            spans = {}
+            bf = time_layer(exm, torch, Workload(f"olmoe_decode_T{T}_bf16", OLMOE, T, {"wr": wr}, bb, xs), steps,
+                            warmup, use_graph, flags=exm.WEIGHTS_BF16, spans=spans)
+            rec = {"T": T, "w4a16_us_per_layer": w4 * 1e3, "bf16_us_per_layer": bf * 1e3,
+                   "w4a16_over_bf16_speedup": bf / w4, "distinct_experts_mean": float(D),
+                   "bf16_kernel_span_us": {n: v[0] for n, v in spans.items()}}
+            if "bf16_decode_gateup" in spans and "bf16_decode_down" in spans:
+                us = spans["bf16_decode_gateup"][0] + spans["bf16_decode_down"][0]
+                alg = D * bf16_bytes + T * H * 2 + T * k * H * 4
+                rec["bf16_expert_kernels_gbs"] = alg / (us * 1e-6) / 1e9
+                rec["bf16_expert_kernels_hbm_frac"] = rec["bf16_expert_kernels_gbs"] / HBM_PEAK_GBS
+            log(f"bf16 comparator decode T={T}: bf16 {bf * 1e3:.1f} us vs w4a16 {w4 * 1e3:.1f} us per layer "
+                f"({bf / w4:.2f}x)" + (f", bf16 expert kernels {rec['bf16_expert_kernels_gbs']:.0f} GB/s"
+                                        if "bf16_expert_kernels_gbs" in rec else ""))
+            out[f"bf16_vs_w4a16_decode_T{T}"] = rec
+        bias = torch.from_numpy(olmoe_syn.zipf_bias()).cuda()
+        for T in prefill_T:
+            xs = [to_dev_bf16(olmoe_syn.x(T, stream=s)) for s in range(4)]
+            w4 = time_layer(exm, torch, Workload(f"olmoe_prefill_T{T}", OLMOE, T, {"wr": wr}, banks[:2], xs, bias),
+                            20, 3, use_graph)
+            spans = {}
+            bf = time_layer(exm, torch, Workload(f"olmoe_prefill_T{T}_bf16", OLMOE, T, {"wr": wr}, bb, xs, bias),
+                            20, 3, use_graph, flags=exm.WEIGHTS_BF16, spans=spans)
+            flops = 6.0 * T * k * H * I
+            rec = {"T": T, "w4a16_ms_per_layer": w4, "bf16_ms_per_layer": bf, "w4a16_over_bf16_speedup": bf / w4,
+                   "bf16_layer_tflops": flops / (bf * 1e-3) / 1e12,
+                   "bf16_kernel_span_us": {n: v[0] for n, v in spans.items()}}
+            log(f"bf16 comparator prefill T={T}: bf16 {bf:.3f} ms vs w4a16 {w4:.3f} ms per layer ({bf / w4:.2f}x)")
+            out[f"bf16_vs_w4a16_prefill_zipf_T{T}"] = rec
+        return out
+
+    if not args.no_secondary and args.only in (None, "bf16"):
+        secondary.update(run_bf16_comparator())
+
     # ------------------------------------------------------------------ prefill through the slot cache
     def run_prefill_cache(slots_list, T=512, layers=16, warm=2, timed=5):
         """Time-to-first-token analogue: a T-token prompt through the expert layers of a
@@ -410,6 +481,36 @@ def main():
         del pin, dev
         out = {}
         for S in slots_list:
+            if S == "bf16":
+                # the comparator: every layer's experts resident in bf16 (one shared bank)
+                bank_bf = build_bf16_banks()[0]
+                n_waves = n_active = 0
+
+                def prompt(x):
+                    nonlocal n_active
+                    for l in range(layers):
+                        logits, ids, w = exm.route_topk(x, wrs[l], k, bias=biases[l])
+                        off, sf, fs = exm.group_tokens(ids, E)
+                        n_active += len(exm.active_experts(off))   # the same host read as the cached runs
+                        exm.moe_forward(x, ids, w, off, sf, fs, bank_bf, I, flags=exm.WEIGHTS_BF16, y=y,
+                                        workspace=ws)
+
+                for p in range(warm):
+                    prompt(xs[p])
+                torch.cuda.synchronize()
+                n_active = 0
+                times = []
+                for p in range(warm, warm + timed):
+                    t0 = time.time()
+                    prompt(xs[p])
+                    torch.cuda.synchronize()
+                    times.append(time.time() - t0)
+                ms = float(np.median(times)) * 1e3
+                log(f"prefill of the bf16 comparator T={T}: {ms:.2f} ms for {layers} layers (resident)")
+                out[f"prefill_bf16_resident_T{T}"] = {"layers": layers, "T": T, "prompts_timed": timed,
+                                                      "ms_per_prompt": ms, "ms_per_prompt_min": min(times) * 1e3,
+                                                      "active_experts_per_layer": n_active / timed / layers}
+                continue
             cache = exm.SlotCache(layers, E, S, expert_bytes)
             for l in range(layers):
                 for e in range(E):
@@ -458,7 +559,7 @@ def main():
         return out
 
     if not args.no_secondary and args.only in (None, "prefill_cache"):
-        secondary.update(run_prefill_cache([8, 16, 32, 64]))
+        secondary.update(run_prefill_cache([8, 16, 32, 64, "bf16"]))
 
     # ------------------------------------------------------------------ prefill lines
     def run_prefill(name, shape, syn, banks_p, wr_p, T, bias, steps, warmup):

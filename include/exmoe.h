@@ -89,6 +89,20 @@ int exmoe_unpack_expert(const void* packed, size_t packed_bytes, int H, int I, i
                         int8_t* q_up, int8_t* q_down, exmoe_bf16* s_gate, exmoe_bf16* s_up,
                         exmoe_bf16* s_down);
 
+/* Dense bf16 expert of the comparator layer (abstract; Tab. 1 and Tab. 4: the same model
+ * with its experts left in bf16). A bf16 blob (exmoe_bf16_expert_bytes(H, I) = 6HI bytes)
+ * holds 1 KiB tiles of 16 rows x 32 inputs, no scales:
+ *   tile order: for row block b < I/16: gate tiles c < H/32, then up tiles c < H/32; then
+ *   for row block b < H/16: down tiles c < I/32. Bytes 16l..16l+15 of a tile (lane l < 64)
+ *   hold row 16b + l%16, inputs 32c + 8(l/16) + j (j < 8) as little-endian bf16.
+ * exmoe_bf16_pack only reorders: w_gate, w_up bf16 [I, H], w_down bf16 [H, I] row-major
+ * (host) into out (host, out_bytes >= exmoe_bf16_expert_bytes). A bank of such blobs runs
+ * with the flag EXMOE_WEIGHTS_BF16 on exmoe_moe_forward, exmoe_moe_layer and
+ * exmoe_moe_forward_cached. 0 for H or I not a positive multiple of 128. */
+size_t exmoe_bf16_expert_bytes(int H, int I);
+int exmoe_bf16_pack(const exmoe_bf16* w_gate, const exmoe_bf16* w_up, const exmoe_bf16* w_down, int H, int I,
+                    void* out, size_t out_bytes);
+
 /* ------------------------------------------------------------------------------------
  * Routing (device, asynchronous). Abstract and Fig. 1: the original BF16 router selects
  * the experts and the top-k procedure is unchanged.
@@ -150,7 +164,7 @@ int exmoe_active_experts(const int32_t* expert_offsets, int E, int32_t* ids_host
  * ---------------------------------------------------------------------------------- */
 typedef struct exmoe_expert_bank {
   const void* base;
-  size_t stride;                 /* bytes between slots, >= packed expert bytes, % 16 == 0 */
+  size_t stride;                 /* bytes between slots, >= packed (or bf16) expert bytes, % 16 == 0 */
   const int32_t* expert_to_slot; /* device int32 [E] or NULL for identity */
 } exmoe_expert_bank;
 
@@ -160,7 +174,9 @@ enum {
   EXMOE_PATH_PREFILL = 2,    /* grouped GEMM kernels, large token tiles */
   EXMOE_PATH_SEQUENTIAL = 3, /* per-expert launches in ascending expert order (reference
                                 W4 path; synchronizes once to read the offsets) */
-  EXMOE_PATH_MASK = 0xff
+  EXMOE_PATH_MASK = 0xff,
+  EXMOE_WEIGHTS_BF16 = 0x100 /* flag: the bank holds dense bf16 experts (exmoe_bf16_pack);
+                                paths AUTO, DECODE and PREFILL */
 };
 
 size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, int flags);

@@ -15,16 +15,18 @@ or exact arithmetic. Parity unpinned: absolute layer-output values (no page prin
 tensor) and the choice of scale divisor absmax/7 (a reading, not a page fact).
 """
 from .quant import quantize_group128, dequantize_group128, bf16_bits_to_f64, f64_to_bf16_bits
-from .layout import packed_expert_bytes, pack_expert, unpack_expert, TILE_ROWS, GROUP
+from .layout import (packed_expert_bytes, pack_expert, unpack_expert, TILE_ROWS, GROUP, bf16_expert_bytes,
+                     pack_expert_bf16)
 from .router import router_logits, topk_ids, topk_weights
 from .group import group_tokens
-from .moe import (QuantExpert, quantize_expert, expert_mlp, forward_per_token,
+from .moe import (QuantExpert, DenseExpert, quantize_expert, expert_mlp, forward_per_token,
                   forward_grouped, combine, moe_layer, knockout_rows)
 from .lru import LRUSlotCacheSim
 
 __all__ = [
     "quantize_group128", "dequantize_group128", "bf16_bits_to_f64", "f64_to_bf16_bits",
-    "packed_expert_bytes", "pack_expert", "unpack_expert", "TILE_ROWS", "GROUP",
+    "packed_expert_bytes", "pack_expert", "unpack_expert", "TILE_ROWS", "GROUP", "bf16_expert_bytes",
+    "pack_expert_bf16", "DenseExpert",
     "router_logits", "topk_ids", "topk_weights", "group_tokens",
     "QuantExpert", "quantize_expert", "expert_mlp", "forward_per_token", "forward_grouped",
     "combine", "moe_layer", "knockout_rows", "LRUSlotCacheSim",

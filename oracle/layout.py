@@ -122,3 +122,39 @@ def unpack_expert(blob: bytes, H: int, I: int):
         mats_q[mat][TILE_ROWS * b:TILE_ROWS * (b + 1), GROUP * g:GROUP * (g + 1)] = qt[t]
         mats_s[mat][TILE_ROWS * b:TILE_ROWS * (b + 1), g] = st[t]
     return qg, sg, qu, su, qd, sd
+
+
+# ---------------------------------------------------------------------------- dense bf16 blob
+# The comparator layer runs the same experts with bf16 weights (abstract; Tab. 1 and Tab. 4,
+# the BF16 rows). Its blob (this project's layout) holds 1 KiB tiles of 16 rows x 32 inputs
+# and no scales: first, for row block b in 0..I/16-1, the gate tiles c in 0..H/32-1 and then
+# the up tiles; then, for row block b in 0..H/16-1, the down tiles c in 0..I/32-1. Bytes
+# 16*l .. 16*l+15 of a tile hold row 16b + l % 16, inputs 32c + 8*(l // 16) + j (j = 0..7)
+# as little-endian bf16.
+def bf16_expert_bytes(H: int, I: int) -> int:
+    return 6 * H * I
+
+
+def pack_expert_bf16(g_bits: np.ndarray, u_bits: np.ndarray, d_bits: np.ndarray) -> bytes:
+    """bf16 bits gate [I,H], up [I,H], down [H,I] -> blob bytes, one tile at a time."""
+    I, H = g_bits.shape
+    out = np.empty(bf16_expert_bytes(H, I) // 2, dtype=np.uint16)
+    pos = 0
+
+    def tile(W, b, c):
+        nonlocal pos
+        blk = W[16 * b:16 * b + 16, 32 * c:32 * c + 32]          # [16 rows, 32 inputs]
+        for l in range(64):
+            out[pos + 8 * l: pos + 8 * l + 8] = blk[l % 16, 8 * (l // 16): 8 * (l // 16) + 8]
+        pos += 512
+
+    for b in range(I // 16):
+        for W in (g_bits, u_bits):
+            for c in range(H // 32):
+                tile(W, b, c)
+    for b in range(H // 16):
+        for c in range(I // 32):
+            tile(d_bits, b, c)
+    assert pos == out.size
+    return out.astype("<u2").tobytes()
+

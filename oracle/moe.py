@@ -41,6 +41,28 @@ class QuantExpert:
         self._deq.clear()
 
 
+@dataclass
+class DenseExpert:
+    """An expert of the comparator layer: bf16 weights (bits), used as they are (abstract;
+    Tab. 1 and Tab. 4: the same model with its experts in bf16). deq() gives the weights as
+    fp64, so every driver below runs it unchanged."""
+    g_bits: np.ndarray
+    u_bits: np.ndarray
+    d_bits: np.ndarray
+    _w: dict = field(default_factory=dict, repr=False)
+
+    def deq(self):
+        from .quant import bf16_bits_to_f64
+        if not self._w:
+            self._w["g"] = bf16_bits_to_f64(self.g_bits)
+            self._w["u"] = bf16_bits_to_f64(self.u_bits)
+            self._w["d"] = bf16_bits_to_f64(self.d_bits)
+        return self._w["g"], self._w["u"], self._w["d"]
+
+    def drop_cache(self):
+        self._w.clear()
+
+
 def quantize_expert(w_gate, w_up, w_down) -> QuantExpert:
     qg, sg = quantize_group128(w_gate)
     qu, su = quantize_group128(w_up)

@@ -52,6 +52,24 @@ class Layer:
         self.bank = exm.bank_from_blobs(self.blobs, device)
         self.wr = to_dev_bf16(self.wr_bits, device)
         self.device = device
+        self.bf16_bank = None
+
+    def add_bf16(self, oracle_experts=True):
+        """The comparator's dense bf16 experts: the same fp32 weights rounded to bf16 (an
+        input of both sides), packed by the library, read as they are by the oracle."""
+        import w4a16_mixture_experts_amd as exm
+        from synthetic import f32_to_bf16_bits
+
+        def one(e):
+            bits = [f32_to_bf16_bits(w) for w in self.syn.expert(e)]
+            return exm.bf16_pack(*bits), (oracle.DenseExpert(*bits) if oracle_experts else None)
+
+        with ThreadPoolExecutor(8) as ex:
+            res = list(ex.map(one, range(self.shape.E)))
+        self.bf16_blobs = [b for b, _ in res]
+        self.dense = [d for _, d in res]
+        self.bf16_bank = exm.bank_from_blobs(self.bf16_blobs, self.device)
+        return self
 
 
 def to_dev_bf16(bits: np.ndarray, device="cuda"):

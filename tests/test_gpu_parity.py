@@ -31,16 +31,17 @@ def run_layer(exm, lay: Layer, x_bits, bias=None, flags=0, renormalize=True):
                 y=bf16_dev_to_f64(out.y), y_bits=bf16_dev_to_bits(out.y))
 
 
-def oracle_layer(lay: Layer, x_bits, bias=None, renormalize=True, grouped=False, tokens=None):
+def oracle_layer(lay: Layer, x_bits, bias=None, renormalize=True, grouped=False, tokens=None, experts=None):
     from oracle.quant import bf16_bits_to_f64
+    experts = lay.experts if experts is None else experts
     if not grouped:
-        return oracle.moe_layer(x_bits, lay.wr_bits, lay.experts, lay.shape.k, bias=bias, renormalize=renormalize,
+        return oracle.moe_layer(x_bits, lay.wr_bits, experts, lay.shape.k, bias=bias, renormalize=renormalize,
                                 tokens=tokens)
     logits = oracle.router_logits(x_bits, lay.wr_bits, bias)
     ids = oracle.topk_ids(logits, lay.shape.k)
     w = oracle.topk_weights(logits, ids, renormalize)
     off, sf, fs = oracle.group_tokens(ids, lay.shape.E)
-    y = oracle.forward_grouped(bf16_bits_to_f64(x_bits), ids, w, lay.experts, off, sf)
+    y = oracle.forward_grouped(bf16_bits_to_f64(x_bits), ids, w, experts, off, sf)
     return dict(logits=logits, ids=ids, weights=w, offsets=off, sorted_flat=sf, flat_to_sorted=fs, y=y)
 
 
@@ -315,3 +316,82 @@ def test_olmoe_cached_waves(exm, olmoe):
     assert n_waves > 1
     _same_counters(cache, sim)
     cache.close()
+
+
+# ------------------------------------------------------------------ bf16 comparator
+def run_layer_bf16(exm, lay: Layer, x_bits, bias=None, flags=0):
+    import torch
+    x = to_dev_bf16(x_bits, lay.device)
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(lay.device)
+    out = exm.moe_layer(x, lay.wr, lay.bf16_bank, lay.shape.I, lay.shape.k, bias=b, flags=flags | exm.WEIGHTS_BF16)
+    torch.cuda.synchronize()
+    T = x_bits.shape[0]
+    return dict(logits=bf16_dev_to_bits(out.logits), ids=out.ids.cpu().numpy(), weights=out.weights.cpu().numpy(),
+                offsets=out.offsets.cpu().numpy(), sorted_flat=out.sorted_flat.cpu().numpy()[: T * lay.shape.k],
+                flat_to_sorted=out.flat_to_sorted.cpu().numpy()[: T * lay.shape.k], y=bf16_dev_to_f64(out.y),
+                y_bits=bf16_dev_to_bits(out.y))
+
+
+def oracle_layer_bf16(lay: Layer, x_bits, bias=None):
+    return oracle_layer(lay, x_bits, bias=bias, grouped=x_bits.shape[0] > 64, experts=lay.dense)
+
+
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_tiny_bf16_layer_paths(exm, path):
+    """The comparator layer (dense bf16 experts) against the oracle on the same routing,
+    every path, with a ragged token count."""
+    log(f"tiny bf16 layer, path {path}")
+    lay = Layer(TINY, seed=3, oracle_experts=False).add_bf16()
+    for T in (16, 37):
+        x = lay.syn.x(T, stream=T)
+        ref = oracle_layer_bf16(lay, x)
+        got = run_layer_bf16(exm, lay, x, flags=path)
+        check_routing(got, ref, f"bf16 T={T} path={path}")
+        check_y(got["y"], ref["y"], f"bf16 T={T} path={path}")
+
+
+def test_bf16_sequential_path_unsupported(exm):
+    lay = Layer(TINY, seed=3, oracle_experts=False).add_bf16(oracle_experts=False)
+    with pytest.raises(exm.ExmoeError) as ei:
+        run_layer_bf16(exm, lay, lay.syn.x(4), flags=exm.PATH_SEQUENTIAL)
+    assert ei.value.status == exm.ERR_UNSUPPORTED
+
+
+def test_olmoe_bf16_decode_and_prefill(exm, olmoe):
+    """OLMoE-shaped comparator layer: decode at 1 and 16 tokens, Zipf-biased prefill at
+    512 tokens, against the oracle's bf16 experts."""
+    log("olmoe bf16 comparator: packing 64 dense experts")
+    olmoe.add_bf16()
+    for T, bias in ((1, None), (16, None), (512, olmoe.syn.zipf_bias())):
+        x = olmoe.syn.x(T, stream=40 + T)
+        ref = oracle_layer_bf16(olmoe, x, bias)
+        got = run_layer_bf16(exm, olmoe, x, bias)
+        check_routing(got, ref, f"olmoe bf16 T={T}")
+        check_y(got["y"], ref["y"], f"olmoe bf16 T={T}")
+    for d in olmoe.dense:
+        d.drop_cache()
+
+
+def test_bf16_cached_waves_equal_resident(exm):
+    """Dense bf16 experts through a slot cache in waves: bitwise equal to the resident bf16
+    bank on the decode and prefill paths."""
+    import torch
+    log("bf16 experts through a 5-slot cache")
+    shape = LayerShape(H=256, I=256, E=16, k=4)
+    lay = Layer(shape, seed=22, oracle_experts=False).add_bf16(oracle_experts=False)
+    nb = exm.bf16_expert_bytes(shape.H, shape.I)
+    cache = exm.SlotCache(1, shape.E, 5, nb)
+    for e in range(shape.E):
+        cache.fill(0, e, lay.bf16_blobs[e])
+    for T, path in ((16, 1), (37, 2), (16, 1)):
+        x = to_dev_bf16(lay.syn.x(T, stream=T))
+        logits, ids, w = exm.route_topk(x, lay.wr, shape.k)
+        off, sf, fs = exm.group_tokens(ids, shape.E)
+        active = exm.active_experts(off)
+        fl = path | exm.WEIGHTS_BF16
+        y_c = exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, 0, active, shape.I, flags=fl)
+        y_r = exm.moe_forward(x, ids, w, off, sf, fs, lay.bf16_bank, shape.I, flags=fl)
+        torch.cuda.synchronize()
+        assert torch.equal(y_c.view(torch.int16), y_r.view(torch.int16)), f"T={T} path={path}"
+    cache.close()
+

@@ -53,6 +53,27 @@ def test_packer_bit_exact_olmoe_expert():
     assert blob.tobytes() == OL.pack_expert(qe.qg, qe.sg, qe.qu, qe.su, qe.qd, qe.sd, 2048, 1024)
 
 
+@pytest.mark.parametrize("H,I,seed", [(256, 128, 0), (128, 384, 1)])
+def test_bf16_packer_bit_exact_vs_oracle(H, I, seed):
+    rng = np.random.default_rng(seed)
+    g = rng.integers(0, 1 << 16, size=(I, H), dtype=np.uint16)
+    u = rng.integers(0, 1 << 16, size=(I, H), dtype=np.uint16)
+    d = rng.integers(0, 1 << 16, size=(H, I), dtype=np.uint16)
+    blob = exm.bf16_pack(g, u, d)
+    assert blob.nbytes == exm.bf16_expert_bytes(H, I) == OL.bf16_expert_bytes(H, I) == 6 * H * I
+    assert blob.tobytes() == OL.pack_expert_bf16(g, u, d)
+
+
+def test_bf16_pack_rejects_bad_input():
+    g = np.zeros((128, 128), np.uint16)
+    lib = exm._lib
+    buf = np.zeros(exm.bf16_expert_bytes(128, 128), np.uint8)
+    assert lib.exmoe_bf16_pack(g.ctypes.data, g.ctypes.data, g.ctypes.data, 128, 128, buf.ctypes.data, buf.nbytes - 1) == exm.ERR_INVALID_ARGUMENT
+    assert lib.exmoe_bf16_pack(g.ctypes.data, g.ctypes.data, g.ctypes.data, 96, 128, buf.ctypes.data, buf.nbytes) == exm.ERR_INVALID_ARGUMENT
+    assert lib.exmoe_bf16_pack(None, g.ctypes.data, g.ctypes.data, 128, 128, buf.ctypes.data, buf.nbytes) == exm.ERR_INVALID_ARGUMENT
+    assert exm.bf16_expert_bytes(100, 128) == 0
+
+
 def test_packer_rejects_bad_input():
     g = np.zeros((128, 128), np.float32)
     with pytest.raises(exm.ExmoeError) as ei:

@@ -475,3 +475,56 @@ def test_lru_waves_closed_forms_and_reference():
     assert (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes) == \
         (ref["lookups"], ref["hits"], ref["misses"], ref["evictions"], ref["bytes"])
     assert sim.slot_of[0] == slots[0]
+
+
+# ---------------------------------------------------------------------------- bf16 comparator
+def test_bf16_layout_positions():
+    """Dense bf16 blob: every element lands where the layout statement puts it (tile order
+    gate/up per row block, then down; lane l holds row l % 16, inputs 8 (l // 16) + j)."""
+    H, I = 128, 96 + 32
+    vals = np.random.default_rng(0).permutation(3 * H * I).astype(np.uint16)   # all distinct
+    g = vals[:I * H].reshape(I, H)
+    u = vals[I * H:2 * I * H].reshape(I, H)
+    d = vals[2 * I * H:].reshape(H, I)
+    blob = np.frombuffer(oracle.pack_expert_bf16(g, u, d), dtype="<u2")
+    CH, CI = H // 32, I // 32
+    rng = np.random.default_rng(1)
+    for _ in range(3000):
+        which = int(rng.integers(0, 3))
+        W, R, K = ((g, I, H), (u, I, H), (d, H, I))[which]
+        r, c = int(rng.integers(0, R)), int(rng.integers(0, K))
+        b, cc = r // 16, c // 32
+        if which < 2:
+            t = b * 2 * CH + which * CH + cc
+        else:
+            t = 2 * (I // 16) * CH + b * CI + cc
+        lane = (r % 16) + 16 * ((c % 32) // 8)
+        assert blob[512 * t + 8 * lane + c % 8] == W[r, c]
+
+
+def test_dense_expert_equals_quant_expert_on_exact_weights():
+    """Weights q * 2^-6 with every (row, group) reaching |q| = 7 are exact in bf16 and are
+    quantized back to the same codes and scales, so the bf16 expert and the int4 expert
+    have identical weights and identical outputs."""
+    H, I = 256, 128
+    rng = np.random.default_rng(5)
+
+    def exact(R, K):
+        q = rng.integers(-7, 8, size=(R, K)).astype(np.float32)
+        for gi in range(K // 128):
+            cols = rng.integers(0, 128, size=R) + 128 * gi
+            q[np.arange(R), cols] = rng.choice([-7.0, 7.0], size=R)
+        return q * np.float32(2.0 ** -6)
+
+    wg, wu, wd = exact(I, H), exact(I, H), exact(H, I)
+    bits = [(w.view(np.uint32) >> 16).astype(np.uint16) for w in (wg, wu, wd)]
+    assert all(np.array_equal(oracle.bf16_bits_to_f64(b), w.astype(np.float64)) for b, w in zip(bits, (wg, wu, wd)))
+    de = oracle.DenseExpert(*bits)
+    qe = oracle.quantize_expert(wg, wu, wd)
+    for a, b in zip(de.deq(), qe.deq()):
+        assert np.array_equal(a, b)
+    x = rng.standard_normal((3, H))
+    assert np.array_equal(oracle.expert_mlp(de, x), oracle.expert_mlp(qe, x))
+    # and a transposed or misread matrix would not pass: the bits are the weights
+    assert not np.array_equal(oracle.DenseExpert(bits[1], bits[0], bits[2]).deq()[0], de.deq()[0])
+

@@ -39,6 +39,7 @@ ERR_OUT_OF_MEMORY = -5
 ERR_CACHE = -6
 
 PATH_AUTO, PATH_DECODE, PATH_PREFILL, PATH_SEQUENTIAL = 0, 1, 2, 3
+WEIGHTS_BF16 = 0x100       # flag: the bank holds dense bf16 experts (bf16_pack)
 CACHE_DRY_RUN = 1
 
 _vp = ctypes.c_void_p
@@ -70,6 +71,8 @@ _SIGS = {
     "exmoe_group_tokens": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "exmoe_active_experts": (_i, [_vp, _i, _vp, _vp, _vp]),
     "exmoe_moe_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "exmoe_bf16_expert_bytes": (_sz, [_i, _i]),
+    "exmoe_bf16_pack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _sz]),
     "exmoe_moe_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _sz, _vp]),
     "exmoe_moe_forward_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
@@ -125,6 +128,24 @@ def packed_expert_bytes(H: int, I: int) -> int:
 
 
 # ----------------------------------------------------------------------------- host packer
+def bf16_expert_bytes(H: int, I: int) -> int:
+    return _lib.exmoe_bf16_expert_bytes(H, I)
+
+
+def bf16_pack(g_bits: np.ndarray, u_bits: np.ndarray, d_bits: np.ndarray) -> np.ndarray:
+    """bf16 bits gate [I,H], up [I,H], down [H,I] (uint16) -> dense bf16 blob (uint8 numpy)."""
+    g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    u = np.ascontiguousarray(u_bits, dtype=np.uint16)
+    d = np.ascontiguousarray(d_bits, dtype=np.uint16)
+    I, H = g.shape
+    if u.shape != (I, H) or d.shape != (H, I):
+        raise ValueError("shape mismatch: gate/up [I,H], down [H,I]")
+    nb = bf16_expert_bytes(H, I)
+    out = np.empty(nb, dtype=np.uint8)
+    _check(_lib.exmoe_bf16_pack(g.ctypes.data, u.ctypes.data, d.ctypes.data, H, I, out.ctypes.data, nb))
+    return out
+
+
 def quantize_pack(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, out: Optional[np.ndarray] = None,
                   out_ptr: Optional[int] = None) -> np.ndarray:
     """fp32 gate [I,H], up [I,H], down [H,I] -> packed blob (uint8 numpy, or written to out_ptr)."""

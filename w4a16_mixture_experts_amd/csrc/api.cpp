@@ -236,6 +236,37 @@ int exmoe_unpack_expert(const void* packed, size_t packed_bytes_given, int H, in
   return EXMOE_OK;
 }
 
+size_t exmoe_bf16_expert_bytes(int H, int I) {
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return 0;
+  return bf16_expert_bytes(H, I);
+}
+
+int exmoe_bf16_pack(const exmoe_bf16* w_gate, const exmoe_bf16* w_up, const exmoe_bf16* w_down, int H, int I,
+                    void* out, size_t out_bytes) {
+  if (!w_gate || !w_up || !w_down || !out)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "weights and output buffer must not be NULL");
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "H and I must be positive multiples of 128");
+  if (out_bytes < bf16_expert_bytes(H, I))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "output buffer too small: %zu < %zu", out_bytes, bf16_expert_bytes(H, I));
+  uint16_t* o = static_cast<uint16_t*>(out);
+  // one tile: rows 16b.., inputs 32c..; lane l's 8 values are row l % 16, inputs 8 (l / 16) + j
+  auto tile = [&](const exmoe_bf16* W, int K, int b, int c, uint16_t* dst) {
+    for (int l = 0; l < 64; l++)
+      for (int j = 0; j < 8; j++)
+        dst[8 * l + j] = W[(size_t)(16 * b + l % 16) * K + 32 * c + 8 * (l / 16) + j];
+  };
+  const int CH = H / 32, CI = I / 32;
+  size_t t = 0;
+  for (int b = 0; b < I / kTileRows; b++) {
+    for (int c = 0; c < CH; c++) tile(w_gate, H, b, c, o + 512 * t++);
+    for (int c = 0; c < CH; c++) tile(w_up, H, b, c, o + 512 * t++);
+  }
+  for (int b = 0; b < H / kTileRows; b++)
+    for (int c = 0; c < CI; c++) tile(w_down, I, b, c, o + 512 * t++);
+  return EXMOE_OK;
+}
+
 // ------------------------------------------------------------------------------------
 // Routing and grouping
 // ------------------------------------------------------------------------------------
@@ -390,12 +421,23 @@ extern "C" size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, i
   return moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
 }
 
-static int validate_bank(const exmoe_expert_bank* bank, int H, int I) {
+static int check_flags(int flags) {
+  const int path = flags & EXMOE_PATH_MASK;
+  if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+  if (flags & ~(EXMOE_PATH_MASK | EXMOE_WEIGHTS_BF16))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if ((flags & EXMOE_WEIGHTS_BF16) && path == EXMOE_PATH_SEQUENTIAL)
+    return set_error(EXMOE_ERR_UNSUPPORTED, "bf16 experts run on the decode and prefill paths only");
+  return EXMOE_OK;
+}
+
+static int validate_bank(const exmoe_expert_bank* bank, int H, int I, int flags) {
   if (!bank) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank must not be NULL");
   if (!bank->base || !aligned16(bank->base)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->base must be non-NULL and 16-byte aligned");
   if (bank->stride % 16) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->stride must be a multiple of 16");
-  if (bank->stride < packed_bytes(H, I))
-    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->stride %zu smaller than the packed expert size %zu", bank->stride, packed_bytes(H, I));
+  const size_t eb = (flags & EXMOE_WEIGHTS_BF16) ? bf16_expert_bytes(H, I) : packed_bytes(H, I);
+  if (bank->stride < eb)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->stride %zu smaller than the expert size %zu", bank->stride, eb);
   if (bank->expert_to_slot && ((uintptr_t)bank->expert_to_slot & 3u))
     return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bank->expert_to_slot must be 4-byte aligned");
   return EXMOE_OK;
@@ -411,7 +453,13 @@ static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const 
   a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
   a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
   moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
-  if (path == EXMOE_PATH_DECODE) {
+  if (flags & EXMOE_WEIGHTS_BF16) {
+    a.part = nullptr;   // no sliced partial outputs: y_perm and the plain combine
+    a.nparts = 0;
+    if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_bf16_decode_experts(a, stream));
+    else EXMOE_HIP(launch_bf16_prefill_experts(a, stream));
+    EXMOE_HIP(launch_combine(a, stream));
+  } else if (path == EXMOE_PATH_DECODE) {
     EXMOE_HIP(launch_moe_decode(a, stream));
   } else if (path == EXMOE_PATH_PREFILL) {
     EXMOE_HIP(launch_moe_prefill(a, stream));
@@ -439,10 +487,8 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
                       void* workspace, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(T, H, I, E, k);
   if (st) return st;
-  const int path = flags & EXMOE_PATH_MASK;
-  if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
-  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
-  if ((st = validate_bank(bank, H, I))) return st;
+  if ((st = check_flags(flags))) return st;
+  if ((st = validate_bank(bank, H, I, flags))) return st;
   if (T == 0) return EXMOE_OK;
   CHECK_PTR(x);
   CHECK_PTR(y);
@@ -466,14 +512,15 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
                              hipStream_t stream) {
   int st = check_shape(T, H, I, E, k);
   if (st) return st;
-  const int pflag = flags & EXMOE_PATH_MASK;
-  if (pflag > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", pflag);
-  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if ((st = check_flags(flags))) return st;
   if (!cache) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache must not be NULL");
   int cE = 0, cS = 0, dry = 0;
-  slot_cache_shape(cache, &cE, &cS, &dry);
+  size_t cB = 0;
+  slot_cache_shape(cache, &cE, &cS, &dry, &cB);
   if (dry) return set_error(EXMOE_ERR_CACHE, "a dry-run cache holds no weights");
   if (cE != E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache has %d experts per layer, the layer %d", cE, E);
+  const size_t eb = (flags & EXMOE_WEIGHTS_BF16) ? bf16_expert_bytes(H, I) : packed_bytes(H, I);
+  if (cB < eb) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache holds %zu bytes per expert, %zu needed", cB, eb);
   if (n_active < 0 || (n_active > 0 && !active_ids_host))
     return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bad active list");
   std::vector<int32_t> A(active_ids_host, active_ids_host + n_active);
@@ -499,7 +546,12 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
   a.flat_to_sorted = flat_to_sorted; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
   moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
-  if (path == EXMOE_PATH_PREFILL) EXMOE_HIP(launch_moe_prefill_xsum(a, stream));
+  const bool bf16w = (flags & EXMOE_WEIGHTS_BF16) != 0;
+  if (bf16w) {
+    a.part = nullptr;
+    a.nparts = 0;
+  }
+  if (path == EXMOE_PATH_PREFILL && !bf16w) EXMOE_HIP(launch_moe_prefill_xsum(a, stream));
   // Waves: the active experts already resident first, then the others, each in ascending
   // id (a repeated active set larger than the cache then hits S times instead of
   // thrashing the LRU). An active set that fits is one wave; a larger one runs in waves of
@@ -542,8 +594,14 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
     a.stride = bank.stride;
     a.e2s = a.wave_table;
     a.skip_absent = 1;
-    if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_moe_decode_experts(a, stream));
-    else EXMOE_HIP(launch_moe_prefill_experts(a, stream));
+    if (bf16w) {
+      if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_bf16_decode_experts(a, stream));
+      else EXMOE_HIP(launch_bf16_prefill_experts(a, stream));
+    } else if (path == EXMOE_PATH_DECODE) {
+      EXMOE_HIP(launch_moe_decode_experts(a, stream));
+    } else {
+      EXMOE_HIP(launch_moe_prefill_experts(a, stream));
+    }
     if (w + 2 < n_waves) {   // the mark that wave w+2's copies wait for
       EXMOE_HIP(slot_cache_event(cache, w + 1, &mark));
       EXMOE_HIP(hipEventRecord(mark, stream));
@@ -564,10 +622,8 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
                     hipStream_t stream) {
   int st = check_shape(T, H, I, E, k);
   if (st) return st;
-  const int path = flags & EXMOE_PATH_MASK;
-  if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
-  if (flags & ~EXMOE_PATH_MASK) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
-  if ((st = validate_bank(bank, H, I))) return st;
+  if ((st = check_flags(flags))) return st;
+  if ((st = validate_bank(bank, H, I, flags))) return st;
   CHECK_PTR4(expert_offsets);
   if (T == 0) return exmoe_group_tokens(topk_ids, 0, k, E, expert_offsets, sorted_flat, flat_to_sorted, nullptr, 0, stream);
   CHECK_PTR(x);
@@ -583,7 +639,8 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
   if (!workspace || ws_bytes < need)
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (choose_path(T, E, k, flags) == EXMOE_PATH_DECODE && (long long)T * k <= kDecMaxRows) {
+  if (!(flags & EXMOE_WEIGHTS_BF16) && choose_path(T, E, k, flags) == EXMOE_PATH_DECODE &&
+      (long long)T * k <= kDecMaxRows) {
     // Decode sizes: the expert kernel groups the rows itself and publishes the grouping;
     // for a few tokens it also makes the top-k selection from the logits, otherwise one
     // workgroup per token routes it first.

@@ -24,6 +24,8 @@ __host__ __device__ inline size_t n_tiles(int H, int I) {
   return 2 * (size_t)(I / kTileRows) * (H / kGroup) + (size_t)(H / kTileRows) * (I / kGroup);
 }
 __host__ __device__ inline size_t packed_bytes(int H, int I) { return n_tiles(H, I) * (kTileBytes + kScaleBytes); }
+// dense bf16 expert of the comparator: gate, up and down, 2 bytes per weight
+__host__ __device__ inline size_t bf16_expert_bytes(int H, int I) { return (size_t)6 * H * I; }
 
 // Thread-local error reporting.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -143,8 +145,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 // The same paths in parts (a forward in waves runs the expert kernels once per wave and
 // the correction sums and the combine once): decode experts; prefill sums, experts.
 hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s);
-// Experts per layer, slots per layer and dry-run flag of a slot cache.
-void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry);
+// Experts per layer, slots per layer, dry-run flag and bytes per expert of a slot cache.
+void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry, size_t* expert_bytes);
 // exmoe_slot_cache_acquire whose copies wait only for `after` (an event recorded on the
 // compute stream) unless one of them lands in a slot of protect_slots; after == NULL
 // waits for everything enqueued on the compute stream so far (the public behaviour).
@@ -154,6 +156,9 @@ int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_
 // Event i of the cache's pool (created on first use, destroyed with the cache).
 hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev);
 hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s);
+// Dense bf16 experts (the comparator): decode and prefill expert kernels.
+hipError_t launch_bf16_decode_experts(const MoeArgs& a, hipStream_t s);
+hipError_t launch_bf16_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);

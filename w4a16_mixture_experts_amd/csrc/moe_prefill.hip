@@ -100,11 +100,14 @@ __device__ __forceinline__ void dma4(const void* src, void* dst) {
 // 8 token subtiles of the 256 x 128 tile. Tokens are the M operand of the MFMA and weight
 // rows the N operand, so a lane's 4 accumulator values belong to one weight row (one
 // scale) and 4 consecutive tokens (one float4 of correction seeds).
-template <bool GATEUP, int NW>
+// Q4 = false: the bank holds dense bf16 experts (the comparator), 1 KiB tiles of 16 rows x
+// 32 columns in operand order, four per 128-column group; no scales and no seeds.
+template <bool GATEUP, int NW, bool Q4>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixed_expert,
                                                            int n_row_tiles) {
   constexpr int NT = NW * 64;            // threads
   constexpr int NA = 16 / NW;            // row subtiles per wave
+  constexpr int NL = Q4 ? 1 : 4;         // 16-byte weight loads per lane, row subtile and group
   // two buffers as separate arrays: the compiler then sees that reading one does not wait
   // for the copies into the other
   __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   }
   const uint8_t* blob = a.base + a.stride * (size_t)slot;
   const uint4* tiles = reinterpret_cast<const uint4*>(blob);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + n_tiles(a.H, a.I) * kTileBytes);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + (Q4 ? n_tiles(a.H, a.I) * kTileBytes : 0));
   const int K = GATEUP ? a.H : a.I;
   const int G = K / kGroup;
   const size_t tile_down0 = 2 * (size_t)(a.I / kTileRows) * (a.H / kGroup);
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   do {                                                                                                  \
     _Pragma("unroll") for (int i = 0; i < kDmaPerWave; i++)                                             \
         dma16(drow[i] + (g_) * kGroup, &ACT[(wave * kDmaPerWave + i) * 4 * kLdsStride]);                \
-    if (wave < 2) dma4(seed_src + (size_t)(g_) * rows_pad, &SEED[wave * 64]);                           \
+    if (Q4 && wave < 2) dma4(seed_src + (size_t)(g_) * rows_pad, &SEED[wave * 64]);                     \
   } while (0)
 
   f32x4 acc[NA][8];
@@ -183,13 +186,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
 #pragma unroll
     for (int bj = 0; bj < 8; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wcur[NA], wnext[NA];
+  uint4 wcur[NA][NL], wnext[NA][NL];
   uint32_t scur[NA], snext[NA];
 #pragma unroll
   for (int ai = 0; ai < NA; ai++) {
     const size_t t = tbase[ai];
-    wcur[ai] = tiles[t * 64 + lane];
-    scur[ai] = scales[t * 16 + (lane & 15)];
+#pragma unroll
+    for (int q = 0; q < NL; q++) wcur[ai][q] = tiles[(t * NL + q) * 64 + lane];
+    if (Q4) scur[ai] = scales[t * 16 + (lane & 15)];
   }
   EXMOE_STAGE(0, s_act0, s_seed0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -204,22 +208,32 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
 #pragma unroll
     for (int ai = 0; ai < NA; ai++) {
       const size_t t = tbase[ai] + gn;
-      wnext[ai] = tiles[t * 64 + lane];
-      snext[ai] = scales[t * 16 + (lane & 15)];
+#pragma unroll
+      for (int q = 0; q < NL; q++) wnext[ai][q] = tiles[(t * NL + q) * 64 + lane];
+      if (Q4) snext[ai] = scales[t * 16 + (lane & 15)];
     }
     __builtin_amdgcn_sched_barrier(0);
-    // weight fragments of the group, dequantized once: [row subtile][K step]
+    // weight fragments of the group (dequantized once): [row subtile][K step]
     bf16x8 wfr[NA][4];
 #pragma unroll
     for (int ai = 0; ai < NA; ai++) {
-      wfr[ai][0] = dequant_word(wcur[ai].x);
-      wfr[ai][1] = dequant_word(wcur[ai].y);
-      wfr[ai][2] = dequant_word(wcur[ai].z);
-      wfr[ai][3] = dequant_word(wcur[ai].w);
+      if (Q4) {
+        wfr[ai][0] = dequant_word(wcur[ai][0].x);
+        wfr[ai][1] = dequant_word(wcur[ai][0].y);
+        wfr[ai][2] = dequant_word(wcur[ai][0].z);
+        wfr[ai][3] = dequant_word(wcur[ai][0].w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint4 v = wcur[ai][Q4 ? 0 : q];
+          i32x4 iv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          wfr[ai][q] = __builtin_bit_cast(bf16x8, iv);
+        }
+      }
     }
     float sc[NA];
 #pragma unroll
-    for (int ai = 0; ai < NA; ai++) sc[ai] = __uint_as_float(scur[ai] << 16);
+    for (int ai = 0; ai < NA; ai++) sc[ai] = Q4 ? __uint_as_float(scur[ai] << 16) : 1.0f;
     // token subtiles in pairs: activation fragments of both for all 4 K steps
 #pragma unroll
     for (int p = 0; p < 4; p++) {
@@ -236,19 +250,26 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
           xfr[j][s4] = __builtin_bit_cast(bf16x8, iv);
         }
         // seeds of tokens 4(l/16)+0..3 of the subtile: -136 * group sum of their activations
-        seed[j] = *reinterpret_cast<const f32x4*>(&cseed[(2 * p + j) * 16 + 4 * (lane >> 4)]);
+        if (Q4) seed[j] = *reinterpret_cast<const f32x4*>(&cseed[(2 * p + j) * 16 + 4 * (lane >> 4)]);
       }
 #pragma unroll
       for (int j = 0; j < 2; j++) {
         const int bj = 2 * p + j;
 #pragma unroll
         for (int ai = 0; ai < NA; ai++) {
-          f32x4 t = mfma16(xfr[j][0], wfr[ai][0], seed[j]);
-          t = mfma16(xfr[j][1], wfr[ai][1], t);
-          t = mfma16(xfr[j][2], wfr[ai][2], t);
-          t = mfma16(xfr[j][3], wfr[ai][3], t);
+          if (Q4) {
+            f32x4 t = mfma16(xfr[j][0], wfr[ai][0], seed[j]);
+            t = mfma16(xfr[j][1], wfr[ai][1], t);
+            t = mfma16(xfr[j][2], wfr[ai][2], t);
+            t = mfma16(xfr[j][3], wfr[ai][3], t);
 #pragma unroll
-          for (int i = 0; i < 4; i++) acc[ai][bj][i] += sc[ai] * t[i];
+            for (int i = 0; i < 4; i++) acc[ai][bj][i] += sc[ai] * t[i];
+          } else {   // bf16 weights: one chain straight into the accumulator
+            f32x4 t = mfma16(xfr[j][0], wfr[ai][0], acc[ai][bj]);
+            t = mfma16(xfr[j][1], wfr[ai][1], t);
+            t = mfma16(xfr[j][2], wfr[ai][2], t);
+            acc[ai][bj] = mfma16(xfr[j][3], wfr[ai][3], t);
+          }
         }
       }
     }
@@ -257,7 +278,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int ai = 0; ai < NA; ai++) {
-      wcur[ai] = wnext[ai];
+#pragma unroll
+      for (int q = 0; q < NL; q++) wcur[ai][q] = wnext[ai][q];
       scur[ai] = snext[ai];
     }
   };
@@ -292,7 +314,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
       }
     }
     // per-token sum over this workgroup's 128 intermediate columns (one down group):
-    // the 16 lanes of a row hold 16 columns each
+    // the 16 lanes of a row hold 16 columns each (the int4 down kernel's correction)
+    if (Q4) {
 #pragma unroll
     for (int bj = 0; bj < 8; bj++)
 #pragma unroll
@@ -313,6 +336,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         for (int w = 1; w < NW; w++) v += s_gsum[w][tid];
         a.gsum[(size_t)rt * rows_pad + pt.seg0 + r] = -136.0f * v;
       }
+    }
     }
   } else {
 #pragma unroll
@@ -369,29 +393,33 @@ hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) {
+template <bool Q4>
+static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
   const int TK = a.T * a.k;
   const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
   const int rt_gu = a.I / 128;
   {
-    ProfScope prof("prefill_gateup", s);
+    ProfScope prof(Q4 ? "prefill_gateup" : "bf16_prefill_gateup", s);
     MoeArgs as = a;
     as.span = prof.span();
-    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, as, -1,
-                       rt_gu);
+    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves, Q4>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, as,
+                 -1, rt_gu);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rt_d = (a.H + kPfRows - 1) / kPfRows;
   {
-    ProfScope prof("prefill_down", s);
+    ProfScope prof(Q4 ? "prefill_down" : "bf16_prefill_down", s);
     MoeArgs as = a;
     as.span = prof.span();
-    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, as, -1,
-                       rt_d);
+    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves, Q4>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, as,
+                 -1, rt_d);
   }
   return hipGetLastError();
 }
+
+hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<true>(a, s); }
+hipError_t launch_bf16_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<false>(a, s); }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
   hipError_t e = launch_moe_prefill_xsum(a, s);

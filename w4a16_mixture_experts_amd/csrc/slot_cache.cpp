@@ -49,10 +49,11 @@ static void cache_free(exmoe_slot_cache* c) {
 }
 
 namespace exmoe {
-void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry) {
+void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry, size_t* expert_bytes) {
   *E = c->E;
   *S = c->S;
   *dry = c->dry ? 1 : 0;
+  *expert_bytes = c->expert_bytes;
 }
 
 hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev) {
