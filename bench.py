@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16", "batched"],
+                    default=None,
                     help="run a single workload (for profiling)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (traffic-counter calibration)")
@@ -238,7 +239,7 @@ def main():
         log(f"calibration copy: 3 x {nb} bytes")
         del src, dst
 
-    if args.only in (None, "decode", "prefill", "cache", "prefill_cache", "bf16"):
+    if args.only in (None, "decode", "prefill", "cache", "prefill_cache", "bf16", "batched"):
         olmoe_syn, banks, olmoe_blobs = build_olmoe(exm, torch, args.rotate)
         wr = to_dev_bf16(olmoe_syn.router())
 
@@ -452,6 +453,99 @@ def main():
 
     if not args.no_secondary and args.only in (None, "bf16"):
         secondary.update(run_bf16_comparator())
+
+    # ------------------------------------------------------------------ batched decode through the cache
+    def run_batched_cache(batches=(1, 2, 4, 8), S=16, layers=16, steps=64):
+        """Batched generation analogue: B sequences decoded together (T = B tokens per call)
+        through `layers` OLMoE-shaped expert layers. The experts sit behind S slots per layer
+        (the batch's distinct experts per layer run in cache-sized waves; the host drives
+        every layer, since each needs its active set), or are resident (int4, and the bf16
+        comparator; those steps are captured in one graph and replayed). Routing comes from a
+        per-sequence trace over each layer's shared Zipf(1.1) popularity (reuse 0.5); every
+        layer shares one set of expert values. The first `steps` steps warm up, the next
+        `steps` are timed; tokens/s = B * steps / wall clock."""
+        from synthetic import batch_trace
+        Bmax = max(batches)
+        trace = batch_trace(E, k, layers, 2 * steps, Bmax, seed=0)
+        ids_all = torch.from_numpy(np.ascontiguousarray(trace)).cuda()          # [steps, layers, B, k]
+        xs = [to_dev_bf16(olmoe_syn.x(Bmax, stream=9000 + st)) for st in range(2 * steps)]
+        bank_bf = build_bf16_banks()[0]
+        cache = exm.SlotCache(layers, E, S, expert_bytes)
+        for l in range(layers):
+            for e in range(E):
+                cache.fill(l, e, olmoe_blobs[e])
+        out = {}
+        for B in batches:
+            ws = exm.alloc_workspace(exm.moe_workspace_bytes(B, H, I, E, k))
+            y = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            rec = {"batch": B, "slots": S, "layers": layers, "steps": steps}
+            for name in ("w4a16_S%d" % S, "w4a16_resident", "bf16_resident"):
+                n_act = 0
+
+                def run(lo, hi):
+                    nonlocal n_act
+                    for st in range(lo, hi):
+                        x = xs[st][:B]
+                        for l in range(layers):
+                            ids = ids_all[st, l, :B]
+                            logits, _, _ = exm.route_topk(x, wr, k)
+                            w = exm.route_weights(logits, ids)
+                            off, sf, fs = exm.group_tokens(ids, E)
+                            if name == "bf16_resident":
+                                exm.moe_forward(x, ids, w, off, sf, fs, bank_bf, I, flags=exm.WEIGHTS_BF16, y=y,
+                                                workspace=ws)
+                            elif name == "w4a16_resident":
+                                exm.moe_forward(x, ids, w, off, sf, fs, banks[0], I, y=y, workspace=ws)
+                            else:
+                                active = np.unique(trace[st, l, :B]).tolist()
+                                n_act += len(active)
+                                exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, l, active, I, y=y,
+                                                       workspace=ws)
+
+                run(0, steps)
+                torch.cuda.synchronize()
+                graph = None
+                if name != "w4a16_S%d" % S:
+                    graph = torch.cuda.CUDAGraph()
+                    s_ = torch.cuda.Stream()
+                    s_.wait_stream(torch.cuda.current_stream())
+                    with torch.cuda.stream(s_):
+                        with torch.cuda.graph(graph, stream=s_):
+                            run(steps, 2 * steps)
+                    torch.cuda.current_stream().wait_stream(s_)
+                    graph.replay()
+                    torch.cuda.synchronize()
+                else:
+                    cache.reset_stats()
+                    n_act = 0
+                t0 = time.time()
+                if graph is not None:
+                    graph.replay()
+                else:
+                    run(steps, 2 * steps)
+                torch.cuda.synchronize()
+                dt = time.time() - t0
+                del graph
+                r = {"tokens_per_s": B * steps / dt, "ms_per_step": dt / steps * 1e3}
+                if name == "w4a16_S%d" % S:
+                    st_ = cache.stats()
+                    r.update({"distinct_experts_per_layer": n_act / steps / layers,
+                              "hit_rate": st_["hits"] / max(st_["lookups"], 1), "misses": st_["misses"],
+                              "h2d_bytes_per_step": st_["h2d_bytes"] / steps})
+                rec[name] = r
+            rec["w4a16_S%d_over_bf16" % S] = rec["w4a16_S%d" % S]["tokens_per_s"] / rec["bf16_resident"]["tokens_per_s"]
+            rec["w4a16_resident_over_bf16"] = rec["w4a16_resident"]["tokens_per_s"] / rec["bf16_resident"]["tokens_per_s"]
+            c16 = rec["w4a16_S%d" % S]
+            log(f"batched decode B={B}: S={S} {c16['tokens_per_s']:.0f} tok/s (hit {c16['hit_rate'] * 100:.1f}%, "
+                f"{c16['h2d_bytes_per_step'] / 1e6:.0f} MB H2D/step, {c16['distinct_experts_per_layer']:.1f} experts/layer), "
+                f"resident {rec['w4a16_resident']['tokens_per_s']:.0f}, bf16 {rec['bf16_resident']['tokens_per_s']:.0f} tok/s")
+            out[f"batched_decode_B{B}"] = rec
+        cache.close()
+        torch.cuda.empty_cache()
+        return out
+
+    if not args.no_secondary and args.only in (None, "batched"):
+        secondary.update(run_batched_cache())
 
     # ------------------------------------------------------------------ prefill through the slot cache
     def run_prefill_cache(slots_list, T=512, layers=16, warm=2, timed=5):

@@ -141,3 +141,42 @@ def slot_cache_trace(E: int, k: int, layers: int, steps: int, seed: int,
             out[st, l] = chosen
             prev = chosen
     return out
+
+
+def batch_trace(E: int, k: int, layers: int, steps: int, batch: int, seed: int,
+                s_exp: float = 1.1, reuse: float = 0.5) -> np.ndarray:
+    """Routing trace int32 [steps, layers, batch, k] of a batch of sequences decoded together.
+
+    The sequences share each layer's Zipf(s) popularity over a seeded permutation (one
+    model); each sequence walks it on its own generator like slot_cache_trace: step 0 draws
+    k distinct experts, each later pick is, with probability ``reuse``, uniform over that
+    sequence's previous experts not yet picked, else drawn from the popularity renormalized
+    over the experts not yet picked.
+    """
+    pop = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xB7])))
+    ranks = np.arange(1, E + 1, dtype=np.float64) ** (-s_exp)
+    out = np.empty((steps, layers, batch, k), dtype=np.int32)
+    for l in range(layers):
+        perm = pop.permutation(E)
+        p = np.empty(E)
+        p[perm] = ranks
+        p /= p.sum()
+        for b in range(batch):
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xB8, l, b])))
+            prev: list[int] = []
+            for st in range(steps):
+                chosen: list[int] = []
+                for _ in range(k):
+                    cand_prev = [e for e in prev if e not in chosen]
+                    if st > 0 and cand_prev and rng.random() < reuse:
+                        e = cand_prev[int(rng.integers(len(cand_prev)))]
+                    else:
+                        q = p.copy()
+                        q[chosen] = 0.0
+                        q /= q.sum()
+                        e = int(rng.choice(E, p=q))
+                    chosen.append(e)
+                out[st, l, b] = chosen
+                prev = chosen
+    return out
+
