@@ -161,7 +161,20 @@ def olmoe(exm):
     return Layer(OLMOE, seed=0)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T,path", [(1, 0), (3, 0), (5, 0), (1, 1), (3, 1)])
+def test_tiny_few_tokens_narrow_kernel(exm, tiny, T, path):
+    """A few routed rows (the narrow fused kernel: 32-row slices, quarters of the input
+    groups, one 32-input step of each down tile): here H = 256 leaves two of the four
+    quarters and most down row blocks empty."""
+    log(f"tiny layer T={T} path={path}")
+    x = tiny.syn.x(T, stream=60 + T)
+    ref = oracle_layer(tiny, x)
+    got = run_layer(exm, tiny, x, flags=path)
+    check_routing(got, ref, f"T={T} path={path}")
+    check_y(got["y"], ref["y"], f"T={T} path={path}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
 def test_olmoe_decode(exm, olmoe, T):
     log(f"olmoe decode T={T}")
     x = olmoe.syn.x(T)

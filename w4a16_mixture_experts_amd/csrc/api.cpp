@@ -394,7 +394,7 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   const size_t o_gs = take((rows + 128) * (I / kGroup) * 4);
   const size_t o_xs = take((rows + 128) * (H / kGroup) * 4);
   // fused decode: down-projection partial outputs per 128-wide slice of I
-  const int fused_waves = path == EXMOE_PATH_DECODE ? decode_fused_waves(T, I, E, k) : 0;
+  const int fused_waves = path == EXMOE_PATH_DECODE ? decode_fused_waves(T, H, I, E, k) : 0;
   const int nparts = fused_waves ? I / (kTileRows * fused_waves) : 0;
   const size_t o_pt = take((size_t)nparts * rows * H * 4);
   const size_t o_sel = take((size_t)E * 16);

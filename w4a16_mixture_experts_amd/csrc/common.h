@@ -120,9 +120,10 @@ constexpr int kDecMaxRows = 1024;
 // Decode path from offsets and permutation given by the caller.
 hipError_t launch_moe_decode(const MoeArgs& a, hipStream_t s);
 // Whether the decode path runs gate/up and down in one kernel (down outputs per slice of
-// 16 * waves rows of I, summed by the combine), and with how many waves per workgroup
-// (8 or 16; 0: two kernels): enough workgroups and few slices.
-int decode_fused_waves(int T, int I, int E, int k);
+// 16 * the returned value rows of I, summed by the combine): 16 or 8 (that many waves per
+// workgroup, one row block each) when that gives enough workgroups, 2 for the narrow
+// kernel (32-row slices, 16 waves) when only a few rows are routed; 0: two kernels.
+int decode_fused_waves(int T, int H, int I, int E, int k);
 // Logits, top-k selection and routing weights of each token by one workgroup per token.
 hipError_t launch_route_token(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
                               int k, int renormalize, uint16_t* logits, int32_t* ids, float* w, hipStream_t s);

@@ -778,6 +778,152 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 }
 
 // ------------------------------------------------------------------------------------
+// Narrow fused gate/up + down for very few routed rows (T <= 16, H <= kDecKC), when the
+// 8-wave fused kernel would leave most compute units idle (one token routes to k experts:
+// k x I/128 workgroups). A compute unit streams about 30 GB/s however deep its queue of
+// loads, so the expert is cut four times finer: workgroup = (expert, slice c of 32 rows of
+// I), 16 waves. Phase 1: wave w computes tile row w % 4 (gate and up of the slice's two
+// row blocks) over quarter w / 4 of the input groups; the quarters are added in LDS and
+// h of the slice (32 columns) goes to LDS as bf16. Phase 2: the slice is one 32-input
+// step (word c % 4 of group c / 4) of every down tile; wave w applies it to row blocks
+// kNarD w .. kNarD w + kNarD - 1 and writes fp32 partial outputs part[c][f][H]. Every
+// weight load of the workgroup is issued at once, right after the expert is known.
+// ------------------------------------------------------------------------------------
+constexpr int kNarRows = 32;                          // rows of I per workgroup
+constexpr int kNarQ = 4;                              // input quarters of the gate/up phase
+constexpr int kNarG = kDecKG / kNarQ;                 // groups per quarter (H <= kDecKC)
+constexpr int kNarD = kDecKC / kTileRows / 16;        // down row blocks per wave (H <= kDecKC)
+
+template <int SRC>
+__global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPublish pub) {
+  constexpr int NW = 16, NT = 64 * NW;
+  __shared__ DecLDS L;
+  __shared__ f32x4 red[NW][64];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kDecTok][kNarRows + 8];
+  const int tid = threadIdx.x, lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  span_begin(a.span);
+  const int nslice = a.I / kNarRows;
+  const int aidx = blockIdx.x / nslice, cs = blockIdx.x % nslice;
+  const int G = a.H / kGroup, GQ = (G + kNarQ - 1) / kNarQ;
+  const int nrbd = a.H / kTileRows, Gd = a.I / kGroup;
+  const int tr = wave & 3, q = wave >> 2;               // tile row (row block 2c + tr / 2, gate / up), quarter
+  const uint32_t tbase = (uint32_t)((cs * 2 + (tr >> 1)) * 2 + (tr & 1)) * G;
+  const uint32_t dbase = 2u * (uint32_t)(a.I / kTileRows) * (uint32_t)G;
+  const uint32_t sc_base = (uint32_t)(n_tiles(a.H, a.I) * kTileBytes);
+  const int nbytes = (int)packed_bytes(a.H, a.I);
+  const uint32_t lo_t = (uint32_t)lane * 16u, lo_s = (uint32_t)(lane >> 4) * 8u;
+  const uint32_t lo_w = lo_t + 4u * (uint32_t)(cs & 3);  // the slice's word of a down tile
+  const bf16x8 n136 = neg136_operand();
+
+  for (int i = tid; i < kDecXS / 8; i += NT)
+    *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
+  const DecPre pre = dec_preload<SRC, NT>(a, pub);
+  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+    dec_publish<NT>(a, L, pub);
+    return;
+  }
+  if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  DecExpert ex;
+  if (!dec_setup<SRC, false, NT>(a, L, pub, pre, -1, aidx, cs == 0, 0, ex)) return;
+
+  // every weight load at once (positions past the data load through a zero-length resource)
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rnone = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, 0, 0x00020000);
+  uint4 w1[kNarG];
+  uint2 s1[kNarG];
+  uint32_t w2[kNarD];
+  uint2 s2[kNarD];
+#pragma unroll
+  for (int i = 0; i < kNarG; i++) {
+    const int g = q * GQ + i;
+    const bool on = i < GQ && g < G;
+    const uint32_t t = tbase + (uint32_t)(on ? g : 0);
+    w1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(on ? rsrc : rnone, lo_t, (int)(t * kTileBytes), 0));
+    s1[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), 0));
+  }
+#pragma unroll
+  for (int i = 0; i < kNarD; i++) {
+    const int r = wave * kNarD + i;
+    const bool on = r < nrbd;
+    const uint32_t t = dbase + (uint32_t)(on ? r : 0) * Gd + (uint32_t)(cs >> 2);
+    w2[i] = __builtin_amdgcn_raw_buffer_load_b32(on ? rsrc : rnone, lo_w, (int)(t * kTileBytes), 0);
+    s2[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), 0));
+  }
+
+  // the expert's rows (at most T <= kDecTok: one pass)
+  const int nrow = ex.cnt;
+  if (tid < kDecTok)
+    L.pf[tid] = tid < nrow ? (SRC == kSrcSel ? L.srows[tid] : SRC == kSrcIds ? L.rows[tid] : a.sorted_flat[ex.seg0 + tid])
+                           : -1;
+  __syncthreads();
+  if (SRC != kSrcSel) {   // table routing: every token row is already staged
+    const int cw8 = a.H / 8;
+    for (int i = tid; i < nrow * cw8; i += NT) {
+      const int r = i / cw8, c8 = i - r * cw8;
+      *reinterpret_cast<uint4*>(L.xs + r * kDecXS + c8 * 8) =
+          *reinterpret_cast<const uint4*>(a.x + (size_t)(L.pf[r] / a.k) * a.H + c8 * 8);
+    }
+    __syncthreads();
+  }
+  // ---- phase 1: this wave's tile row over its quarter of the input groups
+  const int myrow = (lane & 15) < nrow ? (SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
+  const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kNarG; i++) {
+    const int g = q * GQ + i;
+    if (i < GQ && g < G) {
+      bf16x8 act[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) act[s4] = *reinterpret_cast<const bf16x8*>(xrow + g * kGroup + 32 * s4);
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) c = mfma16(n136, act[s4], c);   // seed: -136 * group sum
+      c = mfma16(dequant_word(w1[i].x), act[0], c);
+      c = mfma16(dequant_word(w1[i].y), act[1], c);
+      c = mfma16(dequant_word(w1[i].z), act[2], c);
+      c = mfma16(dequant_word(w1[i].w), act[3], c);
+      scale_accum(acc, c, s1[i]);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave < 2) {   // row block 2c + wave: gate tile row 2 wave, up tile row 2 wave + 1
+    f32x4 g = red[2 * wave][lane], u = red[2 * wave + 1][lane];
+#pragma unroll
+    for (int qq = 1; qq < kNarQ; qq++) {
+      g += red[2 * wave + 4 * qq][lane];
+      u += red[2 * wave + 1 + 4 * qq][lane];
+    }
+    uint16_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(g[i] / (1.0f + expf(-g[i])) * u[i]);
+    uint2 pk;
+    pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+    pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+    *reinterpret_cast<uint2*>(&hs[lane & 15][wave * 16 + 4 * (lane >> 4)]) = pk;
+  }
+  __syncthreads();
+  // ---- phase 2: the slice's 32 inputs of this wave's down row blocks
+  const bf16x8 acth = *reinterpret_cast<const bf16x8*>(&hs[lane & 15][8 * (lane >> 4)]);
+  const f32x4 sdh = mfma16(n136, acth, f32x4{0.f, 0.f, 0.f, 0.f});
+  const int f = L.pf[lane & 15];
+  float* prow = a.part + ((size_t)cs * a.T * a.k + (f >= 0 ? f : 0)) * a.H + 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < kNarD; i++) {
+    const int r = wave * kNarD + i;
+    if (r < nrbd) {
+      const f32x4 c = mfma16(dequant_word(w2[i]), acth, sdh);
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      scale_accum(o, c, s2[i]);
+      if (f >= 0) *reinterpret_cast<float4*>(prow + r * 16) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  span_end(a.span);
+}
+
+// ------------------------------------------------------------------------------------
 // combine: y[t, rows] = bf16(sum_j y_perm[t k + j, rows]) in slot order
 // ------------------------------------------------------------------------------------
 constexpr int kCombineTok = 16;
@@ -817,9 +963,19 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < a.H) {
       const float* src = a.part + ((size_t)t * a.k + j) * a.H + c;
-      for (int q = 0; q < a.nparts; q++) {
-        const float4 v = *reinterpret_cast<const float4*>(src + q * slice);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      // sixteen slices in flight at a time, added in slice order
+      for (int q0 = 0; q0 < a.nparts; q0 += 16) {
+        float4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+          const int q = q0 + u < a.nparts ? q0 + u : a.nparts - 1;
+          v[u] = *reinterpret_cast<const float4*>(src + q * slice);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; u++)
+          if (q0 + u < a.nparts) {
+            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+          }
       }
       const float wt = a.w[t * a.k + j];
       s.x *= wt; s.y *= wt; s.z *= wt; s.w *= wt;
@@ -880,13 +1036,15 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
     EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, as, pub, fixed_expert, nchunk);
 }
 
-int decode_fused_waves(int T, int I, int E, int k) {
+int decode_fused_waves(int T, int H, int I, int E, int k) {
   const long long tk = (long long)T * k;
   const long long ny = E < tk ? E : tk;
   // most experts active and one 16-wave workgroup per compute unit or more: 16 waves
   if (tk >= 2LL * E && I % (2 * kGroup) == 0 && I / (2 * kGroup) <= 8 && (long long)E * (I / (2 * kGroup)) >= 256)
     return 16;
   if (I / kGroup <= 16 && ny * (I / kGroup) >= 256) return 8;
+  // a few routed rows: the narrow kernel (32-row slices; reported as 2 waves' worth of rows)
+  if (T <= kDecTok && H <= kDecKC && tk < 2LL * E) return kNarRows / kTileRows;
   return 0;
 }
 
@@ -903,7 +1061,9 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
 #define EXMOE_FUSED(SRC, P)                                                                                      \
   do {                                                                                                          \
     const dim3 grid((all ? a.E : ny) * a.nparts + extra);                                                       \
-    if (nw == 16) {                                                                                             \
+    if (nw == kNarRows / kTileRows) {                                                                           \
+      EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * a.nparts + extra), dim3(1024), 0, s, as, P);       \
+    } else if (nw == 16) {                                                                                      \
       if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert); \
       else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert);    \
     } else {                                                                                                    \
