@@ -116,6 +116,25 @@ def test_k_equals_E_and_single_expert(exm):
             check_y(got["y"], ref["y"], f"E{shape.E}k{shape.k}/path{path}")
 
 
+@pytest.mark.parametrize("shape,Ts", [
+    (LayerShape(H=128, I=128, E=256, k=64), (1, 3, 40)),      # most experts and the largest k
+    (LayerShape(H=16384, I=128, E=2, k=1), (1, 5, 20)),       # largest hidden size: staged in 8 chunks
+    (LayerShape(H=128, I=16384, E=2, k=2), (1, 5, 20)),       # largest intermediate size
+])
+def test_shape_limits(exm, shape, Ts):
+    """The largest E, k, H and I the boundary accepts, on the decode, prefill and
+    sequential paths and the automatic choice, at a ragged token count."""
+    log(f"shape limits {shape}")
+    lay = Layer(shape, seed=4)
+    for T in Ts:
+        x = lay.syn.x(T, stream=T)
+        ref = oracle_layer(lay, x)
+        for path in (0, 1, 2, 3):
+            got = run_layer(exm, lay, x, flags=path)
+            check_routing(got, ref, f"{shape} T={T} path={path}")
+            check_y(got["y"], ref["y"], f"{shape} T={T} path={path}")
+
+
 def test_zero_tokens_is_noop(exm, tiny):
     import torch
     x = torch.empty((0, TINY.H), dtype=torch.bfloat16, device="cuda")
