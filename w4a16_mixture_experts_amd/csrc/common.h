@@ -130,6 +130,7 @@ hipError_t launch_route_token(const uint16_t* x, const uint16_t* wr, const float
 // Logits, top-k, weights and the decode expert table of T <= kRouteSelMaxTok tokens in one
 // launch (arrival counters: ceil(T / 2) of them, zero before the launch and after it).
 constexpr int kRouteSelMaxTok = 16;
+constexpr int kSelRowBytes = 16;   // bytes per expert row of the routing table: one per token (T <= 16)
 constexpr int kRouteSelCounters = 8, kRouteCounterStride = 64;   // counter i at word i * stride
 hipError_t launch_route_sel(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
                             int renormalize, uint16_t* logits, int32_t* ids, float* w, uint8_t* sel,

@@ -38,7 +38,7 @@ constexpr int kDecKC = 2048;                 // reduction columns staged in LDS 
 constexpr int kDecKG = kDecKC / kGroup;      // 128-input groups per staged chunk
 constexpr int kDecXS = kDecKC + 8;           // LDS row stride (bf16): 16-byte skew per row
 constexpr int kDecRing = 4;                  // weight groups in flight per wave
-constexpr int kSelStride = 16;               // bytes per expert row of the routing table (T <= 16)
+constexpr int kSelStride = kSelRowBytes;     // bytes per expert row of the routing table (T <= 16)
 
 
 // In the routing set-up the staging area holds the ids; afterwards the staged rows, and at

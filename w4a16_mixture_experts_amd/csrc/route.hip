@@ -8,109 +8,9 @@
 #include "device.h"
 #include "group_block.h"
 #include "topk.h"
+#include "route_wave.h"
 
 namespace exmoe {
-
-// ---------------------------------------------------------------------------------
-// Logits. A lane group owns a block of TB tokens x EB experts and splits H among its
-// LANES lanes in interleaved 16-byte chunks (contiguous bytes across the group); each
-// chunk is converted to fp64 once and feeds TB*EB fp64 FMAs (bf16 products are exact in
-// fp64). Partial sums are added with DPP row rotations (and across rows with readlane
-// when LANES = 64); one lane rounds once to bf16. Few tokens: LANES = 64, small blocks,
-// many waves. Many tokens: LANES = 16, 4 x 4 blocks for operand reuse.
-// ---------------------------------------------------------------------------------
-// WT: write-through (agent-scope atomic) stores of the logits, read back by another
-// workgroup in the same launch.
-template <int TB, int EB, int LANES, int MC, bool WT>
-__device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                                                  const float* __restrict__ bias, int T, int H, int E,
-                                                  uint16_t* __restrict__ logits, int blk) {
-  const int lane = (int)lane_id();
-  const int li = lane % LANES;
-  const int nEB = (E + EB - 1) / EB;
-  const int tb = blk / nEB, eb = blk % nEB;   // (token block, expert block)
-  const int t0 = tb * TB, e0 = eb * EB;
-  double acc[TB][EB];
-#pragma unroll
-  for (int i = 0; i < TB; i++)
-#pragma unroll
-    for (int j = 0; j < EB; j++) acc[i][j] = 0.0;
-  if (t0 < T) {
-    const int chunks = H / 8;
-    // MC chunks per lane are loaded before any arithmetic: one memory latency per piece
-    for (int c0 = 0; c0 < chunks; c0 += LANES * MC) {
-      uint4 xu[TB][MC], wu[EB][MC];
-#pragma unroll
-      for (int m = 0; m < MC; m++) {
-        int c = c0 + li + LANES * m;
-        c = c < chunks ? c : chunks - 1;
-#pragma unroll
-        for (int i = 0; i < TB; i++) {
-          const int t = t0 + i < T ? t0 + i : T - 1;
-          xu[i][m] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[c];
-        }
-#pragma unroll
-        for (int j = 0; j < EB; j++) {
-          const int e = e0 + j < E ? e0 + j : E - 1;
-          wu[j][m] = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MC; m++) {
-        if (c0 + li + LANES * m < chunks) {
-          double xv[TB][8], wv[EB][8];
-#pragma unroll
-          for (int i = 0; i < TB; i++) {
-            const uint32_t q4[4] = {xu[i][m].x, xu[i][m].y, xu[i][m].z, xu[i][m].w};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              xv[i][2 * q] = (double)__uint_as_float(q4[q] << 16);
-              xv[i][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < EB; j++) {
-            const uint32_t q4[4] = {wu[j][m].x, wu[j][m].y, wu[j][m].z, wu[j][m].w};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              wv[j][2 * q] = (double)__uint_as_float(q4[q] << 16);
-              wv[j][2 * q + 1] = (double)__uint_as_float(q4[q] & 0xFFFF0000u);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < TB; i++)
-#pragma unroll
-            for (int j = 0; j < EB; j++)
-#pragma unroll
-              for (int q = 0; q < 8; q++) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TB; i++)
-#pragma unroll
-    for (int j = 0; j < EB; j++) {
-      double s = row16_sum_f64(acc[i][j]);
-      if (LANES == 64) {
-        // rows 0..3 of the wave, added in a fixed order
-        const long long b = __double_as_longlong(s);
-        const int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
-        double r[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          r[q] = __longlong_as_double(((long long)(unsigned)__builtin_amdgcn_readlane(lo, 16 * q)) |
-                                      ((long long)__builtin_amdgcn_readlane(hi, 16 * q) << 32));
-        s = ((r[0] + r[1]) + r[2]) + r[3];
-      }
-      const int t = t0 + i, e = e0 + j;
-      if (li == 0 && t < T && e < E) {
-        const double v = bias ? s + (double)bias[e] : s;
-        if (WT) __hip_atomic_store(logits + (size_t)t * E + e, f64_to_bf16(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else logits[(size_t)t * E + e] = f64_to_bf16(v);
-      }
-    }
-}
 
 template <int TB, int EB, int LANES, int MC>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x,
@@ -123,66 +23,16 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------
-// Logits, top-k and the expert table of a few tokens (T <= 16) in one launch. A
-// workgroup has one wave per token of its token block; each wave computes its token's
-// logits for one block of kRouteSelEB experts as above. The last workgroup of a token
-// block to finish (one arrival counter per token block) then selects each token's
-// experts from the bf16 logits of all workgroups, one wave per token, writes ids and
-// weights, and fills the tokens' columns of the table sel[e * 16 + t] = slot + 1 (0: not
-// selected) that the decode expert kernels read; it clears the counter last, so the
-// counters are zero between launches (and must be zero before the first one).
-// Ordering: the logits are written through to the device-coherent level (agent-scope
-// atomic stores) and the wave waits for their completion before it counts; the last
-// arriver reads them with agent-scope atomic loads after its count has returned. With
-// every shared location accessed by such atomics, no cache write-back or invalidate is
-// needed (those order plain loads and stores).
+// Logits, top-k and the expert table of a few tokens (T <= 16) in one launch: the
+// selection part (route_wave.h) with one wave per token of a 4-token block and one block
+// of 2 experts per workgroup.
 // ---------------------------------------------------------------------------------
-constexpr int kRouteSelTB = 4, kRouteSelEB = 2;
-static_assert(kRouteSelMaxTok <= kRouteSelTB * kRouteSelCounters, "one counter per token block");
 __global__ __launch_bounds__(64 * kRouteSelTB) void route_sel_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias, int T, int H,
     int E, int k, int renormalize, uint16_t* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
     uint8_t* __restrict__ sel, uint32_t* __restrict__ counters) {
-  __shared__ uint16_t s_lg[kRouteSelTB][kMaxExperts];
-  __shared__ int s_last;
-  const int lane = (int)lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int nEB = (E + kRouteSelEB - 1) / kRouteSelEB;
-  const int tb = blockIdx.x / nEB, eb = blockIdx.x % nEB;
-  const int t = tb * kRouteSelTB + wave;   // this wave's token
-  if (t < T) route_logits_wave<1, kRouteSelEB, 64, 4, true>(x, wr, bias, T, H, E, logits, t * nEB + eb);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's logits stores have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(counters + tb * kRouteCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (uint32_t)(nEB - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  if (t < T) {
-    for (int e = lane; e < E; e += 64)
-      s_lg[wave][e] = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int id;
-    float wt;
-    if (E <= 64) topk_rank_token(s_lg[wave], E, k, renormalize, id, wt);
-    else topk_token(s_lg[wave], nullptr, E, k, renormalize, id, wt);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = id;
-      w[(size_t)t * k + lane] = wt;
-    }
-    // table column t: expert e gets slot + 1 when selected, else 0 (one store per byte)
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      int v = 0;
-      for (int j = 0; j < k; j++) v = __builtin_amdgcn_readlane(id, j) == e ? j + 1 : v;
-      if (e < E) sel[(size_t)e * 16 + t] = (uint8_t)v;
-    }
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counters + tb * kRouteCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __shared__ RouteSelShared sh;
+  route_sel_part<kRouteSelTB>(x, wr, bias, T, H, E, k, renormalize, logits, ids, w, sel, counters, blockIdx.x, sh);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const uint16_t* __restrict__ logits,
