@@ -135,6 +135,27 @@ def test_shape_limits(exm, shape, Ts):
             check_y(got["y"], ref["y"], f"{shape} T={T} path={path}")
 
 
+@pytest.mark.parametrize("T", [4, 5, 13, 16])
+def test_table_routed_every_expert_repeated(exm, T):
+    """Decode sizes with the routing kernel's table and every expert launched (8-wave fused
+    kernel, 16 experts, intermediate 2048), ragged token counts: all outputs against the
+    oracle, and three calls in a row equal bit for bit (the routing kernel leaves its
+    arrival counters at zero for the next call)."""
+    log(f"table routing, every expert launched, T={T}")
+    lay = Layer(LayerShape(H=256, I=2048, E=16, k=8), seed=5)
+    x = lay.syn.x(T, stream=70 + T)
+    ref = oracle_layer(lay, x)
+    first = None
+    for rep in range(3):
+        got = run_layer(exm, lay, x)
+        check_routing(got, ref, f"T={T} call {rep}")
+        if first is None:
+            check_y(got["y"], ref["y"], f"T={T}")
+            first = got["y_bits"]
+        else:
+            assert np.array_equal(got["y_bits"], first), f"call {rep} differs"
+
+
 def test_zero_tokens_is_noop(exm, tiny):
     import torch
     x = torch.empty((0, TINY.H), dtype=torch.bfloat16, device="cuda")
