@@ -197,6 +197,16 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
  * library writes them, so one workspace may serve calls of any shape and path. Calls
  * that share a workspace must not overlap in time (same stream, or synchronized). */
 size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags);
+
+/* Conditions the expert kernels recorded in a workspace of exmoe_moe_forward,
+ * exmoe_moe_layer or exmoe_moe_forward_cached, since it was cleared. Bit 0
+ * (EXMOE_FLAG_EXPERT_WITHOUT_SLOT): a routed expert had no slot (expert_to_slot = -1),
+ * its rows were skipped and the output of the tokens routed to it is undefined. Reads the
+ * word after the work already enqueued on `stream` (host-synchronous: the stream is
+ * synchronized) into *flags_out, then clears it when clear != 0. workspace: device,
+ * ws_bytes >= 4096. */
+enum { EXMOE_FLAG_EXPERT_WITHOUT_SLOT = 1 };
+int exmoe_workspace_flags(void* workspace, size_t ws_bytes, int clear, uint32_t* flags_out, hipStream_t stream);
 int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
                     const exmoe_expert_bank* bank, int T, int H, int I, int E, int k,
                     int renormalize, int flags, exmoe_bf16* logits, int32_t* topk_ids,

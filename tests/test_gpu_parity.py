@@ -194,6 +194,25 @@ def test_slot_indirection_and_knockout(exm, tiny):
         assert np.array_equal(changed, oracle.knockout_rows(base["ids"], e))
 
 
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_expert_without_slot_is_flagged(exm, tiny, path):
+    """A routed expert mapped to slot -1 is a caller error: the kernels skip its rows and
+    record it in the workspace, which exmoe_workspace_flags reports (and clears); a call
+    with every routed expert mapped records nothing."""
+    import torch
+    x = to_dev_bf16(tiny.syn.x(16))
+    bank = exm.bank_from_blobs(tiny.blobs)
+    out = exm.moe_layer(x, tiny.wr, bank, TINY.I, TINY.k, flags=path)
+    assert exm.workspace_flags(out.workspace) == 0
+    routed = sorted(set(out.ids.cpu().numpy().ravel().tolist()))
+    table = np.arange(TINY.E, dtype=np.int32)
+    table[routed[0]] = -1
+    bank.expert_to_slot = torch.from_numpy(table).cuda()
+    exm.moe_layer(x, tiny.wr, bank, TINY.I, TINY.k, flags=path, buffers=out)
+    assert exm.workspace_flags(out.workspace) & exm.FLAG_EXPERT_WITHOUT_SLOT
+    assert exm.workspace_flags(out.workspace) == 0          # cleared by the previous read
+
+
 # ------------------------------------------------------------------ OLMoE-shaped layers
 @pytest.fixture(scope="module")
 def olmoe(exm):

@@ -192,3 +192,13 @@ def test_slot_cache_errors_and_resident():
     st = r.stats()
     assert st["resident"] == 1 and st["lookups"] == 0 and st["h2d_bytes"] == 0
     assert list(r.table(0)) == list(range(8))
+
+
+def test_workspace_flags_rejects_bad_input():
+    lib = exm._lib
+    v = ctypes.c_uint32(7)
+    assert lib.exmoe_workspace_flags(None, 4096, 1, ctypes.byref(v), None) == exm.ERR_INVALID_ARGUMENT
+    assert lib.exmoe_workspace_flags(FAKE, 4096, 1, None, None) == exm.ERR_INVALID_ARGUMENT
+    assert lib.exmoe_workspace_flags(FAKE, 4095, 1, ctypes.byref(v), None) == exm.ERR_WORKSPACE
+    assert v.value == 7
+

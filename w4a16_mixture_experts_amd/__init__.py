@@ -72,6 +72,7 @@ _SIGS = {
     "exmoe_active_experts": (_i, [_vp, _i, _vp, _vp, _vp]),
     "exmoe_moe_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "exmoe_bf16_expert_bytes": (_sz, [_i, _i]),
+    "exmoe_workspace_flags": (_i, [_vp, _sz, _i, ctypes.POINTER(ctypes.c_uint32), _vp]),
     "exmoe_bf16_pack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _sz]),
     "exmoe_moe_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _sz, _vp]),
@@ -278,6 +279,17 @@ def alloc_workspace(nbytes: int, device="cuda"):
     in its first 4096 bytes."""
     torch = _torch()
     return torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+
+
+FLAG_EXPERT_WITHOUT_SLOT = 1
+
+
+def workspace_flags(workspace, clear: bool = True) -> int:
+    """Conditions the expert kernels recorded in a workspace (bit 0: a routed expert had no
+    slot); synchronizes the current stream."""
+    v = ctypes.c_uint32(0)
+    _check(_lib.exmoe_workspace_flags(_ptr(workspace), workspace.numel(), int(clear), ctypes.byref(v), _stream()))
+    return v.value
 
 
 def moe_forward(x, ids, weights, offsets, sorted_flat, flat_to_sorted, bank: ExpertBank, I: int,

@@ -611,6 +611,23 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   return EXMOE_OK;
 }
 
+int exmoe_workspace_flags(void* workspace, size_t ws_bytes, int clear, uint32_t* flags_out, hipStream_t stream) {
+  if (!workspace || !flags_out) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace and flags_out must not be NULL");
+  if (ws_bytes < kWsHeaderBytes)
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes has no %zu-byte header", ws_bytes, kWsHeaderBytes);
+  uint8_t* word = static_cast<uint8_t*>(workspace) + kWsDebugOffset;
+  uint32_t v = 0;
+  EXMOE_HIP(hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, stream));
+  EXMOE_HIP(hipStreamSynchronize(stream));
+  *flags_out = v;
+  if (clear && v) {
+    const uint32_t zero = 0;
+    EXMOE_HIP(hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, stream));
+    EXMOE_HIP(hipStreamSynchronize(stream));
+  }
+  return EXMOE_OK;
+}
+
 size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags) {
   return exmoe_moe_workspace_bytes(T, H, I, E, k, flags);
 }
