@@ -210,10 +210,14 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   return hipGetLastError();
 }
 
+// One workgroup for both steps saves a launch for a few tokens; its four waves take the
+// tokens one after another, so from kTopkGroupMaxTok tokens on the top-k runs one token
+// per wave over the whole chip and the grouping in a launch of its own.
+constexpr int kTopkGroupMaxTok = 16;
 hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int renormalize, int32_t* ids,
                              float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
                              hipStream_t s) {
-  if (T * k > kTopkGroupMaxRows) {
+  if (T * k > kTopkGroupMaxRows || T > kTopkGroupMaxTok) {
     hipError_t e = launch_topk(logits, nullptr, T, E, k, renormalize, ids, w, s);
     if (e != hipSuccess) return e;
     return launch_group(ids, T, k, E, offsets, sorted_flat, flat_to_sorted, s);
