@@ -390,9 +390,10 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   };
   const size_t o_h = take(rows * I * 2);
   const size_t o_yp = take(rows * H * 4);
-  // correction seeds of the prefill kernels: [group][sorted row], rows padded by one tile
+  // correction seeds of the prefill kernels: gate/up [group][token], down [group][sorted
+  // row] with the rows padded by one tile
   const size_t o_gs = take((rows + 128) * (I / kGroup) * 4);
-  const size_t o_xs = take((rows + 128) * (H / kGroup) * 4);
+  const size_t o_xs = take((size_t)T * (H / kGroup) * 4);
   // fused decode: down-projection partial outputs per 128-wide slice of I
   const int fused_waves = path == EXMOE_PATH_DECODE ? decode_fused_waves(T, H, I, E, k) : 0;
   const int nparts = fused_waves ? I / (kTileRows * fused_waves) : 0;

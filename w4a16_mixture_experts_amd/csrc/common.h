@@ -105,7 +105,7 @@ struct MoeArgs {
   int nparts;         // slices in part (0: the combine reads y_perm)
   float* y_perm;      // fp32 [T*k, H], sorted-row order, already multiplied by the routing weight
   float* gsum;        // fp32 [I/128][T*k + 128]: -136 * group sums of h per sorted row (down seeds)
-  float* xsum;        // fp32 [H/128][T*k + 128]: -136 * group sums of x per sorted row (gate/up seeds)
+  float* xsum;        // fp32 [H/128][T]: -136 * group sums of x per token (gate/up seeds)
   uint8_t* sel;       // u8 [E][16]: decode expert table, sel[e][t] = slot + 1 of token t (0: not routed)
   uint32_t* counters; // arrival counters of the routing kernel (zero between launches)
   uint32_t* debug;    // debug word(s)

@@ -133,8 +133,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   const int K = GATEUP ? a.H : a.I;
   const int G = K / kGroup;
   const size_t tile_down0 = 2 * (size_t)(a.I / kTileRows) * (a.H / kGroup);
-  const int rows_pad = a.T * a.k + kPfBN;          // row count of the seed arrays
-  const float* seeds = GATEUP ? a.xsum : a.gsum;   // [group][sorted row], already * -136
+  const int rows_pad = a.T * a.k + kPfBN;          // row count of the down kernel's seed array
 
   // tile index (without the group) of this wave's NA row subtiles; gate/up subtiles come
   // in (gate, up) pairs of one 16-row block of the intermediate dimension
@@ -172,12 +171,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     }
     drow[i] = src + (((lane & 15) ^ (r & 15)) * 8);
   }
-  const float* seed_src = seeds + pt.seg0 + pt.tok0 + (wave & 1) * 64 + lane;   // padded rows exist
+  // correction seeds, already * -136: gate/up per token (xsum[group][token]), each lane
+  // gathering its row's token (rows past the segment take token 0: their outputs are not
+  // stored); down per sorted row (gsum[group][row], rows padded by one tile)
+  const float* seed_src;
+  size_t seed_stride;
+  if (GATEUP) {
+    const int r = pt.tok0 + (wave & 1) * 64 + lane;
+    seed_src = a.xsum + (r < pt.cnt ? a.sorted_flat[pt.seg0 + r] / a.k : 0);
+    seed_stride = (size_t)a.T;
+  } else {
+    seed_src = a.gsum + pt.seg0 + pt.tok0 + (wave & 1) * 64 + lane;
+    seed_stride = (size_t)rows_pad;
+  }
 #define EXMOE_STAGE(g_, ACT, SEED)                                                                      \
   do {                                                                                                  \
     _Pragma("unroll") for (int i = 0; i < kDmaPerWave; i++)                                             \
         dma16(drow[i] + (g_) * kGroup, &ACT[(wave * kDmaPerWave + i) * 4 * kLdsStride]);                \
-    if (Q4 && wave < 2) dma4(seed_src + (size_t)(g_) * rows_pad, &SEED[wave * 64]);                     \
+    if (Q4 && wave < 2) dma4(seed_src + (size_t)(g_) * seed_stride, &SEED[wave * 64]);                  \
   } while (0)
 
   f32x4 acc[NA][8];
@@ -359,37 +370,30 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   span_end(a.span);
 }
 
-// Correction seeds of the gate/up kernel: xsum[g][r] = -136 * (sum over group g of the
-// activations of sorted row r's token), fp32, one thread per (row, group); rows past T*k
-// (padding read by partial tiles) are zero.
-__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x,
-                                                   const int32_t* __restrict__ sorted_flat, int TK,
-                                                   int k, int H, int rows_pad, float* __restrict__ xsum) {
+// Correction seeds of the gate/up kernel: xsum[g][t] = -136 * (sum over group g of the
+// activations of token t), fp32, one thread per (token, group).
+__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                   float* __restrict__ xsum) {
   const int G = H / kGroup;
-  const int i = blockIdx.x * 256 + threadIdx.x;     // one (group, row) per thread
-  if (i >= G * rows_pad) return;
-  const int g = i / rows_pad, r = i % rows_pad;
+  const int i = blockIdx.x * 256 + threadIdx.x;     // one (group, token) per thread
+  if (i >= G * T) return;
+  const int g = i / T, t = i % T;
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + g * kGroup);
   float s = 0.f;
-  if (r < TK) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)(sorted_flat[r] / k) * H + g * kGroup);
 #pragma unroll 4
-    for (int c = 0; c < kGroup / 8; c++) {
-      const uint4 v = p[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int c = 0; c < kGroup / 8; c++) {
+    const uint4 v = p[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; q++) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
-    }
+    for (int q = 0; q < 4; q++) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
   }
   xsum[i] = -136.0f * s;
 }
 
 hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s) {
-  const int TK = a.T * a.k;
   const int G = a.H / kGroup;
-  const int rows_pad = TK + kPfBN;
   ProfScope prof("xsum", s);
-  EXMOE_LAUNCH(prof, xsum_kernel, dim3((G * rows_pad + 255) / 256), dim3(256), 0, s, a.x, a.sorted_flat, TK, a.k,
-               a.H, rows_pad, a.xsum);
+  EXMOE_LAUNCH(prof, xsum_kernel, dim3((G * a.T + 255) / 256), dim3(256), 0, s, a.x, a.T, a.H, a.xsum);
   return hipGetLastError();
 }
 
