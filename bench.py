@@ -664,7 +664,7 @@ def main():
         ms = time_layer(exm, torch, wl, steps, warmup, use_graph, spans=spans)
         flops = 6.0 * T * shape.k * shape.H * shape.I
         kt = kernel_times(exm, torch, wl, min(steps, 8), ["prefill_gateup", "prefill_down", "xsum", "combine",
-                                                          "route_logits", "topk", "group", "topk_group",
+                                                          "route_logits", "topk", "group", "group_scan", "group_scatter", "topk_group",
                                                           "decode_gateup", "decode_down"])
         rec = {"T": T, "tokens_per_s": T / (ms * 1e-3), "ms_per_layer": ms, "layer_tflops": flops / (ms * 1e-3) / 1e12,
                "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,

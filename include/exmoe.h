@@ -135,7 +135,10 @@ int exmoe_route_weights(const exmoe_bf16* logits, const int32_t* topk_ids, int T
  * expert ascending and within an expert in ascending f, every f routed there;
  * flat_to_sorted int32 [T*k] is its inverse. Ids outside [0, E) are a caller error: they
  * are counted nowhere and the outputs are then unspecified (no memory is touched out of
- * range). The workspace may be NULL when exmoe_group_workspace_bytes returns 0.
+ * range). The workspace may be NULL when exmoe_group_workspace_bytes returns 0; it is
+ * (T*k + 1023) / 1024 * E * 4 bytes of device scratch (4-byte aligned) above 4096 routed
+ * rows, where the grouping runs in chunks over several workgroups; its contents need no
+ * initialization and are not kept.
  * ---------------------------------------------------------------------------------- */
 size_t exmoe_group_workspace_bytes(int T, int k, int E);
 int exmoe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,

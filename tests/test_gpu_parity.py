@@ -213,6 +213,25 @@ def test_expert_without_slot_is_flagged(exm, tiny, path):
     assert exm.workspace_flags(out.workspace) == 0          # cleared by the previous read
 
 
+@pytest.mark.parametrize("T,k,E", [(4096, 1, 8), (4097, 1, 64), (2049, 8, 64), (300, 64, 256), (5000, 2, 3)])
+def test_grouping_many_rows_chunked(exm, T, k, E):
+    """The grouping of more than 4096 routed rows (chunk counts, one scan, chunk scatters)
+    against the oracle, bit for bit, including a ragged last chunk and empty experts."""
+    import torch
+    rng = np.random.default_rng(T + E)
+    if E >= k:
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[:, 0] = np.where(rng.random(T) < 0.5, 0, ids[:, 0]) if k == 1 else ids[:, 0]   # skew toward expert 0
+    off, sf, fs = exm.group_tokens(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    r_off, r_sf, r_fs = oracle.group_tokens(ids, E)
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(sf.cpu().numpy(), r_sf)
+    assert np.array_equal(fs.cpu().numpy(), r_fs)
+
+
 # ------------------------------------------------------------------ OLMoE-shaped layers
 @pytest.fixture(scope="module")
 def olmoe(exm):

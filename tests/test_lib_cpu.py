@@ -202,3 +202,12 @@ def test_workspace_flags_rejects_bad_input():
     assert lib.exmoe_workspace_flags(FAKE, 4095, 1, ctypes.byref(v), None) == exm.ERR_WORKSPACE
     assert v.value == 7
 
+
+def test_group_workspace_size_and_check():
+    assert exm._lib.exmoe_group_workspace_bytes(512, 8, 64) == 0                    # 4096 rows: one workgroup
+    assert exm._lib.exmoe_group_workspace_bytes(513, 8, 64) == 5 * 64 * 4           # 4104 rows: 5 chunks
+    assert exm._lib.exmoe_group_workspace_bytes(2048, 8, 64) == 16 * 64 * 4
+    lib = exm._lib
+    assert lib.exmoe_group_tokens(FAKE, 513, 8, 64, FAKE, FAKE, FAKE, None, 0, None) == exm.ERR_WORKSPACE
+    assert lib.exmoe_group_tokens(FAKE, 513, 8, 64, FAKE, FAKE, FAKE, FAKE, 5 * 64 * 4 - 1, None) == exm.ERR_WORKSPACE
+

@@ -230,8 +230,10 @@ def group_tokens(ids, E: int, offsets=None, sorted_flat=None, flat_to_sorted=Non
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     sorted_flat = torch.empty(T * k, dtype=torch.int32, device=dev) if sorted_flat is None else sorted_flat
     flat_to_sorted = torch.empty(T * k, dtype=torch.int32, device=dev) if flat_to_sorted is None else flat_to_sorted
-    _check(_lib.exmoe_group_tokens(_ptr(ids), T, k, E, _ptr(offsets), _ptr(sorted_flat), _ptr(flat_to_sorted), None, 0,
-                                   _stream()))
+    nws = _lib.exmoe_group_workspace_bytes(T, k, E)
+    ws = torch.empty(max(nws, 4), dtype=torch.uint8, device=dev) if nws else None
+    _check(_lib.exmoe_group_tokens(_ptr(ids), T, k, E, _ptr(offsets), _ptr(sorted_flat), _ptr(flat_to_sorted),
+                                   _ptr(ws) if ws is not None else None, nws, _stream()))
     return offsets, sorted_flat, flat_to_sorted
 
 

@@ -321,13 +321,12 @@ int exmoe_route_weights(const exmoe_bf16* logits, const int32_t* topk_ids, int T
 }
 
 size_t exmoe_group_workspace_bytes(int T, int k, int E) {
-  (void)T; (void)k; (void)E;
-  return 0;
+  if (check_shape(T, kGroup, kGroup, E, k)) return 0;
+  return group_workspace_bytes(T * k, E);
 }
 
 int exmoe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets, int32_t* sorted_flat,
                        int32_t* flat_to_sorted, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  (void)workspace; (void)ws_bytes;
   int st = check_shape(T, kGroup, kGroup, E, k);
   if (st) return st;
   CHECK_PTR4(expert_offsets);
@@ -336,7 +335,12 @@ int exmoe_group_tokens(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
     CHECK_PTR4(sorted_flat);
     CHECK_PTR4(flat_to_sorted);
   }
-  EXMOE_HIP(launch_group(topk_ids, T, k, E, expert_offsets, sorted_flat, flat_to_sorted, stream));
+  const size_t need = group_workspace_bytes(T * k, E);
+  if (need && (!workspace || ws_bytes < need))
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (need && ((uintptr_t)workspace & 3u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 4-byte aligned");
+  EXMOE_HIP(launch_group(topk_ids, T, k, E, expert_offsets, sorted_flat, flat_to_sorted,
+                         static_cast<int32_t*>(need ? workspace : nullptr), stream));
   return EXMOE_OK;
 }
 
@@ -400,10 +404,12 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
   const size_t o_pt = take((size_t)nparts * rows * H * 4);
   const size_t o_sel = take((size_t)E * 16);
   const size_t o_wt = take((size_t)E * 4);
+  const size_t o_gw = take(group_workspace_bytes((int)rows, E));
   if (a && ws) {
     uint8_t* b = static_cast<uint8_t*>(ws);
     a->sel = b + o_sel;
     a->wave_table = reinterpret_cast<int32_t*>(b + o_wt);
+    a->group_ws = reinterpret_cast<int32_t*>(b + o_gw);
     a->h = reinterpret_cast<uint16_t*>(b + o_h);
     a->y_perm = reinterpret_cast<float*>(b + o_yp);
     a->gsum = reinterpret_cast<float*>(b + o_gs);
@@ -678,9 +684,11 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     }
     return EXMOE_OK;
   }
+  MoeArgs ag{};
+  moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), &ag, workspace);
   EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
   EXMOE_HIP(launch_topk_group(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
-                              flat_to_sorted, stream));
+                              flat_to_sorted, ag.group_ws, stream));
   return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
                           k, flags, y, workspace, ws_bytes, stream);
 }

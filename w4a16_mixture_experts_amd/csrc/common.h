@@ -81,11 +81,13 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
                                int E, uint16_t* logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
                        int renormalize, int32_t* ids, float* w, hipStream_t s);
+// group_ws: group_workspace_bytes(T * k, E) bytes (may be null when that is 0)
 hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int renormalize, int32_t* ids,
                              float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
-                             hipStream_t s);
+                             int32_t* group_ws, hipStream_t s);
+size_t group_workspace_bytes(int n, int E);
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_flat,
-                        int32_t* flat_to_sorted, hipStream_t s);
+                        int32_t* flat_to_sorted, int32_t* group_ws, hipStream_t s);
 
 struct MoeArgs {
   const uint16_t* x;
@@ -112,6 +114,7 @@ struct MoeArgs {
   unsigned long long* span;   // launch span slot (benchmark timing) or null
   int skip_absent;    // experts without a slot are skipped silently (one wave of a cached forward)
   int32_t* wave_table;  // int32 [E] workspace: the expert->slot table of one wave
+  int32_t* group_ws;    // chunk counts of the grouping of more than 4096 rows
 };
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);

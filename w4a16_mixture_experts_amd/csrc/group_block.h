@@ -13,6 +13,7 @@ namespace exmoe {
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kTopkGroupMaxRows = 4096;
+constexpr int kGroupSingleMaxRows = 4096;   // more rows: the chunked three-launch grouping
 
 template <int THREADS>
 struct GroupSharedT {

@@ -217,11 +217,11 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
 constexpr int kTopkGroupMaxTok = 16;
 hipError_t launch_topk_group(const uint16_t* logits, int T, int E, int k, int renormalize, int32_t* ids,
                              float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
-                             hipStream_t s) {
+                             int32_t* group_ws, hipStream_t s) {
   if (T * k > kTopkGroupMaxRows || T > kTopkGroupMaxTok) {
     hipError_t e = launch_topk(logits, nullptr, T, E, k, renormalize, ids, w, s);
     if (e != hipSuccess) return e;
-    return launch_group(ids, T, k, E, offsets, sorted_flat, flat_to_sorted, s);
+    return launch_group(ids, T, k, E, offsets, sorted_flat, flat_to_sorted, group_ws, s);
   }
   ProfScope prof("topk_group", s);
   EXMOE_LAUNCH(prof, topk_group_kernel, dim3(1), dim3(kTopkGroupThreads), 0, s, logits, T, E, k, renormalize, ids, w,
