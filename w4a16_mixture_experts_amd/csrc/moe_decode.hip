@@ -935,9 +935,20 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
   for (int i = threadIdx.x; i < (t1 - t0) * 16; i += blockDim.x) {
     const int t = t0 + i / 16, c = row0 + (i % 16) * 4;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; j++) {
-      const float4 v = *reinterpret_cast<const float4*>(a.y_perm + ((size_t)t * a.k + j) * a.H + c);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    const float* src = a.y_perm + (size_t)t * a.k * a.H + c;
+    // eight slots in flight at a time, added in slot order
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int j = j0 + u < a.k ? j0 + u : a.k - 1;
+        v[u] = *reinterpret_cast<const float4*>(src + (size_t)j * a.H);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        if (j0 + u < a.k) {
+          s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+        }
     }
     uint2 pk;
     pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
