@@ -363,14 +363,18 @@ int exmoe_active_experts(const int32_t* expert_offsets, int E, int32_t* ids_host
 // ------------------------------------------------------------------------------------
 // Expert layer
 // ------------------------------------------------------------------------------------
-static int choose_path(int T, int E, int k, int flags) {
+static int choose_path(int T, int H, int I, int E, int k, int flags) {
   const int p = flags & EXMOE_PATH_MASK;
   if (p != EXMOE_PATH_AUTO) return p;
   const long long rows = (long long)T * k;
   const long long act = std::min<long long>(E, rows);
-  // Measured crossover on the OLMoE shape: the grouped GEMM wins from about 16 routed
-  // rows per active expert on.
-  if (T <= 16 || rows < 16 * act) return EXMOE_PATH_DECODE;
+  if (T <= 16) return EXMOE_PATH_DECODE;
+  // Routed rows per possibly-active expert at which the grouped GEMM catches up, measured
+  // on the OLMoE shape: about 40 with the pass-parallel fused decode kernel (uniform
+  // routing; about 65 under Zipf skew), about 16 for the two-kernel decode path and for
+  // the bf16 comparator's decode kernels (one workgroup walks its expert's passes).
+  const bool fused = !(flags & EXMOE_WEIGHTS_BF16) && decode_fused_waves(T, H, I, E, k) != 0;
+  if (rows <= (fused ? 40 : 16) * act) return EXMOE_PATH_DECODE;
   return EXMOE_PATH_PREFILL;
 }
 
@@ -425,7 +429,7 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
 
 extern "C" size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, int flags) {
   if (check_shape(T, H, I, E, k)) return 0;
-  return moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+  return moe_workspace_layout(T, H, I, E, k, choose_path(T, H, I, E, k, flags), nullptr, nullptr);
 }
 
 static int check_flags(int flags) {
@@ -454,7 +458,7 @@ static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const 
                             const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
                             const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int flags, exmoe_bf16* y,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-  const int path = choose_path(T, E, k, flags);
+  const int path = choose_path(T, H, I, E, k, flags);
   MoeArgs a{};
   a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
   a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
@@ -504,7 +508,7 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
   CHECK_PTR4(expert_offsets);
   CHECK_PTR4(sorted_flat);
   CHECK_PTR4(flat_to_sorted);
-  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, H, I, E, k, flags), nullptr, nullptr);
   if (!workspace || ws_bytes < need)
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
@@ -535,7 +539,7 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
     if (e < 0 || e >= E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
   std::sort(A.begin(), A.end());
   A.erase(std::unique(A.begin(), A.end()), A.end());
-  const int path = choose_path(T, E, k, flags);
+  const int path = choose_path(T, H, I, E, k, flags);
   if (path == EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_UNSUPPORTED, "the sequential path does not run in waves");
   if (T == 0) return EXMOE_OK;
   CHECK_PTR(x);
@@ -659,11 +663,11 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
   CHECK_PTR4(sorted_flat);
   CHECK_PTR4(flat_to_sorted);
   if (logit_bias && ((uintptr_t)logit_bias & 3u)) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "logit_bias must be 4-byte aligned");
-  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), nullptr, nullptr);
+  const size_t need = moe_workspace_layout(T, H, I, E, k, choose_path(T, H, I, E, k, flags), nullptr, nullptr);
   if (!workspace || ws_bytes < need)
     return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (((uintptr_t)workspace) & 255u) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (!(flags & EXMOE_WEIGHTS_BF16) && choose_path(T, E, k, flags) == EXMOE_PATH_DECODE &&
+  if (!(flags & EXMOE_WEIGHTS_BF16) && choose_path(T, H, I, E, k, flags) == EXMOE_PATH_DECODE &&
       (long long)T * k <= kDecMaxRows) {
     // Decode sizes: the expert kernel groups the rows itself and publishes the grouping;
     // for a few tokens it also makes the top-k selection from the logits, otherwise one
@@ -685,7 +689,7 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     return EXMOE_OK;
   }
   MoeArgs ag{};
-  moe_workspace_layout(T, H, I, E, k, choose_path(T, E, k, flags), &ag, workspace);
+  moe_workspace_layout(T, H, I, E, k, choose_path(T, H, I, E, k, flags), &ag, workspace);
   EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
   EXMOE_HIP(launch_topk_group(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
                               flat_to_sorted, ag.group_ws, stream));

@@ -54,10 +54,12 @@ struct DecLDS {
   int32_t pf[kDecTok];                       // flat indices of the current pass (-1: padding)
   int32_t srows[kDecTok];                    // this expert's flat indices (table routing)
   int32_t n_act;
+  int32_t pp_idx, pp_pass;                   // pass-parallel launch: active-expert index and pass
 };
 
 struct DecExpert {
   int e, seg0, cnt;
+  int row0;   // first of the expert's rows this workgroup takes (pass-parallel launches)
   const uint4* tiles;
   const uint16_t* scales;
 };
@@ -140,9 +142,12 @@ __device__ void dec_publish(const MoeArgs& a, DecLDS& L, const DecPublish& pub) 
   group_block<NT>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
 }
 
+// pp (pass-parallel, not ALL): aidx counts 16-row passes over the active experts in
+// ascending order instead of the experts themselves, so that a hot expert's passes run in
+// workgroups of their own; ex.row0 / ex.cnt are then this pass's rows.
 template <int SRC, bool ALL, int NT>
 __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, const DecPre& pr, int fixed_expert,
-                          int aidx, bool first_of_expert, int slot_known, DecExpert& ex) {
+                          int aidx, bool first_of_expert, int slot_known, DecExpert& ex, bool pp = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int TK = a.T * a.k;
   int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);            // staging rows are free (ids mode)
@@ -211,11 +216,38 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
     }
   }
   __syncthreads();
-  if (!ALL && aidx >= L.n_act) return false;
+  if (!ALL && pp) {
+    if (wave == 0) {
+      if (lane == 0) L.pp_idx = -1;   // past the last pass: nothing to do
+      int base = 0;
+      for (int i0 = 0; i0 < L.n_act; i0 += 64) {
+        const int i = i0 + lane;
+        const int e = i < L.n_act ? L.act[i] : 0;
+        const int np = i < L.n_act ? (L.off[e + 1] - L.off[e] + kDecTok - 1) / kDecTok : 0;
+        int incl = np;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(incl, d);
+          if (lane >= d) incl += u;
+        }
+        const int excl = base + incl - np;
+        if (np > 0 && aidx >= excl && aidx < excl + np) {
+          L.pp_idx = i;
+          L.pp_pass = aidx - excl;
+        }
+        base += __shfl(incl, 63);
+      }
+    }
+    __syncthreads();
+  }
+  const int ai = !ALL && pp ? L.pp_idx : aidx;
+  const int pass = !ALL && pp ? L.pp_pass : 0;
+  if (!ALL && (ai < 0 || ai >= L.n_act)) return false;
   // uniform values: keep them (and the addresses built from them) in scalar registers
-  ex.e = ALL ? aidx : __builtin_amdgcn_readfirstlane(L.act[aidx]);
+  ex.e = ALL ? aidx : __builtin_amdgcn_readfirstlane(L.act[ai]);
   ex.seg0 = __builtin_amdgcn_readfirstlane(L.off[ex.e]);
   ex.cnt = __builtin_amdgcn_readfirstlane(L.off[ex.e + 1]) - ex.seg0;
+  ex.row0 = 0;
   if (SRC == kSrcSel) {
     // the tokens that selected this expert, ascending (the table gives each one's slot)
     if (wave == 0) {
@@ -237,7 +269,7 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
       }
     }
     __syncthreads();
-    if (first_of_expert) {
+    if (first_of_expert && pass == 0) {
       for (int r = tid; r < ex.cnt; r += NT) {
         const int f = L.rows[r];
         pub.sorted_flat[ex.seg0 + r] = f;
@@ -248,6 +280,10 @@ __device__ bool dec_setup(const MoeArgs& a, DecLDS& L, const DecPublish& pub, co
       for (int i = tid; i <= a.E; i += NT) pub.offsets[i] = L.off[i];
   }
   if (ex.cnt <= 0) return false;
+  if (pass > 0 || pp) {   // this pass's rows only
+    ex.row0 = __builtin_amdgcn_readfirstlane(pass * kDecTok);
+    ex.cnt = ex.cnt - ex.row0 < kDecTok ? ex.cnt - ex.row0 : kDecTok;
+  }
   const int slot = ALL ? slot_known : a.e2s ? __builtin_amdgcn_readfirstlane(a.e2s[ex.e]) : ex.e;
   if (slot < 0) {
     if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
@@ -517,7 +553,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
 // wide, which halves the partial outputs the combine reads.
 // ------------------------------------------------------------------------------------
 template <int SRC, bool ALL, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPublish pub, int fixed_expert) {
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPublish pub, int fixed_expert, int pp) {
   static_assert(NW == 8 || NW == 16, "8 or 16 waves");
   constexpr int NT = 64 * NW, RS = kTileRows * NW, NCG = NW / 8;
   __shared__ DecLDS L;
@@ -626,6 +662,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     if (wave == 0 && sb > 0) L.srows[__popcll(m & ((1ull << lane) - 1ull))] = lane * a.k + sb - 1;
     ex.e = aidx;
     ex.seg0 = 0;
+    ex.row0 = 0;
     ex.cnt = __popcll(m);
     __syncthreads();   // token list and activation rows visible
     if (ex.cnt == 0) return;
@@ -635,7 +672,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
-  } else if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex)) {
+  } else if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex, pp != 0)) {
     return;
   }
   if (!ALL) {
@@ -650,7 +687,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     const int nrow = ex.cnt - p * kDecTok < kDecTok ? ex.cnt - p * kDecTok : kDecTok;
     if (tid < kDecTok) {
       const int r = p * kDecTok + tid;
-      L.pf[tid] = r < ex.cnt ? (SRC == kSrcSel ? L.srows[r] : SRC == kSrcIds ? L.rows[r] : a.sorted_flat[ex.seg0 + r])
+      L.pf[tid] = r < ex.cnt ? (SRC == kSrcSel ? L.srows[r] : SRC == kSrcIds ? L.rows[ex.row0 + r]
+                                                                          : a.sorted_flat[ex.seg0 + ex.row0 + r])
                              : -1;
     }
     auto next_issue = [&](int sn, WSlot2& w) {
@@ -1047,13 +1085,25 @@ static void launch_expert(ProfScope& prof, const MoeArgs& a, const DecPublish& p
     EXMOE_LAUNCH(prof, (decode_expert_kernel<GATEUP, SRC, 4, false>), grid, block, 0, s, as, pub, fixed_expert, nchunk);
 }
 
-int decode_fused_waves(int T, int H, int I, int E, int k) {
+// Workgroups per slice of I of a fused launch: every expert (T <= 16 and most experts
+// active), one per active expert (T <= 16), or one per 16-row pass of an active expert
+// (more tokens: at most T k / 16 + min(E, T k) passes).
+static long long fused_units(int T, int E, int k) {
   const long long tk = (long long)T * k;
   const long long ny = E < tk ? E : tk;
-  // most experts active and one 16-wave workgroup per compute unit or more: 16 waves
-  if (tk >= 2LL * E && I % (2 * kGroup) == 0 && I / (2 * kGroup) <= 8 && (long long)E * (I / (2 * kGroup)) >= 256)
+  if (T > kDecTok) return (tk + kDecTok - 1) / kDecTok + ny;
+  return tk >= 2LL * E ? E : ny;
+}
+
+int decode_fused_waves(int T, int H, int I, int E, int k) {
+  const long long tk = (long long)T * k;
+  const long long units = fused_units(T, E, k);
+  // most experts active (or many passes) and one 16-wave workgroup per compute unit or
+  // more: 16 waves
+  if ((tk >= 2LL * E || T > kDecTok) && I % (2 * kGroup) == 0 && I / (2 * kGroup) <= 8 &&
+      units * (I / (2 * kGroup)) >= 256)
     return 16;
-  if (I / kGroup <= 16 && ny * (I / kGroup) >= 256) return 8;
+  if (I / kGroup <= 16 && units * (I / kGroup) >= 256) return 8;
   // a few routed rows: the narrow kernel (32-row slices; reported as 2 waves' worth of rows)
   if (T <= kDecTok && H <= kDecKC && tk < 2LL * E) return kNarRows / kTileRows;
   return 0;
@@ -1063,7 +1113,9 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
                                         hipStream_t s) {
   if (a.nparts > 0 && fixed_expert < 0) {
     ProfScope prof("decode_fused", s);
-    const bool all = (long long)a.T * a.k >= 2LL * a.E;
+    const bool pp = a.T > kDecTok && !(pub && pub->sel);   // pass-parallel: one workgroup per 16-row pass
+    const bool all = !pp && (long long)a.T * a.k >= 2LL * a.E;
+    const int units = (int)fused_units(a.T, a.E, a.k);
     const int nw = a.I / (kTileRows * a.nparts);   // the workspace layout chose the width
     const int extra = pub && pub->sel ? 1 : 0;     // the publisher workgroup
     const DecPublish none{};
@@ -1071,15 +1123,15 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
     as.span = prof.span();
 #define EXMOE_FUSED(SRC, P)                                                                                      \
   do {                                                                                                          \
-    const dim3 grid((all ? a.E : ny) * a.nparts + extra);                                                       \
+    const dim3 grid((pp ? units : all ? a.E : ny) * a.nparts + extra);                                          \
     if (nw == kNarRows / kTileRows) {                                                                           \
       EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * a.nparts + extra), dim3(1024), 0, s, as, P);       \
     } else if (nw == 16) {                                                                                      \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert); \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert);    \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, 0); \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, pp); \
     } else {                                                                                                    \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert);   \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, as, P, fixed_expert);      \
+      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, 0);  \
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, pp); \
     }                                                                                                           \
   } while (0)
     if (!pub) EXMOE_FUSED(kSrcGiven, none);
