@@ -232,6 +232,26 @@ def test_grouping_many_rows_chunked(exm, T, k, E):
     assert np.array_equal(fs.cpu().numpy(), r_fs)
 
 
+@pytest.mark.parametrize("T", [40, 128, 300])
+def test_pass_parallel_decode_hot_experts(exm, T):
+    """More than 16 tokens with every token on the same k experts (a +30 logit bias on
+    them): the pass-parallel decode kernel gives each expert T / 16 passes of its own
+    workgroups. T k <= 1024 groups in the kernel (ids), above that the grouping comes in
+    (offsets and permutation); against the oracle, with the automatic path as well."""
+    log(f"hot experts, T={T}")
+    shape = LayerShape(H=256, I=1024, E=32, k=4)
+    lay = Layer(shape, seed=8)
+    bias = np.zeros(shape.E, np.float32)
+    bias[[3, 11, 20, 29]] = 30.0
+    x = lay.syn.x(T, stream=T)
+    ref = oracle_layer(lay, x, bias=bias)
+    assert set(np.unique(ref["ids"])) == {3, 11, 20, 29}
+    for path in (0, 1):
+        got = run_layer(exm, lay, x, bias=bias, flags=path)
+        check_routing(got, ref, f"T={T} path={path}")
+        check_y(got["y"], ref["y"], f"T={T} path={path}")
+
+
 # ------------------------------------------------------------------ OLMoE-shaped layers
 @pytest.fixture(scope="module")
 def olmoe(exm):
