@@ -1,22 +1,24 @@
 // Prefill-sized expert layer (many tokens per expert): grouped GEMMs on bf16 MFMA, gfx950.
 //
 // Every selected expert runs over the tokens grouped to it (ExactMoE abstract; Fig. 1).
-// One workgroup (4 waves, one per SIMD, up to 512 registers each) computes a 256-row x
-// 128-token output tile of one expert; each wave owns 64 rows x all 128 tokens:
+// One workgroup (8 waves, two per SIMD) computes a 256-row x 128-token output tile of one
+// expert; each wave owns 32 rows (two 16-row subtiles) x all 128 tokens:
 //   gate/up: rows = 128 gate rows + the matching 128 up rows (one 128-wide slice of the
 //            intermediate dimension), epilogue h = bf16(silu(g) * u) plus the fp32 sum of
-//            each token's 128 rounded h values (the next kernel's dequant correction);
+//            each token's 128 rounded h values (the down kernel's dequant correction);
 //   down:    rows = 256 output rows, epilogue y_perm = o * routing weight (fp32), stored in
 //            flat (token, slot) order for the combine.
-// The activation tile of each 128-input group is gathered (gate/up: through the token
-// permutation) into LDS, double-buffered, rows padded to 272 B so that the 16 tokens of a
-// fragment read hit distinct banks. Packed int4 tiles go straight from HBM to registers
-// (one 1 KiB tile per wave-wide 128-bit load, prefetched a group ahead) and are turned
-// into exact bf16 operands 128 + u in registers. Each group's MFMA chain starts from
-// -136 * (group sum of the activations), so it ends at sum(x * q); the bf16 scale of the
-// row is applied once per group in fp32. A wave dequantizes its 4 row fragments of a group
-// once and reuses each across the 8 token subtiles (16 tokens each), which keeps the
-// VALU work per MFMA near 1 + 8/8.
+// The activation tile of each 128-input group goes straight from memory into LDS
+// (global_load_lds, gate/up gathered through the token permutation), double-buffered; the
+// 16-byte chunks of row r sit at position chunk ^ (r mod 16), so the 16 rows of a fragment
+// read hit distinct banks. Packed int4 tiles go from HBM to registers (one 1 KiB tile per
+// wave-wide 128-bit load, prefetched a group ahead) and become exact bf16 operands 128 + u
+// in registers. Each group's MFMA chain starts from -136 * (group sum of the activations:
+// per token for gate/up, per routed row of h for down), so it ends at sum(x * q); the bf16
+// scale of the row is applied once per group in fp32. A wave dequantizes its 2 row
+// subtiles of a group once and reuses them across the 8 token subtiles (16 tokens each).
+// Q4 = false runs the same tiling on dense bf16 experts (the comparator): the weight
+// fragments are loaded as they are, with no scales and no seeds.
 #include "common.h"
 #include "device.h"
 
