@@ -16,9 +16,12 @@
 //
 // decode_fused_kernel (most batches): gate/up, SiLU * up and down in one kernel; the
 //   workgroup keeps h of its slice of I in LDS and writes fp32 down outputs per slice,
-//   which combine_parts_kernel adds in a fixed order with the routing weights.
-// decode_expert_kernel (one token, too few workgroups to fuse): gate/up into h, then
-//   down into y_perm (already weighted), then combine_kernel.
+//   which combine_parts_kernel adds in a fixed order with the routing weights. Above 16
+//   tokens every 16-row pass of an active expert has workgroups of its own.
+// decode_narrow_kernel (a few routed rows): the same in slices of 32 rows of I, so that a
+//   single token's experts still cover the chip.
+// decode_expert_kernel (shapes the fused kernels do not take): gate/up into h, then down
+//   into y_perm (already weighted), then combine_kernel.
 // Routing sources: the caller's grouping, the top-k ids (grouped here: histogram, scan
 // and ballot over at most kDecMaxRows rows in LDS, and published by the first workgroup
 // of each expert), or the routing kernel's per-expert token table (no grouping here; a
