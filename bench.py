@@ -321,6 +321,7 @@ def main():
         trace = slot_cache_trace(E, k, layers, 2 * steps, seed=0)
         ids_dev = torch.from_numpy(trace.reshape(2 * steps, layers, 1, k)).cuda()
         xs = [to_dev_bf16(olmoe_syn.x(1, stream=5000 + st)) for st in range(2 * steps)]
+        actives = [[sorted(set(int(e) for e in trace[st, l])) for l in range(layers)] for st in range(2 * steps)]
         # pinned-host -> device copy rate of one packed expert, for reference
         pin = torch.empty(expert_bytes, dtype=torch.uint8).pin_memory()
         dev = torch.empty(expert_bytes, dtype=torch.uint8, device="cuda")
@@ -342,16 +343,21 @@ def main():
             if S == E:
                 cache.preload()
 
+            b = exm.LayerBuffers(1, H, I, E, k)
+            ws = exm.alloc_workspace(exm.moe_workspace_bytes(1, H, I, E, k))
+
             def run(lo, hi):
+                # preallocated buffers; per layer: logits, weights of the trace's ids,
+                # grouping, then acquire + experts + combine in one library call
                 for st in range(lo, hi):
                     x = xs[st]
                     for l in range(layers):
                         ids = ids_dev[st, l]
-                        logits, _, _ = exm.route_topk(x, wr, k)
-                        w = exm.route_weights(logits, ids)
-                        off, sf, fs = exm.group_tokens(ids, E)
-                        bank = cache.acquire(l, sorted(int(e) for e in trace[st, l]))
-                        exm.moe_forward(x, ids, w, off, sf, fs, bank, I)
+                        exm.route_topk(x, wr, k, logits=b.logits, ids=b.ids, weights=b.weights)
+                        exm.route_weights(b.logits, ids, weights=b.weights)
+                        exm.group_tokens(ids, E, b.offsets, b.sorted_flat, b.flat_to_sorted)
+                        exm.moe_forward_cached(x, ids, b.weights, b.offsets, b.sorted_flat, b.flat_to_sorted, cache,
+                                               l, actives[st][l], I, y=b.y, workspace=ws)
 
             cache.reset_stats()
             torch.cuda.synchronize()
@@ -469,6 +475,8 @@ def main():
         trace = batch_trace(E, k, layers, 2 * steps, Bmax, seed=0)
         ids_all = torch.from_numpy(np.ascontiguousarray(trace)).cuda()          # [steps, layers, B, k]
         xs = [to_dev_bf16(olmoe_syn.x(Bmax, stream=9000 + st)) for st in range(2 * steps)]
+        actives = {B: [[np.unique(trace[st, l, :B]).tolist() for l in range(layers)] for st in range(2 * steps)]
+                   for B in batches}
         bank_bf = build_bf16_banks()[0]
         cache = exm.SlotCache(layers, E, S, expert_bytes)
         for l in range(layers):
@@ -478,6 +486,7 @@ def main():
         for B in batches:
             ws = exm.alloc_workspace(exm.moe_workspace_bytes(B, H, I, E, k))
             y = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            lb = exm.LayerBuffers(B, H, I, E, k)
             rec = {"batch": B, "slots": S, "layers": layers, "steps": steps}
             for name in ("w4a16_S%d" % S, "w4a16_resident", "bf16_resident"):
                 n_act = 0
@@ -488,16 +497,16 @@ def main():
                         x = xs[st][:B]
                         for l in range(layers):
                             ids = ids_all[st, l, :B]
-                            logits, _, _ = exm.route_topk(x, wr, k)
-                            w = exm.route_weights(logits, ids)
-                            off, sf, fs = exm.group_tokens(ids, E)
+                            exm.route_topk(x, wr, k, logits=lb.logits, ids=lb.ids, weights=lb.weights)
+                            w = exm.route_weights(lb.logits, ids, weights=lb.weights)
+                            off, sf, fs = exm.group_tokens(ids, E, lb.offsets, lb.sorted_flat, lb.flat_to_sorted)
                             if name == "bf16_resident":
                                 exm.moe_forward(x, ids, w, off, sf, fs, bank_bf, I, flags=exm.WEIGHTS_BF16, y=y,
                                                 workspace=ws)
                             elif name == "w4a16_resident":
                                 exm.moe_forward(x, ids, w, off, sf, fs, banks[0], I, y=y, workspace=ws)
                             else:
-                                active = np.unique(trace[st, l, :B]).tolist()
+                                active = actives[B][st][l]
                                 n_act += len(active)
                                 exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, l, active, I, y=y,
                                                        workspace=ws)

@@ -266,8 +266,7 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
 
 /* Expert layer through the slot cache in cache-sized waves (Fig. 1: waves of experts that
  * fit the cache). The distinct active experts (host list; it must hold every routed expert
- * of the call, e.g. from exmoe_active_experts, or the rows of a missing one are left
- * unwritten) are ordered with the ones already resident in the layer's slots first, then
+ * of the call, e.g. from exmoe_active_experts) are ordered with the ones already resident in the layer's slots first, then
  * the others, each part in ascending id. A list that fits slots_per_layer is one wave; a
  * longer one is cut into waves of slots_per_layer / 2 (1 when there is one slot). Each
  * wave is acquired (one layer-step of the cache's policy and counters: misses copied on
@@ -278,9 +277,12 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
  * a resident bank bit for bit. Arguments as exmoe_moe_forward, with the bank replaced by
  * (cache, layer); the cache must hold E experts per layer and not be a dry-run cache;
  * EXMOE_PATH_SEQUENTIAL -> EXMOE_ERR_UNSUPPORTED. The workspace size is
- * exmoe_moe_workspace_bytes (the per-wave expert->slot table lives there). The host
- * returns once every wave is enqueued; each per-wave table upload is a small copy from
- * pageable host memory. Calls on one cache must come from one host thread. */
+ * exmoe_moe_workspace_bytes (the per-wave expert->slot table lives there). A routed
+ * expert missing from the list: in a one-wave call it is computed if it happens to be
+ * resident, else flagged (exmoe_workspace_flags) and its rows are left unwritten; in a
+ * call of several waves its rows are left unwritten. The host returns once every wave is
+ * enqueued, without waiting for the GPU (a per-wave table travels in the arguments of a
+ * one-workgroup kernel). Calls on one cache must come from one host thread. */
 int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
                              const int32_t* expert_offsets, const int32_t* sorted_flat,
                              const int32_t* flat_to_sorted, exmoe_slot_cache* cache, int layer,

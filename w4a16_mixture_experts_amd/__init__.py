@@ -214,11 +214,11 @@ def topk_from_logits(logits, k: int, renormalize: bool = True):
     return ids, weights
 
 
-def route_weights(logits, ids, renormalize: bool = True):
+def route_weights(logits, ids, renormalize: bool = True, weights=None):
     torch = _torch()
     T, E = logits.shape
     k = ids.shape[1]
-    weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    weights = torch.empty((T, k), dtype=torch.float32, device=logits.device) if weights is None else weights
     _check(_lib.exmoe_route_weights(_ptr(logits), _ptr(ids), T, E, k, int(renormalize), _ptr(weights), _stream()))
     return weights
 

@@ -591,20 +591,27 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
     if ((st = slot_cache_acquire_ex(cache, layer, A.data() + w0, n, stream, after, prev_slots.data(),
                                     (int)prev_slots.size(), &bank)))
       return st;
-    if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
-    std::fill(wave_tbl.begin(), wave_tbl.end(), -1);
-    prev_slots.clear();
-    for (int i = 0; i < n; i++) {
-      wave_tbl[A[w0 + i]] = tbl[A[w0 + i]];
-      prev_slots.push_back(tbl[A[w0 + i]]);
-    }
-    // pageable source: the runtime stages it before returning, so wave_tbl can be reused;
-    // the upload is ordered after the previous wave's kernels on the same stream
-    EXMOE_HIP(hipMemcpyAsync(a.wave_table, wave_tbl.data(), sizeof(int32_t) * E, hipMemcpyHostToDevice, stream));
     a.base = static_cast<const uint8_t*>(bank.base);
     a.stride = bank.stride;
-    a.e2s = a.wave_table;
-    a.skip_absent = 1;
+    if (n_waves == 1) {
+      // every listed expert is resident now: the layer's own table serves, and a routed
+      // expert without a slot is flagged in the debug word
+      a.e2s = static_cast<const int32_t*>(bank.expert_to_slot);
+      a.skip_absent = 0;
+    } else {
+      if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
+      std::fill(wave_tbl.begin(), wave_tbl.end(), -1);
+      prev_slots.clear();
+      for (int i = 0; i < n; i++) {
+        wave_tbl[A[w0 + i]] = tbl[A[w0 + i]];
+        prev_slots.push_back(tbl[A[w0 + i]]);
+      }
+      // by value in the kernel arguments (no staging, no wait on the host), ordered after
+      // the previous wave's kernels on the same stream
+      EXMOE_HIP(table_upload(a.wave_table, wave_tbl.data(), E, stream));
+      a.e2s = a.wave_table;
+      a.skip_absent = 1;
+    }
     if (bf16w) {
       if (path == EXMOE_PATH_DECODE) EXMOE_HIP(launch_bf16_decode_experts(a, stream));
       else EXMOE_HIP(launch_bf16_prefill_experts(a, stream));

@@ -77,6 +77,9 @@ class ProfScope {
 
 // ---- kernel launchers (defined in the .hip files); each returns a HIP error code
 hipError_t span_fill(unsigned long long* p, int n, hipStream_t s);
+// dst[0..n) = host[0..n) (n <= kMaxExperts) by a one-workgroup kernel that takes the values
+// as kernel arguments: ordered on s, and the host buffer may be reused when the call returns.
+hipError_t table_upload(int32_t* dst, const int32_t* host, int n, hipStream_t s);
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,

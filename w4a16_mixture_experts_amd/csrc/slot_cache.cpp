@@ -137,9 +137,8 @@ int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_
       EXMOE_HIP(hipMemcpyAsync(layer_dev + (size_t)es.second * c->stride,
                                c->pinned + ((size_t)layer * c->E + es.first) * c->stride, c->expert_bytes,
                                hipMemcpyHostToDevice, c->copy_stream));
-    // Table from pageable memory: the runtime stages it before returning.
-    EXMOE_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * c->E, slot_of, sizeof(int32_t) * c->E,
-                             hipMemcpyHostToDevice, c->copy_stream));
+    // the table by value in kernel arguments: the host's copy may change right away
+    EXMOE_HIP(table_upload(c->d_tables + (size_t)layer * c->E, slot_of, c->E, c->copy_stream));
     EXMOE_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
     EXMOE_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
   }

@@ -1,4 +1,5 @@
-// Plain device copy: the kernel of known traffic used to calibrate HBM byte counters.
+// Small utility kernels: the plain device copy (the kernel of known traffic used to
+// calibrate HBM byte counters), span slot reset and the expert->slot table upload.
 #include "common.h"
 
 namespace exmoe {
@@ -20,6 +21,26 @@ __global__ __launch_bounds__(256) void span_fill_kernel(unsigned long long* p, i
 hipError_t span_fill(unsigned long long* p, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(span_fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+// An expert->slot table passed by value: the launch copies it into the kernel arguments, so
+// the host buffer is free as soon as the call returns and nothing waits for the stream.
+struct SlotTableArg {
+  int32_t v[kMaxExperts];
+};
+
+__global__ __launch_bounds__(kMaxExperts) void table_fill_kernel(int32_t* __restrict__ dst, SlotTableArg t, int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = t.v[i];
+}
+
+hipError_t table_upload(int32_t* dst, const int32_t* host, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > kMaxExperts) return hipErrorInvalidValue;
+  SlotTableArg t;
+  for (int i = 0; i < n; i++) t.v[i] = host[i];
+  hipLaunchKernelGGL(table_fill_kernel, dim3(1), dim3(kMaxExperts), 0, s, dst, t, n);
   return hipGetLastError();
 }
 
