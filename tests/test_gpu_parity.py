@@ -429,6 +429,53 @@ def test_olmoe_cached_waves(exm, olmoe):
     cache.close()
 
 
+def test_cached_forward_layer_stack_without_sync(exm):
+    """Three layers behind 4 slots each, 24 steps of 3-token cached forwards enqueued with
+    no synchronization in between, so the copies of one layer run while the kernels of
+    others are in flight (several waves when a step routes to more than 4 experts); every
+    fifth step layer 1 goes through the public acquire and a plain forward instead. Every
+    output equals the resident bank's bit for bit and the counters are the oracle's."""
+    import torch
+    from synthetic import slot_cache_trace
+    log("3-layer stack through 4-slot caches, no synchronization between layers")
+    shape = LayerShape(H=256, I=256, E=8, k=2)
+    layers = [Layer(shape, seed=40 + l, oracle_experts=False) for l in range(3)]
+    nb = exm.packed_expert_bytes(shape.H, shape.I)
+    S, steps = 4, 24
+    cache = exm.SlotCache(3, shape.E, S, nb)
+    for l, lay in enumerate(layers):
+        for e in range(shape.E):
+            cache.fill(l, e, lay.blobs[e])
+    sim = oracle.LRUSlotCacheSim(3, shape.E, S, nb)
+    trace = slot_cache_trace(E=shape.E, k=2, layers=3, steps=steps, seed=7)
+    outs, n_multi = [], 0
+    for st in range(steps):
+        x_all = to_dev_bf16(layers[0].syn.x(3, stream=100 + st))
+        for l, lay in enumerate(layers):
+            public = l == 1 and st % 5 == 2
+            rows = [trace[(st + j) % steps][l] for j in range(1 if public else 3)]
+            ids = torch.from_numpy(np.stack(rows).astype(np.int32)).cuda()
+            x = x_all[: len(rows)]
+            logits, _, _ = exm.route_topk(x, lay.wr, shape.k)
+            w = exm.route_weights(logits, ids)
+            off, sf, fs = exm.group_tokens(ids, shape.E)
+            active = sorted(set(int(e) for r in rows for e in r))
+            if public:
+                sim.acquire(l, active)
+                y = exm.moe_forward(x, ids, w, off, sf, fs, cache.acquire(l, active), shape.I)
+            else:
+                n_multi += len(sim.acquire_waves(l, active)) > 1
+                y = exm.moe_forward_cached(x, ids, w, off, sf, fs, cache, l, active, shape.I)
+            outs.append((st, l, y, exm.moe_forward(x, ids, w, off, sf, fs, lay.bank, shape.I)))
+    torch.cuda.synchronize()
+    for st, l, y, y_ref in outs:
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"step {st} layer {l}"
+    log(f"  {n_multi} calls ran in several waves")
+    assert n_multi > 0
+    _same_counters(cache, sim)
+    cache.close()
+
+
 # ------------------------------------------------------------------ bf16 comparator
 def run_layer_bf16(exm, lay: Layer, x_bits, bias=None, flags=0):
     import torch

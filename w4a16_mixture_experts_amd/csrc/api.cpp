@@ -576,18 +576,27 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   std::stable_partition(A.begin(), A.end(), [&](int e) { return tbl[e] >= 0; });
   const int W = ((int)A.size() > cS && cS >= 2) ? cS / 2 : cS;
   const int n_waves = ((int)A.size() + W - 1) / W;
+  // The layer's slots were last read by the kernels behind the layer's mark, when the cache
+  // knows it: the copies of waves 0 and 1 then wait only for those and overlap the kernels
+  // of other layers still in flight (without it, for all earlier work on the stream). The
+  // mark is dropped while this call enqueues (a failure part-way leaves it unknown) and
+  // recorded again after the last wave.
+  hipEvent_t prior = slot_cache_layer_mark(cache, layer);
+  slot_cache_forget_layer(cache, layer);
   std::vector<int32_t> prev_slots;
-  hipEvent_t mark = nullptr;
-  if (n_waves > 1) {
+  hipEvent_t mark = nullptr, start = prior;
+  if (n_waves > 1 && !prior) {
     EXMOE_HIP(slot_cache_event(cache, 0, &mark));
     EXMOE_HIP(hipEventRecord(mark, stream));   // everything before this call
+    start = mark;
   }
   for (int w = 0; w < n_waves; w++) {
     const int w0 = w * W;
     const int n = std::min((int)A.size() - w0, W);
     exmoe_expert_bank bank{};
-    hipEvent_t after = nullptr;   // wave 0 waits for all earlier work
-    if (w > 0) EXMOE_HIP(slot_cache_event(cache, w - 1, &after));   // done through wave w-2
+    hipEvent_t after = prior;     // wave 0: the layer's last readers (null: all earlier work)
+    if (w == 1) after = start;
+    if (w >= 2) EXMOE_HIP(slot_cache_event(cache, w - 1, &after));   // done through wave w-2
     if ((st = slot_cache_acquire_ex(cache, layer, A.data() + w0, n, stream, after, prev_slots.data(),
                                     (int)prev_slots.size(), &bank)))
       return st;
@@ -625,6 +634,7 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
       EXMOE_HIP(hipEventRecord(mark, stream));
     }
   }
+  EXMOE_HIP(slot_cache_mark_layer(cache, layer, stream));
   EXMOE_HIP(launch_combine(a, stream));
   return EXMOE_OK;
 }

@@ -163,6 +163,12 @@ int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_
                           exmoe_expert_bank* bank_out);
 // Event i of the cache's pool (created on first use, destroyed with the cache).
 hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev);
+// Per-layer mark of the cached forward: recorded on the compute stream after the last
+// kernels that read the layer's slots; null when unknown (none yet, or the layer was
+// acquired through the public call since, whose readers the cache cannot see).
+hipEvent_t slot_cache_layer_mark(exmoe_slot_cache* c, int layer);
+hipError_t slot_cache_mark_layer(exmoe_slot_cache* c, int layer, hipStream_t s);
+void slot_cache_forget_layer(exmoe_slot_cache* c, int layer);
 hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s);
 // Dense bf16 experts (the comparator): decode and prefill expert kernels.
 hipError_t launch_bf16_decode_experts(const MoeArgs& a, hipStream_t s);

@@ -2,7 +2,8 @@
 // Tab. 1): every packed expert stays in pinned host memory; each layer has a fixed
 // number of device slots; a miss copies the packed blob (int4 weights + bf16 scales, no
 // 16-bit expansion) on the cache's own copy stream, and the compute stream waits on an
-// event. The eviction policy is least-recently-used per layer with deterministic
+// event. Misses are split over two copy streams (two DMA queues move more than one over the
+// host link). The eviction policy is least-recently-used per layer with deterministic
 // tie-breaking (lowest free slot first; the victim is the oldest resident expert outside
 // the current active set), so the counters are reproducible.
 #include <hip/hip_runtime.h>
@@ -24,8 +25,8 @@ struct exmoe_slot_cache {
   uint8_t* pinned = nullptr;
   uint8_t* dev = nullptr;
   int32_t* d_tables = nullptr;       // [layers, E]
-  hipStream_t copy_stream = nullptr;
-  hipEvent_t ev_compute = nullptr, ev_copy = nullptr;
+  hipStream_t copy_stream = nullptr, copy_stream2 = nullptr;
+  hipEvent_t ev_compute = nullptr, ev_copy = nullptr, ev_copy2 = nullptr;
   std::vector<int32_t> slot_of;      // [layers, E], -1 = absent
   std::vector<int32_t> owner;        // [layers, S], -1 = free
   std::vector<uint64_t> stamp;       // [layers, E]
@@ -33,18 +34,27 @@ struct exmoe_slot_cache {
   exmoe_cache_stats st{};
   int device = 0;
   std::vector<hipEvent_t> wave_ev;   // compute-stream marks of a forward in waves (grown on demand)
+  // [layers] compute-stream mark after the last kernels that read the layer's slots, valid
+  // only while every reader of the layer came from the cached forward (created on demand)
+  std::vector<hipEvent_t> layer_ev;
+  std::vector<char> layer_ev_ok;
 };
 
 static void cache_free(exmoe_slot_cache* c) {
   if (!c) return;
   if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
+  if (c->copy_stream2) (void)hipStreamSynchronize(c->copy_stream2);
   if (c->pinned) (void)hipHostFree(c->pinned);
   if (c->dev) (void)hipFree(c->dev);
   if (c->d_tables) (void)hipFree(c->d_tables);
   if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  if (c->ev_copy2) (void)hipEventDestroy(c->ev_copy2);
   for (hipEvent_t ev : c->wave_ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : c->layer_ev)
+    if (ev) (void)hipEventDestroy(ev);
   if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  if (c->copy_stream2) (void)hipStreamDestroy(c->copy_stream2);
   delete c;
 }
 
@@ -65,6 +75,30 @@ hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev) {
   }
   *ev = c->wave_ev[i];
   return hipSuccess;
+}
+
+hipEvent_t slot_cache_layer_mark(exmoe_slot_cache* c, int layer) {
+  if (layer < 0 || layer >= (int)c->layer_ev_ok.size() || !c->layer_ev_ok[layer]) return nullptr;
+  return c->layer_ev[layer];
+}
+
+void slot_cache_forget_layer(exmoe_slot_cache* c, int layer) {
+  if (layer >= 0 && layer < (int)c->layer_ev_ok.size()) c->layer_ev_ok[layer] = 0;
+}
+
+hipError_t slot_cache_mark_layer(exmoe_slot_cache* c, int layer, hipStream_t s) {
+  if (c->resident) return hipSuccess;   // nothing is ever copied into its slots
+  if (c->layer_ev.empty()) {
+    c->layer_ev.assign(c->layers, nullptr);
+    c->layer_ev_ok.assign(c->layers, 0);
+  }
+  if (!c->layer_ev[layer]) {
+    hipError_t r = hipEventCreateWithFlags(&c->layer_ev[layer], hipEventDisableTiming);
+    if (r != hipSuccess) { c->layer_ev[layer] = nullptr; return r; }
+  }
+  hipError_t r = hipEventRecord(c->layer_ev[layer], s);
+  c->layer_ev_ok[layer] = r == hipSuccess;
+  return r;
 }
 
 int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
@@ -127,20 +161,26 @@ int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_
     bool early = after != nullptr;
     for (auto& es : copies)
       for (int i = 0; i < n_protect; i++) early = early && es.second != protect_slots[i];
-    if (early) {
-      EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, after, 0));
-    } else {
+    const bool two = copies.size() > 1;   // alternate the copies over both streams
+    hipEvent_t wait_for = after;
+    if (!early) {
       EXMOE_HIP(hipEventRecord(c->ev_compute, compute_stream));
-      EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, c->ev_compute, 0));
+      wait_for = c->ev_compute;
     }
-    for (auto& es : copies)
-      EXMOE_HIP(hipMemcpyAsync(layer_dev + (size_t)es.second * c->stride,
-                               c->pinned + ((size_t)layer * c->E + es.first) * c->stride, c->expert_bytes,
-                               hipMemcpyHostToDevice, c->copy_stream));
+    EXMOE_HIP(hipStreamWaitEvent(c->copy_stream, wait_for, 0));
+    if (two) EXMOE_HIP(hipStreamWaitEvent(c->copy_stream2, wait_for, 0));
+    for (size_t i = 0; i < copies.size(); i++)
+      EXMOE_HIP(hipMemcpyAsync(layer_dev + (size_t)copies[i].second * c->stride,
+                               c->pinned + ((size_t)layer * c->E + copies[i].first) * c->stride, c->expert_bytes,
+                               hipMemcpyHostToDevice, (i & 1) ? c->copy_stream2 : c->copy_stream));
     // the table by value in kernel arguments: the host's copy may change right away
     EXMOE_HIP(table_upload(c->d_tables + (size_t)layer * c->E, slot_of, c->E, c->copy_stream));
     EXMOE_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
     EXMOE_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
+    if (two) {
+      EXMOE_HIP(hipEventRecord(c->ev_copy2, c->copy_stream2));
+      EXMOE_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy2, 0));
+    }
   }
   bank_out->base = layer_dev;
   bank_out->stride = c->stride;
@@ -196,8 +236,12 @@ int exmoe_slot_cache_create(int layers, int E, int slots_per_layer, size_t exper
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess) {
       c->copy_stream = nullptr; cache_free(c); return hip_error(e, "hipStreamCreate");
     }
+    if ((e = hipStreamCreateWithFlags(&c->copy_stream2, hipStreamNonBlocking)) != hipSuccess) {
+      c->copy_stream2 = nullptr; cache_free(c); return hip_error(e, "hipStreamCreate");
+    }
     if ((e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_copy2, hipEventDisableTiming)) != hipSuccess) {
       cache_free(c); return hip_error(e, "hipEventCreate");
     }
     std::vector<int32_t> init((size_t)layers * E);
@@ -233,6 +277,9 @@ int exmoe_slot_cache_preload(exmoe_slot_cache* c, hipStream_t stream) {
 
 int exmoe_slot_cache_acquire(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
                              hipStream_t compute_stream, exmoe_expert_bank* bank_out) {
+  // the caller's kernels that will read these slots are unknown here: a later cached
+  // forward of this layer waits for everything enqueued before its copies
+  if (c) exmoe::slot_cache_forget_layer(c, layer);
   return exmoe::slot_cache_acquire_ex(c, layer, active_ids_host, n_active, compute_stream, nullptr, nullptr, 0,
                                       bank_out);
 }
