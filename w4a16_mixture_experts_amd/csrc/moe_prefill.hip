@@ -19,6 +19,8 @@
 // subtiles of a group once and reuses them across the 8 token subtiles (16 tokens each).
 // Q4 = false runs the same tiling on dense bf16 experts (the comparator): the weight
 // fragments are loaded as they are, with no scales and no seeds.
+#include <type_traits>
+
 #include "common.h"
 #include "device.h"
 
@@ -212,8 +214,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // Token subtile pairs (32 tokens) that hold rows of the segment: the last token tile of
+  // an expert is often mostly padding, and its MFMAs on padding rows are skipped.
+  const int npairs = pt.cnt - pt.tok0 >= kPfBN ? 4 : (pt.cnt - pt.tok0 + 31) / 32;
+
   // One group: compute it from (cact, cseed) while the next one lands in (nact, nseed).
-  auto group = [&](int g_, const uint16_t* cact, const float* cseed, uint16_t* nact, float* nseed) {
+  // full: every pair holds rows (no skip tests in the MFMA stream).
+  auto group = [&](auto full, int g_, const uint16_t* cact, const float* cseed, uint16_t* nact, float* nseed) {
     const int gn = g_ + 1 < G ? g_ + 1 : g_;   // the last prefetch repeats a group, harmlessly
     // the next group's activations and seeds into the other buffer, its weights into
     // registers; everything is waited for once, at the end of this group
@@ -250,6 +257,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     // token subtiles in pairs: activation fragments of both for all 4 K steps
 #pragma unroll
     for (int p = 0; p < 4; p++) {
+      if constexpr (!decltype(full)::value) {
+        if (p >= npairs) break;
+      }
       bf16x8 xfr[2][4];
       f32x4 seed[2];
 #pragma unroll
@@ -296,9 +306,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
       scur[ai] = snext[ai];
     }
   };
-  for (int g = 0; g < G; g += 2) {
-    group(g, s_act0, s_seed0, s_act1, s_seed1);
-    if (g + 1 < G) group(g + 1, s_act1, s_seed1, s_act0, s_seed0);
+  if (npairs == 4) {
+    for (int g = 0; g < G; g += 2) {
+      group(std::true_type{}, g, s_act0, s_seed0, s_act1, s_seed1);
+      if (g + 1 < G) group(std::true_type{}, g + 1, s_act1, s_seed1, s_act0, s_seed0);
+    }
+  } else {
+    for (int g = 0; g < G; g += 2) {
+      group(std::false_type{}, g, s_act0, s_seed0, s_act1, s_seed1);
+      if (g + 1 < G) group(std::false_type{}, g + 1, s_act1, s_seed1, s_act0, s_seed0);
+    }
   }
 #undef EXMOE_STAGE
 
