@@ -87,11 +87,23 @@ __device__ __forceinline__ void span_end(unsigned long long* sp) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even (finite values).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two fp32 values -> packed bf16 pair (lo in bits 0..15), round to nearest even, one
+// instruction.
+typedef float exmoe_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 exmoe_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const exmoe_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, exmoe_bf16x2));
+}
+
+// silu(g) * u = g / (1 + e^-g) * u in fp32, from the hardware 2^x and reciprocal (each
+// within about one ulp); g -> -inf gives -0, g -> +inf gives g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // fp64 -> bf16 with a single rounding (nearest even), no detour through fp32.

@@ -122,12 +122,9 @@ __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(MoeArgs a, int 
     if (tok < nrow) {
       const int row = seg0 + p * kBfTok + tok;   // sorted row
       if (GATEUP) {
-        uint16_t hb[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(acc0[i] / (1.0f + expf(-acc0[i])) * acc1[i]);
         uint2 pk;
-        pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-        pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+        pk.x = pack_bf16x2(silu_mul(acc0[0], acc1[0]), silu_mul(acc0[1], acc1[1]));
+        pk.y = pack_bf16x2(silu_mul(acc0[2], acc1[2]), silu_mul(acc0[3], acc1[3]));
         *reinterpret_cast<uint2*>(a.h + (size_t)row * a.I + rb0 * kTileRows + r4) = pk;
       } else {
         const int f = a.sorted_flat[row];

@@ -515,12 +515,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
       if (f >= 0) {
         if (GATEUP) {
           if (live0) {
-            uint16_t hb[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(acc0[i] / (1.0f + expf(-acc0[i])) * acc1[i]);
             uint2 pk;
-            pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-            pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+            pk.x = pack_bf16x2(silu_mul(acc0[0], acc1[0]), silu_mul(acc0[1], acc1[1]));
+            pk.y = pack_bf16x2(silu_mul(acc0[2], acc1[2]), silu_mul(acc0[3], acc1[3]));
             *reinterpret_cast<uint2*>(a.h + (size_t)(ex.seg0 + p * kDecTok + r) * a.I + rb0 * 16 + 4 * (lane >> 4)) = pk;
           }
         } else {
@@ -753,12 +750,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     uint16_t* hs = L.xs;
     {
       // padding token slots computed from the zero row: their h is 0
-      uint16_t hb[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(acc0[i] / (1.0f + expf(-acc0[i])) * acc1[i]);
       uint2 pk;
-      pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-      pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+      pk.x = pack_bf16x2(silu_mul(acc0[0], acc1[0]), silu_mul(acc0[1], acc1[1]));
+      pk.y = pack_bf16x2(silu_mul(acc0[2], acc1[2]), silu_mul(acc0[3], acc1[3]));
       *reinterpret_cast<uint2*>(hs + (lane & 15) * kHS + wave * 16 + 4 * (lane >> 4)) = pk;
     }
     __syncthreads();
@@ -937,12 +931,9 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
       g += red[2 * wave + 4 * qq][lane];
       u += red[2 * wave + 1 + 4 * qq][lane];
     }
-    uint16_t hb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) hb[i] = f32_to_bf16(g[i] / (1.0f + expf(-g[i])) * u[i]);
     uint2 pk;
-    pk.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-    pk.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+    pk.x = pack_bf16x2(silu_mul(g[0], u[0]), silu_mul(g[1], u[1]));
+    pk.y = pack_bf16x2(silu_mul(g[2], u[2]), silu_mul(g[3], u[3]));
     *reinterpret_cast<uint2*>(&hs[lane & 15][wave * 16 + 4 * (lane >> 4)]) = pk;
   }
   __syncthreads();
@@ -992,8 +983,8 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
         }
     }
     uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
-    pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+    pk.x = pack_bf16x2(s.x, s.y);
+    pk.y = pack_bf16x2(s.z, s.w);
     *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
   }
   span_end(a.span);
@@ -1044,8 +1035,8 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
     }
     if (c < a.H) {
       uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+      pk.x = pack_bf16x2(s.x, s.y);
+      pk.y = pack_bf16x2(s.z, s.w);
       *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
     }
   }

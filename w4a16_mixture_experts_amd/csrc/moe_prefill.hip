@@ -336,7 +336,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         const f32x4 gv = acc[2 * rbl][bj], uv = acc[2 * rbl + 1][bj];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint16_t hb = f32_to_bf16(gv[i] / (1.0f + expf(-gv[i])) * uv[i]);
+          const uint16_t hb = f32_to_bf16(silu_mul(gv[i], uv[i]));
           gpart[bj][i] += bf16_to_f32(hb);
           const int r = pt.tok0 + bj * 16 + tl0 + i;
           if (r < pt.cnt) a.h[(size_t)(pt.seg0 + r) * a.I + col] = hb;
