@@ -117,7 +117,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
   __shared__ __attribute__((aligned(16))) float s_seed0[kPfBN], s_seed1[kPfBN];
   __shared__ int s_scan[kMaxExperts + 1];
-  __shared__ float s_gsum[NW][kPfBN];
+  __shared__ __attribute__((aligned(16))) float s_gsum[NW][kPfBN];
 
   span_begin(a.span);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -331,32 +331,48 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
 #pragma unroll
     for (int rbl = 0; rbl < NA / 2; rbl++) {
       const int col = (rt * 8 + (NA / 2) * wave + rbl) * 16 + (lane & 15);
+      // this lane's first h row; its other rows follow at multiples of I. A full tile
+      // stores without row tests.
+      uint16_t* hrow = a.h + (size_t)(pt.seg0 + pt.tok0 + tl0) * a.I + col;
+      const int nv = pt.cnt - pt.tok0 - tl0;
+      auto store = [&](auto full) {
 #pragma unroll
-      for (int bj = 0; bj < 8; bj++) {
-        const f32x4 gv = acc[2 * rbl][bj], uv = acc[2 * rbl + 1][bj];
+        for (int bj = 0; bj < 8; bj++) {
+          const f32x4 gv = acc[2 * rbl][bj], uv = acc[2 * rbl + 1][bj];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const uint16_t hb = f32_to_bf16(silu_mul(gv[i], uv[i]));
-          gpart[bj][i] += bf16_to_f32(hb);
-          const int r = pt.tok0 + bj * 16 + tl0 + i;
-          if (r < pt.cnt) a.h[(size_t)(pt.seg0 + r) * a.I + col] = hb;
+          for (int i = 0; i < 4; i++) {
+            const uint16_t hb = f32_to_bf16(silu_mul(gv[i], uv[i]));
+            gpart[bj][i] += bf16_to_f32(hb);
+            const int rr = bj * 16 + i;
+            if (decltype(full)::value || rr < nv) hrow[(size_t)rr * a.I] = hb;
+          }
         }
-      }
+      };
+      if (pt.cnt - pt.tok0 >= kPfBN) store(std::true_type{});
+      else store(std::false_type{});
     }
     // per-token sum over this workgroup's 128 intermediate columns (one down group):
     // the 16 lanes of a row hold 16 columns each (the int4 down kernel's correction)
+    // (row rotations by 1, 2, 4 and 8, each step over all 32 values before the next, so
+    // that the steps of different values interleave; lane 0 of each row then writes them)
     if (Q4) {
+    auto rot_add = [&](auto ctrl) {
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++)
+      for (int bj = 0; bj < 8; bj++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float v = gpart[bj][i];
-        v += __uint_as_float(dpp_u32<0x121>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x122>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
-        if ((lane & 15) == 0) s_gsum[wave][bj * 16 + tl0 + i] = v;
-      }
+        for (int i = 0; i < 4; i++)
+          gpart[bj][i] += __uint_as_float(dpp_u32<decltype(ctrl)::value>(__float_as_uint(gpart[bj][i])));
+    };
+    rot_add(std::integral_constant<int, 0x121>{});
+    rot_add(std::integral_constant<int, 0x122>{});
+    rot_add(std::integral_constant<int, 0x124>{});
+    rot_add(std::integral_constant<int, 0x128>{});
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int bj = 0; bj < 8; bj++)
+        *reinterpret_cast<float4*>(&s_gsum[wave][bj * 16 + tl0]) =
+            make_float4(gpart[bj][0], gpart[bj][1], gpart[bj][2], gpart[bj][3]);
+    }
     __syncthreads();
     if (tid < kPfBN) {
       const int r = pt.tok0 + tid;
