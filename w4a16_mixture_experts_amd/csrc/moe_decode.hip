@@ -958,34 +958,48 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
 // ------------------------------------------------------------------------------------
 // combine: y[t, rows] = bf16(sum_j y_perm[t k + j, rows]) in slot order
 // ------------------------------------------------------------------------------------
-constexpr int kCombineTok = 16;
+// Workgroup = (token, 256 M float4 columns: grid x = token, y = column block); thread = M float4 columns 256 apart (every
+// load instruction of the workgroup covers 4 KiB in a row), with 16 / M slots of them in
+// flight at a time. M = 4 for many tokens (fewer, longer workgroups), 1 for few.
+template <int M>
 __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
   span_begin(a.span);
-  const int t0 = blockIdx.y * kCombineTok;
-  const int t1 = t0 + kCombineTok < a.T ? t0 + kCombineTok : a.T;
-  const int row0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < (t1 - t0) * 16; i += blockDim.x) {
-    const int t = t0 + i / 16, c = row0 + (i % 16) * 4;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* src = a.y_perm + (size_t)t * a.k * a.H + c;
-    // eight slots in flight at a time, added in slot order
-    for (int j0 = 0; j0 < a.k; j0 += 8) {
-      float4 v[8];
+  const int t = blockIdx.x;
+  const int nv = a.H >> 2;                               // float4 per row
+  const int q0 = blockIdx.y * (256 * M) + (int)threadIdx.x;
+  const float* src = a.y_perm + (size_t)t * a.k * a.H;
+  constexpr int JB = 16 / M;
+  float4 s[M];
 #pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int j = j0 + u < a.k ? j0 + u : a.k - 1;
-        v[u] = *reinterpret_cast<const float4*>(src + (size_t)j * a.H);
+  for (int m = 0; m < M; m++) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < a.k; j0 += JB) {
+    float4 v[JB][M];
+#pragma unroll
+    for (int u = 0; u < JB; u++)
+#pragma unroll
+      for (int m = 0; m < M; m++) {
+        const int q = q0 + 256 * m;
+        v[u][m] = (j0 + u < a.k && q < nv) ? *reinterpret_cast<const float4*>(src + (size_t)(j0 + u) * a.H + 4 * q)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < 8; u++)
-        if (j0 + u < a.k) {
-          s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+    for (int u = 0; u < JB; u++)
+      if (j0 + u < a.k) {   // added in slot order
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+          s[m].x += v[u][m].x; s[m].y += v[u][m].y; s[m].z += v[u][m].z; s[m].w += v[u][m].w;
         }
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    const int q = q0 + 256 * m;
+    if (q < nv) {
+      uint2 pk;
+      pk.x = pack_bf16x2(s[m].x, s[m].y);
+      pk.y = pack_bf16x2(s[m].z, s[m].w);
+      *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + 4 * q) = pk;
     }
-    uint2 pk;
-    pk.x = pack_bf16x2(s.x, s.y);
-    pk.y = pack_bf16x2(s.z, s.w);
-    *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
   }
   span_end(a.span);
 }
@@ -1191,7 +1205,11 @@ hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
     EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, as);
     return hipGetLastError();
   }
-  EXMOE_LAUNCH(prof, combine_kernel, dim3(a.H / 64, (a.T + kCombineTok - 1) / kCombineTok), dim3(256), 0, s, as);
+  const int nv = a.H / 4;
+  if (a.T >= 512)
+    EXMOE_LAUNCH(prof, combine_kernel<4>, dim3(a.T, (nv + 1023) / 1024), dim3(256), 0, s, as);
+  else
+    EXMOE_LAUNCH(prof, combine_kernel<1>, dim3(a.T, (nv + 255) / 256), dim3(256), 0, s, as);
   return hipGetLastError();
 }
 
