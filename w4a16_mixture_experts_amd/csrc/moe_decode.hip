@@ -1024,10 +1024,9 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
       for (int q0 = 0; q0 < a.nparts; q0 += 16) {
         float4 v[16];
 #pragma unroll
-        for (int u = 0; u < 16; u++) {
-          const int q = q0 + u < a.nparts ? q0 + u : a.nparts - 1;
-          v[u] = *reinterpret_cast<const float4*>(src + q * slice);
-        }
+        for (int u = 0; u < 16; u++)
+          v[u] = q0 + u < a.nparts ? *reinterpret_cast<const float4*>(src + (q0 + u) * slice)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int u = 0; u < 16; u++)
           if (q0 + u < a.nparts) {
