@@ -1056,6 +1056,49 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
   span_end(a.span);
 }
 
+// The same sums for many tokens (the pass-parallel decode): workgroup = (token, 1024
+// columns), thread = one float4 column over every slot and slice, 16 loads in flight; the
+// slot and slice order and the roundings (slot sum, times the weight, then added) are the
+// ones of combine_parts_kernel.
+template <int NP>
+__global__ __launch_bounds__(256) void combine_parts_tok_kernel(MoeArgs a) {
+  span_begin(a.span);
+  const int t = blockIdx.x;
+  const int q4 = blockIdx.y * 256 + (int)threadIdx.x;   // float4 column
+  if (q4 < (a.H >> 2)) {
+    const size_t slice = (size_t)a.T * a.k * a.H;
+    const float* src = a.part + (size_t)t * a.k * a.H + 4 * q4;
+    constexpr int JB = 16 / NP;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < a.k; j0 += JB) {
+      float4 v[JB][NP];
+#pragma unroll
+      for (int u = 0; u < JB; u++)
+#pragma unroll
+        for (int q = 0; q < NP; q++)
+          v[u][q] = j0 + u < a.k ? *reinterpret_cast<const float4*>(src + (size_t)(j0 + u) * a.H + q * slice)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < JB; u++)
+        if (j0 + u < a.k) {
+          float4 sj = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int q = 0; q < NP; q++) {
+            sj.x += v[u][q].x; sj.y += v[u][q].y; sj.z += v[u][q].z; sj.w += v[u][q].w;
+          }
+          const float wt = a.w[t * a.k + j0 + u];
+          acc.x += __fmul_rn(sj.x, wt); acc.y += __fmul_rn(sj.y, wt);
+          acc.z += __fmul_rn(sj.z, wt); acc.w += __fmul_rn(sj.w, wt);
+        }
+    }
+    uint2 pk;
+    pk.x = pack_bf16x2(acc.x, acc.y);
+    pk.y = pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + 4 * q4) = pk;
+  }
+  span_end(a.span);
+}
+
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
@@ -1201,7 +1244,13 @@ hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
   MoeArgs as = a;
   as.span = prof.span();
   if (a.nparts > 0) {
-    EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, as);
+    const dim3 tok_grid(a.T, (a.H / 4 + 255) / 256);
+    if (a.T > kDecTok && a.nparts == 4)
+      EXMOE_LAUNCH(prof, combine_parts_tok_kernel<4>, tok_grid, dim3(256), 0, s, as);
+    else if (a.T > kDecTok && a.nparts == 8)
+      EXMOE_LAUNCH(prof, combine_parts_tok_kernel<8>, tok_grid, dim3(256), 0, s, as);
+    else
+      EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, as);
     return hipGetLastError();
   }
   const int nv = a.H / 4;

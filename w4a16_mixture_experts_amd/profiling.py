@@ -105,7 +105,7 @@ def _ours(name: str) -> bool:
     return name.split("<")[0] in ("route_logits_kernel", "topk_kernel", "topk_group_kernel", "group_kernel",
                                   "decode_gateup_kernel", "decode_down_kernel", "combine_kernel", "xsum_kernel",
                                   "prefill_kernel", "copy_kernel", "route_token_kernel", "decode_expert_kernel",
-                                  "decode_fused_kernel", "combine_parts_kernel", "route_sel_kernel",
+                                  "decode_fused_kernel", "combine_parts_kernel", "combine_parts_tok_kernel", "route_sel_kernel",
                                   "decode_narrow_kernel", "bf16_decode_kernel", "group_count_kernel",
                                   "group_scan_kernel", "group_scatter_kernel", "table_fill_kernel", "span_fill_kernel")
 
