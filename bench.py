@@ -211,7 +211,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the layer is not sharded across GPUs "
-                                   "(see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+                                   "(sharded, each GPU would hold E/G experts and trade token rows all-to-all)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import w4a16_mixture_experts_amd as exm
