@@ -17,7 +17,7 @@
  *    outputs are untouched. Faults of already-enqueued device work surface as
  *    EXMOE_ERR_HIP on a later synchronizing call.
  *  - Ownership: the caller owns every buffer passed in. The library owns only slot-cache
- *    handles (pinned pool, device slots, copy stream, events).
+ *    handles (pinned pool, device slots, copy streams, events).
  *  - Device calls are asynchronous on the caller's stream unless stated otherwise.
  *  - bf16 values travel as raw uint16_t bit patterns; indices are int32; routing weights
  *    are fp32. Device buffers must be 16-byte aligned.
@@ -224,7 +224,8 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
  * Policy (the pages name none): least-recently-used per layer. A layer-step looks up its
  * distinct active experts in ascending id; a hit refreshes the expert's stamp; a miss
  * takes the lowest free slot, else evicts the resident expert with the oldest stamp that
- * is not in the current active set, and copies the blob on the cache's copy stream.
+ * is not in the current active set, and copies the blob on one of the cache's two copy
+ * streams (successive misses alternate between them).
  * slots_per_layer == E is full residency: exmoe_slot_cache_preload copies everything and
  * lookups are bypassed (counters stay 0, stats.resident = 1).
  * ---------------------------------------------------------------------------------- */
@@ -241,7 +242,7 @@ typedef struct exmoe_cache_stats {
 enum { EXMOE_CACHE_DRY_RUN = 1 }; /* policy and counters only: no allocation, no copies */
 
 /* Allocates the pinned pool (layers*E*expert_stride bytes), the device slots
- * (layers*slots*expert_stride), a copy stream and the device expert->slot tables;
+ * (layers*slots*expert_stride), two copy streams and the device expert->slot tables;
  * synchronous. expert_bytes is the packed size; the stride rounds it up to 256 B. */
 int exmoe_slot_cache_create(int layers, int E, int slots_per_layer, size_t expert_bytes, int flags,
                             exmoe_slot_cache** out);
@@ -251,9 +252,9 @@ int exmoe_slot_cache_host_slot(exmoe_slot_cache* cache, int layer, int expert, v
 /* Full residency only: copies every blob to its slot and waits. */
 int exmoe_slot_cache_preload(exmoe_slot_cache* cache, hipStream_t stream);
 /* One layer-step: looks up the active experts (host ids, any order, duplicates ignored),
- * enqueues the copies for the misses on the copy stream, uploads the layer's
- * expert->slot table, and makes compute_stream wait for both; bank_out then describes the
- * layer's slots. More distinct active experts than slots -> EXMOE_ERR_CACHE, state kept.
+ * enqueues the copies for the misses on the copy streams after everything enqueued on
+ * compute_stream so far, uploads the layer's expert->slot table, and makes compute_stream
+ * wait for them; bank_out then describes the layer's slots. More distinct active experts than slots -> EXMOE_ERR_CACHE, state kept.
  * In dry-run mode only the policy and counters run and bank_out is zeroed. */
 int exmoe_slot_cache_acquire(exmoe_slot_cache* cache, int layer, const int32_t* active_ids_host,
                              int n_active, hipStream_t compute_stream, exmoe_expert_bank* bank_out);
@@ -270,10 +271,13 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
  * the others, each part in ascending id. A list that fits slots_per_layer is one wave; a
  * longer one is cut into waves of slots_per_layer / 2 (1 when there is one slot). Each
  * wave is acquired (one layer-step of the cache's policy and counters: misses copied on
- * the cache's copy stream, the compute stream waits for them), then the expert kernels
+ * the cache's copy streams, the compute stream waits for them), then the expert kernels
  * run for that wave's experts only. With half-size waves the copies of wave w+1 land in
  * slots that wave w does not read, so they wait only for wave w-1's kernels and overlap
- * wave w's. The combine runs once after the last wave, so y equals exmoe_moe_forward's on
+ * wave w's. The copies of a layer's first waves wait only for the last kernels that read
+ * that layer's slots (recorded by the previous cached forward of the layer; after an
+ * exmoe_slot_cache_acquire of the layer, for all earlier work), so they overlap the
+ * kernels of other layers still in flight. The combine runs once after the last wave, so y equals exmoe_moe_forward's on
  * a resident bank bit for bit. Arguments as exmoe_moe_forward, with the bank replaced by
  * (cache, layer); the cache must hold E experts per layer and not be a dry-run cache;
  * EXMOE_PATH_SEQUENTIAL -> EXMOE_ERR_UNSUPPORTED. The workspace size is
