@@ -409,6 +409,27 @@ def test_forward_cached_waves_equal_resident(exm, path):
     cache.close()
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_forward_cached_most_experts(exm, path):
+    """256 experts (the largest E, so every per-wave table is the full 1 KiB of kernel
+    arguments) behind 24 slots, top-8 of 40 tokens: several waves per call, bitwise equal
+    to the resident bank; the counters are the oracle's wave simulation."""
+    log(f"cached waves, 256 experts, 24 slots, path {path}")
+    shape = LayerShape(H=128, I=128, E=256, k=8)
+    lay = Layer(shape, seed=23, oracle_experts=False)
+    nb = exm.packed_expert_bytes(shape.H, shape.I)
+    cache = exm.SlotCache(1, shape.E, 24, nb)
+    for e in range(shape.E):
+        cache.fill(0, e, lay.blobs[e])
+    sim = oracle.LRUSlotCacheSim(1, shape.E, 24, nb)
+    for T, stream in ((40, 1), (7, 2), (40, 3)):
+        n_act, n_waves = _cached_vs_resident(exm, lay, cache, sim, to_dev_bf16(lay.syn.x(T, stream=stream)), path)
+        assert n_waves == -(-n_act // (24 if n_act <= 24 else 12))
+    assert n_waves > 1
+    _same_counters(cache, sim)
+    cache.close()
+
+
 def test_olmoe_cached_waves(exm, olmoe):
     """OLMoE-shaped decode (16 tokens, fused expert kernel) and Zipf-biased prefill (128
     tokens) through a 16-slot cache: bitwise equal to the resident bank."""
