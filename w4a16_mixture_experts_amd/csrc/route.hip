@@ -23,6 +23,77 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------
+// Logits of many tokens on the fp64 matrix cores: a workgroup owns a tile of 16 tokens x
+// 16 experts, each of its KW waves a strided share of the 32-column chunks of H, and the
+// KW partial tiles are added in wave order through LDS. v_mfma_f64_16x16x4f64 takes A[m][k]
+// from lane 16 k + m and B[k][n] from lane 16 k + n, and leaves C[g + 4 i][n] in value i of
+// lane 16 g + n. Lane group g loads 8 bf16 of its row at columns 8 g .. 8 g + 7 of the
+// chunk; MFMA j of the chunk multiplies element j of every lane, so that the 4 K slots of
+// MFMA j are columns {8 g + j}. The products of bf16 values are exact in fp64 and the sum
+// is rounded to bf16 once, as in the vector form.
+// ---------------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <int KW>
+__global__ __launch_bounds__(64 * KW) void route_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ wr,
+                                                                    const float* __restrict__ bias, int T, int H,
+                                                                    int E, uint16_t* __restrict__ logits) {
+  __shared__ f64x4 red[KW][64];
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nEB = (E + 15) / 16;
+  const int t0 = (blockIdx.x / nEB) * 16, e0 = (blockIdx.x % nEB) * 16;
+  const int m = lane & 15, g = lane >> 4;
+  const int t = t0 + m < T ? t0 + m : T - 1, e = e0 + m < E ? e0 + m : E - 1;   // clamped rows
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H) + g;
+  const uint4* wrr = reinterpret_cast<const uint4*>(wr + (size_t)e * H) + g;
+  const int nch = H / 32;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  auto chunk = [&](const uint4 xu, const uint4 wu) {
+    const uint32_t xq[4] = {xu.x, xu.y, xu.z, xu.w}, wq[4] = {wu.x, wu.y, wu.z, wu.w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(xq[q] << 16),
+                                                 (double)__uint_as_float(wq[q] << 16), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(xq[q] & 0xFFFF0000u),
+                                                 (double)__uint_as_float(wq[q] & 0xFFFF0000u), acc, 0, 0, 0);
+    }
+  };
+  // two chunks in flight: the loads of chunk c + 2 KW go out before chunk c's MFMAs
+  int c = wave;
+  uint4 xa, wa, xb, wb;
+  if (c < nch) { xa = xr[4 * c]; wa = wrr[4 * c]; }
+  if (c + KW < nch) { xb = xr[4 * (c + KW)]; wb = wrr[4 * (c + KW)]; }
+  for (; c < nch; c += 2 * KW) {
+    const uint4 xc = xa, wc = wa;
+    if (c + 2 * KW < nch) { xa = xr[4 * (c + 2 * KW)]; wa = wrr[4 * (c + 2 * KW)]; }
+    chunk(xc, wc);
+    if (c + KW < nch) {
+      const uint4 xd = xb, wd = wb;
+      if (c + 3 * KW < nch) { xb = xr[4 * (c + 3 * KW)]; wb = wrr[4 * (c + 3 * KW)]; }
+      chunk(xd, wd);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f64x4 s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < KW; w++) s += red[w][lane];
+    const int ee = e0 + m;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int tt = t0 + g + 4 * i;
+      if (tt < T && ee < E) {
+        const double v = bias ? s[i] + (double)bias[ee] : s[i];
+        logits[(size_t)tt * E + ee] = f64_to_bf16(v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Logits, top-k and the expert table of a few tokens (T <= 16) in one launch: the
 // selection part (route_wave.h) with one wave per token of a 4-token block and one block
 // of 2 experts per workgroup.
@@ -200,23 +271,17 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   ProfScope prof("route_logits", s);
   if (T <= 128) {
     // one wave per 2 tokens x 2 experts, the whole wave on H: a row in one round trip
-    // (beyond about 128 tokens the 4 x 4 blocks' operand reuse wins: 512 tokens and 64
-    // experts 15.8 -> 12.3 us)
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
     EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
   } else {
-    const int blocks = ((T + 3) / 4) * ((E + 3) / 4);
-    if ((blocks + 3) / 4 >= 1024) {
-      // four 16-lane groups per wave, each on a 4 x 4 block
-      EXMOE_LAUNCH(prof, (route_logits_kernel<4, 4, 16, 2>), dim3((blocks + 3) / 4), dim3(64), 0, s, x, wr, bias, T,
-                   H, E, logits);
-    } else {
-      // few experts: a 4 x 4 block per wave, so that the launch still has about two waves
-      // per SIMD to overlap the fp64 arithmetic with the loads (measured on a 4096-token,
-      // 8-expert router: 37 -> 20 us)
-      EXMOE_LAUNCH(prof, (route_logits_kernel<4, 4, 64, 2>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E,
-                   logits);
-    }
+    // 16 x 16 tiles on the fp64 matrix cores (H is a multiple of 128); the K split keeps
+    // about two waves per SIMD. Measured against four 4 x 4 blocks per wave: 2048 tokens
+    // and 64 experts 30.9 -> 16.7 us, 512 tokens 12.4 -> 8.9 us.
+    const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
+    if (tiles >= 512)
+      EXMOE_LAUNCH(prof, route_logits_mfma_kernel<4>, dim3(tiles), dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+    else
+      EXMOE_LAUNCH(prof, route_logits_mfma_kernel<8>, dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
   }
   return hipGetLastError();
 }

@@ -17,8 +17,8 @@ namespace exmoe {
 // LANES lanes in interleaved 16-byte chunks (contiguous bytes across the group); each
 // chunk is converted to fp64 once and feeds TB*EB fp64 FMAs (bf16 products are exact in
 // fp64). Partial sums are added with DPP row rotations (and across rows with readlane
-// when LANES = 64); one lane rounds once to bf16. Few tokens: LANES = 64, small blocks,
-// many waves. Many tokens: LANES = 16, 4 x 4 blocks for operand reuse.
+// when LANES = 64); one lane rounds once to bf16. Used with LANES = 64 and small blocks
+// (many waves) for a few tokens; many tokens go to the fp64 matrix-core kernel.
 // ---------------------------------------------------------------------------------
 // WT: write-through (agent-scope atomic) stores of the logits, read back by another
 // workgroup in the same launch.

@@ -106,6 +106,7 @@ def _ours(name: str) -> bool:
                                   "decode_gateup_kernel", "decode_down_kernel", "combine_kernel", "xsum_kernel",
                                   "prefill_kernel", "copy_kernel", "route_token_kernel", "decode_expert_kernel",
                                   "decode_fused_kernel", "combine_parts_kernel", "combine_parts_tok_kernel", "route_sel_kernel",
+                                  "route_logits_mfma_kernel",
                                   "decode_narrow_kernel", "bf16_decode_kernel", "group_count_kernel",
                                   "group_scan_kernel", "group_scatter_kernel", "table_fill_kernel", "span_fill_kernel")
 
