@@ -274,14 +274,11 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
     EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
   } else {
-    // 16 x 16 tiles on the fp64 matrix cores (H is a multiple of 128); the K split keeps
-    // about two waves per SIMD. Measured against four 4 x 4 blocks per wave: 2048 tokens
-    // and 64 experts 30.9 -> 16.7 us, 512 tokens 12.4 -> 8.9 us.
+    // 16 x 16 tiles on the fp64 matrix cores (H is a multiple of 128), H split over 8
+    // waves. Measured against four 4 x 4 blocks of vector FMAs per wave: 2048 tokens and
+    // 64 experts 30.9 -> 15.5 us, 512 tokens 12.4 -> 8.8 us.
     const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
-    if (tiles >= 512)
-      EXMOE_LAUNCH(prof, route_logits_mfma_kernel<4>, dim3(tiles), dim3(256), 0, s, x, wr, bias, T, H, E, logits);
-    else
-      EXMOE_LAUNCH(prof, route_logits_mfma_kernel<8>, dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
+    EXMOE_LAUNCH(prof, route_logits_mfma_kernel<8>, dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
   }
   return hipGetLastError();
 }
