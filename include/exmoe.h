@@ -258,6 +258,18 @@ int exmoe_slot_cache_preload(exmoe_slot_cache* cache, hipStream_t stream);
  * In dry-run mode only the policy and counters run and bank_out is zeroed. */
 int exmoe_slot_cache_acquire(exmoe_slot_cache* cache, int layer, const int32_t* active_ids_host,
                              int n_active, hipStream_t compute_stream, exmoe_expert_bank* bank_out);
+/* The cache-sized waves (Fig. 1) of one exmoe_moe_forward_cached call on `layer`, as that
+ * call's host side forms them: the distinct ids of active_ids_host (host, any order,
+ * duplicates ignored) in wave order -- the experts already resident in the layer's slots
+ * first, then the others, each part ascending -- into order_out (host, room for n_active
+ * ints), their count into *n_distinct and the wave size into *wave_size (the waves are
+ * consecutive runs of that many ids, the last one possibly shorter: slots_per_layer when
+ * every id fits, else slots_per_layer / 2, or 1 with one slot). run == 0 only plans and
+ * changes nothing. run != 0 then looks each wave up in turn, the policy and counters a
+ * cached forward applies, and is allowed on a dry-run cache only (EXMOE_ERR_CACHE
+ * otherwise: with device slots the cached forward itself runs the waves, with copies). */
+int exmoe_slot_cache_waves(exmoe_slot_cache* cache, int layer, const int32_t* active_ids_host, int n_active,
+                           int run, int32_t* order_out, int* n_distinct, int* wave_size);
 /* Host copy of the layer's expert->slot table (-1 = not resident), int32 [E]. */
 int exmoe_slot_cache_table(const exmoe_slot_cache* cache, int layer, int32_t* table_host);
 int exmoe_slot_cache_stats(const exmoe_slot_cache* cache, exmoe_cache_stats* out);

@@ -1,7 +1,7 @@
 """Symmetric group-128 int4 weight quantization (oracle).
 
-Follows the ExactMoE abstract ("symmetric group-128 four-bit weight quantization
-only to routed experts"). Readings where the pages are silent:
+Follows the ExactMoE abstract: symmetric int4 with one scale per 128 inputs, applied to
+the routed experts only. Readings where the pages are silent:
   * scale divisor: s = absmax / 7 (largest positive int4 code), computed as an IEEE
     fp32 division, then rounded to bf16 (nearest, ties to even);
   * code: q = clamp(round_half_even(w / s), -8, 7), the quotient formed in fp64

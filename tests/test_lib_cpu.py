@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from oracle import layout as OL
-from synthetic import SyntheticLayer, TINY, OLMOE, LayerShape, slot_cache_trace
+from synthetic import SyntheticLayer, TINY, OLMOE, LayerShape, slot_cache_trace, batch_trace
 
 exm = pytest.importorskip("w4a16_mixture_experts_amd")
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -169,6 +169,89 @@ def test_slot_cache_policy_matches_oracle(S):
     assert st["h2d_copies"] == sim.misses and st["resident"] == 0
     c.reset_stats()
     assert c.stats()["lookups"] == 0
+    c.close()
+
+
+def _same_stats(c, sim):
+    st = c.stats()
+    assert (st["lookups"], st["hits"], st["misses"], st["evictions"], st["h2d_bytes"]) == \
+        (sim.lookups, sim.hits, sim.misses, sim.evictions, sim.h2d_bytes)
+    return st
+
+
+@pytest.mark.parametrize("S", [8, 16, 32, 64])
+def test_slot_cache_benchmark_trace_matches_oracle(S):
+    """The slot-cache decode workload as timed: 16 OLMoE-shaped layers, one 256-step trace
+    (seed 0), the first 128 steps warm the cache, counters reset, the next 128 are the
+    reported ones. The library's policy (dry run, the same host code as the cached forward,
+    one wave per layer-step since 8 experts fit every S) and the oracle's simulator agree
+    on every counter at both points, and the reported hit rates are those counters."""
+    E, k, layers, steps = 64, 8, 16, 128
+    nb = 3_244_032
+    trace = slot_cache_trace(E, k, layers, 2 * steps, seed=0)
+    c = exm.SlotCache(layers, E, S, nb, dry_run=True)
+    sim = oracle.LRUSlotCacheSim(layers, E, S, nb)
+    rates = []
+    for half in range(2):
+        for st in range(half * steps, (half + 1) * steps):
+            for l in range(layers):
+                active = sorted(set(int(e) for e in trace[st, l]))
+                waves = c.waves(l, active, run=True)
+                ref = sim.acquire_waves(l, active)
+                assert waves == [w for w, _ in ref]
+                assert np.array_equal(c.table(l), ref[-1][1])
+        got = _same_stats(c, sim)
+        rates.append(got["hits"] / max(got["lookups"], 1))
+        c.reset_stats(); sim.reset_stats()
+    if S == E:
+        assert got["resident"] == 1 and got["lookups"] == 0
+    else:
+        # every layer-step looks up its 8 distinct experts
+        assert got["lookups"] == steps * layers * k
+    print(f"S={S}: cold hit rate {rates[0]:.4f}, warm {rates[1]:.4f}")
+    c.close()
+
+
+def test_batched_trace_waves_match_oracle():
+    """Batched decode through 16 slots per layer as timed: batch 1, 2, 4, 8 in turn on one
+    cache, each 64 warm-up steps then 64 counted ones (counters reset in between), the
+    batch's distinct experts per layer in cache-sized waves. The library's wave plan and
+    policy (dry run) equal the oracle's wave simulation at every layer-step, and the
+    counters agree at every reset."""
+    E, k, layers, steps, S = 64, 8, 16, 64, 16
+    nb = 3_244_032
+    trace = batch_trace(E, k, layers, 2 * steps, 8, seed=0)
+    c = exm.SlotCache(layers, E, S, nb, dry_run=True)
+    sim = oracle.LRUSlotCacheSim(layers, E, S, nb)
+    multi = 0
+    for B in (1, 2, 4, 8):
+        for half in range(2):
+            for st in range(half * steps, (half + 1) * steps):
+                for l in range(layers):
+                    active = np.unique(trace[st, l, :B]).tolist()
+                    waves = c.waves(l, active, run=True)
+                    ref = sim.acquire_waves(l, active)
+                    assert waves == [w for w, _ in ref], (B, st, l)
+                    multi += len(waves) > 1
+            _same_stats(c, sim)
+            c.reset_stats(); sim.reset_stats()
+    assert multi > 0          # batch 2 and above route some layer-steps past 16 experts
+    c.close()
+
+
+def test_slot_cache_waves_plan_only():
+    c = exm.SlotCache(1, 8, 4, 100, dry_run=True)
+    assert c.waves(0, [5, 1, 1, 7, 3, 2]) == [[1, 2], [3, 5], [7]]     # 5 > 4: waves of 2
+    assert c.stats()["lookups"] == 0                                     # plan only
+    c.acquire(0, [5, 7])
+    assert c.waves(0, [1, 5, 7]) == [[5, 7, 1]]                          # fits: residents first
+    assert c.waves(0, [1, 2, 3, 5, 7]) == [[5, 7], [1, 2], [3]]
+    with pytest.raises(exm.ExmoeError) as ei:
+        c.waves(1, [0])
+    assert ei.value.status == exm.ERR_CACHE
+    with pytest.raises(exm.ExmoeError):
+        c.waves(0, [8])
+    assert c.waves(0, []) == []
     c.close()
 
 

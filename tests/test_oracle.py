@@ -186,6 +186,46 @@ def test_pack_fast_equals_loop_and_roundtrip():
         assert np.array_equal(x, y)
 
 
+def test_int4_layout_positions():
+    """Packed int4 blob: random elements of every matrix, in both the gate/up and the down
+    region and over several input groups, land at the tile, lane, word and nibble that
+    the layout statement gives, and their row scales at the tile's scale slot. The
+    positions are computed here from the statement alone (not from the packer's tile
+    list), so a swapped loop order, a transposed operand or a wrong nibble shift fails."""
+    H, I = 256, 384
+    G, GD = H // 128, I // 128
+    rng = np.random.default_rng(11)
+    qg = rng.integers(-8, 8, (I, H)).astype(np.int8); qu = rng.integers(-8, 8, (I, H)).astype(np.int8)
+    qd = rng.integers(-8, 8, (H, I)).astype(np.int8)
+    # scales all distinct, so a scale read from the wrong slot cannot match
+    sv = rng.permutation(2 * I * G + H * GD).astype(np.uint16) + 1
+    sg = sv[:I * G].reshape(I, G); su = sv[I * G:2 * I * G].reshape(I, G); sd = sv[2 * I * G:].reshape(H, GD)
+    blob = L.pack_expert(qg, sg, qu, su, qd, sd, H, I)
+    nt = 2 * (I // 16) * G + (H // 16) * GD
+    assert len(blob) == nt * (1024 + 32)
+    mats = ((qg, sg, I, H), (qu, su, I, H), (qd, sd, H, I))
+    hit = {0: set(), 1: set(), 2: set()}
+    for _ in range(4000):
+        which = int(rng.integers(0, 3))
+        Q, S, R, K = mats[which]
+        r, c = int(rng.integers(0, R)), int(rng.integers(0, K))
+        b, g = r // 16, c // 128
+        if which < 2:   # row block b: H/128 gate tiles, then H/128 up tiles
+            t = b * 2 * G + which * G + g
+        else:           # after every gate/up tile: row block b of down, I/128 tiles
+            t = 2 * (I // 16) * G + b * GD + g
+        lane = (r % 16) + 16 * ((c % 32) // 8)
+        word, j = (c % 128) // 32, c % 8
+        off = 1024 * t + 16 * lane + 4 * word
+        w = int.from_bytes(blob[off:off + 4], "little")
+        shift = 4 * (j // 2) if j % 2 == 0 else 16 + 4 * (j // 2)
+        assert (w >> shift) & 0xF == int(Q[r, c]) + 8, (which, r, c)
+        so = 1024 * nt + 32 * t + 2 * (r % 16)
+        assert int.from_bytes(blob[so:so + 2], "little") == int(S[r, g]), (which, r, g)
+        hit[which].add(g)
+    assert hit[0] == hit[1] == set(range(G)) and hit[2] == set(range(GD))
+
+
 # ---------------------------------------------------------------- router
 def test_logits_equal_exact_rational_sum_tiny_layer():
     lay = SyntheticLayer(TINY, seed=0)

@@ -86,6 +86,7 @@ _SIGS = {
     "exmoe_slot_cache_preload": (_i, [_vp, _vp]),
     "exmoe_slot_cache_acquire": (_i, [_vp, _i, _vp, _i, _vp, ctypes.POINTER(ExpertBankC)]),
     "exmoe_slot_cache_table": (_i, [_vp, _i, _vp]),
+    "exmoe_slot_cache_waves": (_i, [_vp, _i, _vp, _i, _i, _vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "exmoe_slot_cache_stats": (_i, [_vp, ctypes.POINTER(CacheStatsC)]),
     "exmoe_slot_cache_reset_stats": (_i, [_vp]),
     "exmoe_slot_cache_destroy": (_i, [_vp]),
@@ -387,6 +388,17 @@ class SlotCache:
         _check(_lib.exmoe_slot_cache_acquire(self._h, layer, ctypes.cast(arr, _vp), len(active),
                                              None if self.dry_run else _stream(), ctypes.byref(bc)))
         return ExpertBank(base=None, stride=bc.stride, expert_to_slot=bc.expert_to_slot, base_ptr=bc.base)
+
+    def waves(self, layer: int, active, run: bool = False):
+        """The cache-sized waves a cached forward on `layer` would run: list of id lists.
+        run=True (dry-run caches only) also looks the waves up, as that forward does."""
+        arr = (ctypes.c_int32 * max(len(active), 1))(*[int(e) for e in active])
+        order = np.empty(max(len(active), 1), dtype=np.int32)
+        n, w = _i(0), _i(0)
+        _check(_lib.exmoe_slot_cache_waves(self._h, layer, ctypes.cast(arr, _vp), len(active), int(run),
+                                           order.ctypes.data, ctypes.byref(n), ctypes.byref(w)))
+        ids = order[:n.value].tolist()
+        return [ids[i:i + w.value] for i in range(0, len(ids), w.value)] if ids else []
 
     def table(self, layer: int) -> np.ndarray:
         out = np.empty(self.E, dtype=np.int32)

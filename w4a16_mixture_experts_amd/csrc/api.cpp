@@ -538,8 +538,6 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   std::vector<int32_t> A(active_ids_host, active_ids_host + n_active);
   for (int e : A)
     if (e < 0 || e >= E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
-  std::sort(A.begin(), A.end());
-  A.erase(std::unique(A.begin(), A.end()), A.end());
   const int path = choose_path(T, H, I, E, k, flags);
   if (path == EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_UNSUPPORTED, "the sequential path does not run in waves");
   if (T == 0) return EXMOE_OK;
@@ -572,10 +570,9 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   // kernels: they wait only for wave w-1's. Per wave: acquire (misses copied), then the
   // expert kernels with a table that maps only this wave's experts; the rows of the other
   // experts are left alone (skipped silently) and written by their own wave.
+  if (layer < 0 || layer >= slot_cache_layers(cache)) return set_error(EXMOE_ERR_CACHE, "layer %d out of range", layer);
   std::vector<int32_t> tbl(E), wave_tbl(E);
-  if ((st = exmoe_slot_cache_table(cache, layer, tbl.data()))) return st;
-  std::stable_partition(A.begin(), A.end(), [&](int e) { return tbl[e] >= 0; });
-  const int W = ((int)A.size() > cS && cS >= 2) ? cS / 2 : cS;
+  const int W = slot_cache_plan_waves(cache, layer, A);
   const int n_waves = ((int)A.size() + W - 1) / W;
   // The layer's slots were last read by the kernels behind the layer's mark, when the cache
   // knows it: the copies of waves 0 and 1 then wait only for those and overlap the kernels

@@ -6,6 +6,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "exmoe.h"
 
@@ -155,12 +156,17 @@ hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s);
 // Experts per layer, slots per layer, dry-run flag and bytes per expert of a slot cache.
 void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry, size_t* expert_bytes);
+int slot_cache_layers(const exmoe_slot_cache* c);
 // exmoe_slot_cache_acquire whose copies wait only for `after` (an event recorded on the
 // compute stream) unless one of them lands in a slot of protect_slots; after == NULL
 // waits for everything enqueued on the compute stream so far (the public behaviour).
 int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
                           hipStream_t compute_stream, hipEvent_t after, const int32_t* protect_slots, int n_protect,
                           exmoe_expert_bank* bank_out);
+// The cache-sized waves of a cached forward: A (any order, duplicates allowed) becomes the
+// distinct ids in wave order (resident first, then the others, each ascending); returns
+// the wave size.
+int slot_cache_plan_waves(const exmoe_slot_cache* c, int layer, std::vector<int32_t>& A);
 // Event i of the cache's pool (created on first use, destroyed with the cache).
 hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev);
 // Per-layer mark of the cached forward: recorded on the compute stream after the last

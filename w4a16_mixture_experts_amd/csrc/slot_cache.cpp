@@ -66,6 +66,8 @@ void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry, size_
   *expert_bytes = c->expert_bytes;
 }
 
+int slot_cache_layers(const exmoe_slot_cache* c) { return c->layers; }
+
 hipError_t slot_cache_event(exmoe_slot_cache* c, int i, hipEvent_t* ev) {
   while ((int)c->wave_ev.size() <= i) {
     hipEvent_t e = nullptr;
@@ -99,6 +101,14 @@ hipError_t slot_cache_mark_layer(exmoe_slot_cache* c, int layer, hipStream_t s) 
   hipError_t r = hipEventRecord(c->layer_ev[layer], s);
   c->layer_ev_ok[layer] = r == hipSuccess;
   return r;
+}
+
+int slot_cache_plan_waves(const exmoe_slot_cache* c, int layer, std::vector<int32_t>& A) {
+  std::sort(A.begin(), A.end());
+  A.erase(std::unique(A.begin(), A.end()), A.end());
+  const int32_t* slot_of = c->slot_of.data() + (size_t)layer * c->E;
+  std::stable_partition(A.begin(), A.end(), [&](int32_t e) { return slot_of[e] >= 0; });
+  return ((int)A.size() > c->S && c->S >= 2) ? c->S / 2 : c->S;
 }
 
 int slot_cache_acquire_ex(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active,
@@ -282,6 +292,32 @@ int exmoe_slot_cache_acquire(exmoe_slot_cache* c, int layer, const int32_t* acti
   if (c) exmoe::slot_cache_forget_layer(c, layer);
   return exmoe::slot_cache_acquire_ex(c, layer, active_ids_host, n_active, compute_stream, nullptr, nullptr, 0,
                                       bank_out);
+}
+
+int exmoe_slot_cache_waves(exmoe_slot_cache* c, int layer, const int32_t* active_ids_host, int n_active, int run,
+                          int32_t* order_out, int* n_distinct, int* wave_size) {
+  if (!c || !order_out || !n_distinct || !wave_size)
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "cache and outputs must not be NULL");
+  if (layer < 0 || layer >= c->layers) return set_error(EXMOE_ERR_CACHE, "layer %d out of range", layer);
+  if (n_active < 0 || (n_active > 0 && !active_ids_host))
+    return set_error(EXMOE_ERR_INVALID_ARGUMENT, "bad active list");
+  if (run && !c->dry) return set_error(EXMOE_ERR_CACHE, "waves run only on a dry-run cache here");
+  std::vector<int32_t> A(active_ids_host, active_ids_host + n_active);
+  for (int e : A)
+    if (e < 0 || e >= c->E) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "expert id %d out of range", e);
+  const int W = exmoe::slot_cache_plan_waves(c, layer, A);
+  if (run) {
+    exmoe_expert_bank bank{};
+    for (size_t w0 = 0; w0 < A.size(); w0 += W) {
+      const int n = (int)std::min(A.size() - w0, (size_t)W);
+      int st = exmoe::slot_cache_acquire_ex(c, layer, A.data() + w0, n, nullptr, nullptr, nullptr, 0, &bank);
+      if (st) return st;
+    }
+  }
+  std::copy(A.begin(), A.end(), order_out);
+  *n_distinct = (int)A.size();
+  *wave_size = W;
+  return EXMOE_OK;
 }
 
 int exmoe_slot_cache_table(const exmoe_slot_cache* c, int layer, int32_t* table_host) {
