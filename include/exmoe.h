@@ -133,9 +133,10 @@ int exmoe_route_weights(const exmoe_bf16* logits, const int32_t* topk_ids, int T
  * Flat index f = t*k + j. expert_offsets int32 [E+1] is the exclusive prefix sum of the
  * per-expert counts (offsets[E] = T*k, unpadded); sorted_flat int32 [T*k] lists, expert by
  * expert ascending and within an expert in ascending f, every f routed there;
- * flat_to_sorted int32 [T*k] is its inverse. Ids outside [0, E) are a caller error: they
- * are counted nowhere and the outputs are then unspecified (no memory is touched out of
- * range). The workspace may be NULL when exmoe_group_workspace_bytes returns 0; it is
+ * flat_to_sorted int32 [T*k] is its inverse. Ids outside [0, E) are a caller error: such a
+ * row is counted nowhere and gets flat_to_sorted = -1, so expert_offsets[E] falls short of
+ * T*k (the expert layer flags that grouping: EXMOE_FLAG_ROWS_UNGROUPED); sorted_flat is
+ * then written only up to expert_offsets[E], and no memory is touched out of range. The workspace may be NULL when exmoe_group_workspace_bytes returns 0; it is
  * (T*k + 1023) / 1024 * E * 4 bytes of device scratch (4-byte aligned) above 4096 routed
  * rows, where the grouping runs in chunks over several workgroups; its contents need no
  * initialization and are not kept.
@@ -178,8 +179,13 @@ enum {
   EXMOE_PATH_SEQUENTIAL = 3, /* per-expert launches in ascending expert order (reference
                                 W4 path; synchronizes once to read the offsets) */
   EXMOE_PATH_MASK = 0xff,
-  EXMOE_WEIGHTS_BF16 = 0x100 /* flag: the bank holds dense bf16 experts (exmoe_bf16_pack);
+  EXMOE_WEIGHTS_BF16 = 0x100, /* flag: the bank holds dense bf16 experts (exmoe_bf16_pack);
                                 paths AUTO, DECODE and PREFILL */
+  EXMOE_FLAG_DEBUG_COUNTERS = 0x200 /* flag: every expert kernel adds the routed rows it ran
+                                to its expert's counter in the workspace header (read with
+                                exmoe_workspace_rows); the exactness check of the abstract's
+                                claim that every selected expert runs and none is pruned or
+                                substituted (Fig. 1: all routed rows, grouped by expert) */
 };
 
 size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, int flags);
@@ -202,14 +208,28 @@ int exmoe_moe_forward(const exmoe_bf16* x, const int32_t* topk_ids, const float*
 size_t exmoe_moe_layer_workspace_bytes(int T, int H, int I, int E, int k, int flags);
 
 /* Conditions the expert kernels recorded in a workspace of exmoe_moe_forward,
- * exmoe_moe_layer or exmoe_moe_forward_cached, since it was cleared. Bit 0
- * (EXMOE_FLAG_EXPERT_WITHOUT_SLOT): a routed expert had no slot (expert_to_slot = -1),
- * its rows were skipped and the output of the tokens routed to it is undefined. Reads the
- * word after the work already enqueued on `stream` (host-synchronous: the stream is
- * synchronized) into *flags_out, then clears it when clear != 0. workspace: device,
- * ws_bytes >= 4096. */
-enum { EXMOE_FLAG_EXPERT_WITHOUT_SLOT = 1 };
+ * exmoe_moe_layer or exmoe_moe_forward_cached, since it was cleared (abstract: no selected
+ * expert may be skipped; these report a call where one was). Bit 0
+ * (EXMOE_FLAG_EXPERT_WITHOUT_SLOT): a routed expert had no slot (expert_to_slot = -1), or
+ * was missing from the active list of a cached forward of several waves; its rows were
+ * skipped and the output of the tokens routed to it is undefined. Bit 1
+ * (EXMOE_FLAG_ROWS_UNGROUPED): the grouping did not cover every routed row
+ * (expert_offsets[E] != T*k, e.g. an id outside [0, E) in exmoe_group_tokens); those
+ * rows' outputs are undefined. Reads the word after the work already enqueued on `stream`
+ * (host-synchronous: the stream is synchronized) into *flags_out, then clears it when
+ * clear != 0. workspace: device, ws_bytes >= 4096. */
+enum { EXMOE_FLAG_EXPERT_WITHOUT_SLOT = 1, EXMOE_FLAG_ROWS_UNGROUPED = 2 };
 int exmoe_workspace_flags(void* workspace, size_t ws_bytes, int clear, uint32_t* flags_out, hipStream_t stream);
+
+/* Exactness counters (abstract and Fig. 1: every selected expert runs on all of its routed
+ * rows). With EXMOE_FLAG_DEBUG_COUNTERS in a call's flags, the kernel that finishes a
+ * routed row (the down projection) adds it to its expert's int32 counter in the
+ * workspace header; a call that ran every routed row exactly once adds
+ * expert_offsets[e+1] - expert_offsets[e] to counter e. The counters accumulate over calls
+ * until cleared; a zero-filled workspace starts them at zero. Copies counters 0..E-1 to
+ * rows_out (host, E ints) after the work enqueued on `stream` (synchronizes), then zeroes
+ * them when clear != 0. workspace: device, ws_bytes >= 4096; 1 <= E <= 256. */
+int exmoe_workspace_rows(void* workspace, size_t ws_bytes, int E, int clear, int32_t* rows_out, hipStream_t stream);
 int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
                     const exmoe_expert_bank* bank, int T, int H, int I, int E, int k,
                     int renormalize, int flags, exmoe_bf16* logits, int32_t* topk_ids,
@@ -296,7 +316,8 @@ int exmoe_slot_cache_destroy(exmoe_slot_cache* cache);
  * exmoe_moe_workspace_bytes (the per-wave expert->slot table lives there). A routed
  * expert missing from the list: in a one-wave call it is computed if it happens to be
  * resident, else flagged (exmoe_workspace_flags) and its rows are left unwritten; in a
- * call of several waves its rows are left unwritten. The host returns once every wave is
+ * call of several waves its rows are left unwritten and a check after the last wave
+ * flags it (EXMOE_FLAG_EXPERT_WITHOUT_SLOT). The host returns once every wave is
  * enqueued, without waiting for the GPU (a per-wave table travels in the arguments of a
  * one-workgroup kernel). Calls on one cache must come from one host thread. */
 int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,

@@ -298,37 +298,6 @@ def test_olmoe_prefill_zipf(exm, olmoe, T):
         check_y(got["y"], ref["y"], f"prefill T={T} path={path}")
 
 
-# ------------------------------------------------------------------ large-expert prefill
-def test_large_prefill_sampled(exm):
-    """Full-size large-expert layer (hidden 4096, 8 experts, top-2, intermediate 14336,
-    4096 tokens) in the benchmark's launch configuration; the oracle checks routing on
-    every token and the output on sampled tokens one by one."""
-    log("large prefill: building 8 experts (hidden 4096, intermediate 14336)")
-    lay = Layer(LARGE, seed=0, oracle_experts=False)
-    T = 4096
-    x = lay.syn.x(T)
-    got = run_layer(exm, lay, x)
-    logits = oracle.router_logits(x, lay.wr_bits)
-    ids = oracle.topk_ids(logits, LARGE.k)
-    w = oracle.topk_weights(logits, ids)
-    off, sf, fs = oracle.group_tokens(ids, LARGE.E)
-    check_routing(got, dict(logits=logits, ids=ids, weights=w, offsets=off, sorted_flat=sf, flat_to_sorted=fs),
-                  "large")
-    # sampled tokens: the first, the last and four more whose experts are among theirs
-    S = set(int(e) for e in ids[0]) | set(int(e) for e in ids[T - 1])
-    cand = [t for t in range(1, T - 1) if set(int(e) for e in ids[t]) <= S]
-    rng = np.random.default_rng(0)
-    sample = [0, T - 1] + [int(t) for t in rng.choice(cand, 4, replace=False)]
-    need = sorted(S)
-    log(f"  oracle on tokens {sample} (experts {need})")
-    experts = [None] * LARGE.E
-    for e in need:
-        experts[e] = oracle.quantize_expert(*lay.syn.expert(e))
-    from oracle.quant import bf16_bits_to_f64
-    y_ref = oracle.forward_per_token(bf16_bits_to_f64(x), ids, w, experts, tokens=sample)
-    check_y(got["y"][sample], y_ref, "large sampled")
-
-
 # ------------------------------------------------------------------ slot cache
 def test_slot_cache_outputs_equal_resident(exm):
     """A 3-layer stack through a 3-slot cache: outputs bitwise equal to the fully resident

@@ -111,7 +111,7 @@ def test_forward_validation_errors():
     assert _fwd(x=None) == E_INV and "x" in exm.last_error()
     assert _fwd(x=FAKE + 2) == E_INV and "aligned" in exm.last_error()
     assert _fwd(flags=7) == E_INV
-    assert _fwd(flags=1 << 9) == E_INV
+    assert _fwd(flags=1 << 10) == E_INV      # 0x100 and 0x200 are flags; 0x400 is not
     assert _fwd(bank=_bank(stride=100)) == E_INV
     assert _fwd(bank=_bank(base=None)) == E_INV
     need = exm.moe_workspace_bytes(4, 256, 256, 8, 2)

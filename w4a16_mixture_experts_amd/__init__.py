@@ -40,6 +40,7 @@ ERR_CACHE = -6
 
 PATH_AUTO, PATH_DECODE, PATH_PREFILL, PATH_SEQUENTIAL = 0, 1, 2, 3
 WEIGHTS_BF16 = 0x100       # flag: the bank holds dense bf16 experts (bf16_pack)
+DEBUG_COUNTERS = 0x200     # flag: expert kernels count the rows they ran per expert (workspace_rows)
 CACHE_DRY_RUN = 1
 
 _vp = ctypes.c_void_p
@@ -73,6 +74,7 @@ _SIGS = {
     "exmoe_moe_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "exmoe_bf16_expert_bytes": (_sz, [_i, _i]),
     "exmoe_workspace_flags": (_i, [_vp, _sz, _i, ctypes.POINTER(ctypes.c_uint32), _vp]),
+    "exmoe_workspace_rows": (_i, [_vp, _sz, _i, _i, _vp, _vp]),
     "exmoe_bf16_pack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _sz]),
     "exmoe_moe_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _sz, _vp]),
@@ -285,6 +287,7 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 
 FLAG_EXPERT_WITHOUT_SLOT = 1
+FLAG_ROWS_UNGROUPED = 2
 
 
 def workspace_flags(workspace, clear: bool = True) -> int:
@@ -293,6 +296,14 @@ def workspace_flags(workspace, clear: bool = True) -> int:
     v = ctypes.c_uint32(0)
     _check(_lib.exmoe_workspace_flags(_ptr(workspace), workspace.numel(), int(clear), ctypes.byref(v), _stream()))
     return v.value
+
+
+def workspace_rows(workspace, E: int, clear: bool = True) -> np.ndarray:
+    """Per-expert counters of routed rows run since the last clear (DEBUG_COUNTERS calls);
+    synchronizes the current stream."""
+    out = np.empty(E, dtype=np.int32)
+    _check(_lib.exmoe_workspace_rows(_ptr(workspace), workspace.numel(), E, int(clear), out.ctypes.data, _stream()))
+    return out
 
 
 def moe_forward(x, ids, weights, offsets, sorted_flat, flat_to_sorted, bank: ExpertBank, I: int,

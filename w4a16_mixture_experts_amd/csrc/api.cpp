@@ -381,10 +381,13 @@ static int choose_path(int T, int H, int I, int E, int k, int flags) {
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace header: routing arrival counters (one per 256-byte line, so that their atomics
-// do not serialize on one cache line) and a debug word.
-constexpr size_t kWsHeaderBytes = 4096, kWsCounterOffset = 0, kWsDebugOffset = 2048;
+// do not serialize on one cache line), a debug word, and the per-expert row counters of
+// EXMOE_FLAG_DEBUG_COUNTERS.
+constexpr size_t kWsHeaderBytes = 4096, kWsCounterOffset = 0, kWsDebugOffset = 2048, kWsRowsOffset = 3072;
 static_assert(kWsCounterOffset + (size_t)kRouteSelCounters * kRouteCounterStride * 4 <= kWsDebugOffset,
               "counters overlap the debug word");
+static_assert(kWsRowsOffset + 4 * (size_t)kMaxExperts <= kWsHeaderBytes && kWsDebugOffset + 4 <= kWsRowsOffset,
+              "row counters outside the header");
 
 namespace exmoe {
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws) {
@@ -423,6 +426,7 @@ size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs
     a->nparts = nparts;
     a->counters = reinterpret_cast<uint32_t*>(b + kWsCounterOffset);
     a->debug = reinterpret_cast<uint32_t*>(b + kWsDebugOffset);
+    a->rows_ctr = nullptr;   // set by the entry point when EXMOE_FLAG_DEBUG_COUNTERS is given
   }
   return off;
 }
@@ -436,7 +440,7 @@ extern "C" size_t exmoe_moe_workspace_bytes(int T, int H, int I, int E, int k, i
 static int check_flags(int flags) {
   const int path = flags & EXMOE_PATH_MASK;
   if (path > EXMOE_PATH_SEQUENTIAL) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
-  if (flags & ~(EXMOE_PATH_MASK | EXMOE_WEIGHTS_BF16))
+  if (flags & ~(EXMOE_PATH_MASK | EXMOE_WEIGHTS_BF16 | EXMOE_FLAG_DEBUG_COUNTERS))
     return set_error(EXMOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   if ((flags & EXMOE_WEIGHTS_BF16) && path == EXMOE_PATH_SEQUENTIAL)
     return set_error(EXMOE_ERR_UNSUPPORTED, "bf16 experts run on the decode and prefill paths only");
@@ -455,6 +459,12 @@ static int validate_bank(const exmoe_expert_bank* bank, int H, int I, int flags)
   return EXMOE_OK;
 }
 
+static void set_row_counters(MoeArgs& a, void* workspace, int flags) {
+  a.rows_ctr = (flags & EXMOE_FLAG_DEBUG_COUNTERS)
+                   ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kWsRowsOffset)
+                   : nullptr;
+}
+
 static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
                             const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
                             const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int flags, exmoe_bf16* y,
@@ -465,6 +475,7 @@ static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const 
   a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
   a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
   moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
+  set_row_counters(a, workspace, flags);
   if (flags & EXMOE_WEIGHTS_BF16) {
     a.part = nullptr;   // no sliced partial outputs: y_perm and the plain combine
     a.nparts = 0;
@@ -556,6 +567,7 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
   a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
   a.flat_to_sorted = flat_to_sorted; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
   moe_workspace_layout(T, H, I, E, k, path, &a, workspace);
+  set_row_counters(a, workspace, flags);
   const bool bf16w = (flags & EXMOE_WEIGHTS_BF16) != 0;
   if (bf16w) {
     a.part = nullptr;
@@ -633,6 +645,13 @@ int exmoe_moe_forward_cached(const exmoe_bf16* x, const int32_t* topk_ids, const
     }
   }
   EXMOE_HIP(slot_cache_mark_layer(cache, layer, stream));
+  if (n_waves > 1) {
+    // each wave skipped the experts outside it silently: an expert with rows that no wave
+    // held (missing from the caller's list) is flagged here
+    uint32_t mask[kMaxExperts / 32] = {};
+    for (int e : A) mask[e >> 5] |= 1u << (e & 31);
+    EXMOE_HIP(check_wave_union(expert_offsets, E, mask, a.debug, stream));
+  }
   EXMOE_HIP(launch_combine(a, stream));
   return EXMOE_OK;
 }
@@ -649,6 +668,22 @@ int exmoe_workspace_flags(void* workspace, size_t ws_bytes, int clear, uint32_t*
   if (clear && v) {
     const uint32_t zero = 0;
     EXMOE_HIP(hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, stream));
+    EXMOE_HIP(hipStreamSynchronize(stream));
+  }
+  return EXMOE_OK;
+}
+
+int exmoe_workspace_rows(void* workspace, size_t ws_bytes, int E, int clear, int32_t* rows_out, hipStream_t stream) {
+  if (!workspace || !rows_out) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "workspace and rows_out must not be NULL");
+  if (E < 1 || E > kMaxExperts) return set_error(EXMOE_ERR_INVALID_ARGUMENT, "E must be in [1, 256]");
+  if (ws_bytes < kWsHeaderBytes)
+    return set_error(EXMOE_ERR_WORKSPACE, "workspace of %zu bytes has no %zu-byte header", ws_bytes, kWsHeaderBytes);
+  uint8_t* rows = static_cast<uint8_t*>(workspace) + kWsRowsOffset;
+  EXMOE_HIP(hipMemcpyAsync(rows_out, rows, sizeof(int32_t) * E, hipMemcpyDeviceToHost, stream));
+  EXMOE_HIP(hipStreamSynchronize(stream));
+  if (clear) {
+    static const int32_t zeros[kMaxExperts] = {};
+    EXMOE_HIP(hipMemcpyAsync(rows, zeros, sizeof(int32_t) * E, hipMemcpyHostToDevice, stream));
     EXMOE_HIP(hipStreamSynchronize(stream));
   }
   return EXMOE_OK;
@@ -692,6 +727,7 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
     a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
     moe_workspace_layout(T, H, I, E, k, EXMOE_PATH_DECODE, &a, workspace);
+    set_row_counters(a, workspace, flags);
     if (decode_table_routing_ok(T, H, E, k)) {
       EXMOE_HIP(launch_route_sel(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids, topk_weights,
                                  a.sel, a.counters, stream));

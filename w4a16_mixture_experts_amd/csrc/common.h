@@ -81,6 +81,10 @@ hipError_t span_fill(unsigned long long* p, int n, hipStream_t s);
 // dst[0..n) = host[0..n) (n <= kMaxExperts) by a one-workgroup kernel that takes the values
 // as kernel arguments: ordered on s, and the host buffer may be reused when the call returns.
 hipError_t table_upload(int32_t* dst, const int32_t* host, int n, hipStream_t s);
+// After the waves of a cached forward: flags (bit 0 of *debug) every expert with a
+// non-empty segment whose bit is clear in mask (the union of the waves' experts).
+hipError_t check_wave_union(const int32_t* offsets, int E, const uint32_t mask[kMaxExperts / 32], uint32_t* debug,
+                            hipStream_t s);
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                                int E, uint16_t* logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
@@ -119,6 +123,8 @@ struct MoeArgs {
   int skip_absent;    // experts without a slot are skipped silently (one wave of a cached forward)
   int32_t* wave_table;  // int32 [E] workspace: the expert->slot table of one wave
   int32_t* group_ws;    // chunk counts of the grouping of more than 4096 rows
+  int32_t* rows_ctr;    // int32 [E] in the workspace header: rows executed per expert
+                        // (EXMOE_FLAG_DEBUG_COUNTERS), or null
 };
 
 size_t moe_workspace_layout(int T, int H, int I, int E, int k, int path, MoeArgs* a, void* ws);

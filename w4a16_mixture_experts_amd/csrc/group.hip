@@ -117,6 +117,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_scatter_kernel(const int3
     for (int w = 0; w < wave; w++) pos += wavecnt[w][e];
     sorted_flat[pos] = f;
     flat_to_sorted[f] = pos;
+  } else if (f < n) {
+    flat_to_sorted[f] = -1;   // id outside [0, E): in no segment
   }
 }
 

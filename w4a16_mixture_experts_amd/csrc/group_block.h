@@ -92,6 +92,8 @@ __device__ __forceinline__ void group_block(const int32_t* ids, int n, int E, in
       for (int w = 0; w < wave; w++) pos += gs.wave[w][e];
       sorted_flat[pos] = f;
       flat_to_sorted[f] = pos;
+    } else if (f < n) {
+      flat_to_sorted[f] = -1;   // id outside [0, E): in no segment
     }
     __syncthreads();
     for (int e2 = tid; e2 < E; e2 += kThreads) {

@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(MoeArgs a, int 
       }
     }
   }
+  if (!GATEUP && a.rows_ctr && chunk == 0 && tid == 0) atomicAdd(a.rows_ctr + e, cnt);   // exactness counter
   span_end(a.span);
 }
 

@@ -532,6 +532,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
     }
     __syncthreads();   // pass row list and reduction space free for the next pass
   }
+  // exactness counter: the down projection's first chunk counts the rows it wrote
+  if (!GATEUP && a.rows_ctr && chunk == 0 && tid == 0) atomicAdd(a.rows_ctr + ex.e, ex.cnt);
   span_end(a.span);
 }
 
@@ -809,6 +811,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     }
     __syncthreads();   // pass row list and LDS free for the next pass
   }
+  // exactness counter: the rows this expert ran (once per row: slice 0 counts them)
+  if (a.rows_ctr && cs == 0 && tid == 0) atomicAdd(a.rows_ctr + ex.e, ex.cnt);
   span_end(a.span);
 }
 
@@ -952,6 +956,7 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
       if (f >= 0) *reinterpret_cast<float4*>(prow + r * 16) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
+  if (a.rows_ctr && cs == 0 && tid == 0) atomicAdd(a.rows_ctr + ex.e, ex.cnt);   // exactness counter
   span_end(a.span);
 }
 
@@ -961,9 +966,17 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
 // Workgroup = (token, 256 M float4 columns: grid x = token, y = column block); thread = M float4 columns 256 apart (every
 // load instruction of the workgroup covers 4 KiB in a row), with 16 / M slots of them in
 // flight at a time. M = 4 for many tokens (fewer, longer workgroups), 1 for few.
+// A grouping that misses rows (an id outside [0, E) counted nowhere: offsets[E] < T k)
+// leaves their outputs unwritten; the combine's first thread records it.
+__device__ __forceinline__ void check_grouped_rows(const MoeArgs& a) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.offsets[a.E] != a.T * a.k)
+    atomicOr(a.debug, (uint32_t)EXMOE_FLAG_ROWS_UNGROUPED);
+}
+
 template <int M>
 __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
   span_begin(a.span);
+  check_grouped_rows(a);
   const int t = blockIdx.x;
   const int nv = a.H >> 2;                               // float4 per row
   const int q0 = blockIdx.y * (256 * M) + (int)threadIdx.x;
@@ -1011,6 +1024,7 @@ constexpr int kCombCols = 128;
 __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
   __shared__ float4 red[kMaxK][kCombCols / 4];
   span_begin(a.span);
+  check_grouped_rows(a);
   const int t = blockIdx.y;
   const int col0 = blockIdx.x * kCombCols;
   const size_t slice = (size_t)a.T * a.k * a.H;
@@ -1063,6 +1077,7 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
 template <int NP>
 __global__ __launch_bounds__(256) void combine_parts_tok_kernel(MoeArgs a) {
   span_begin(a.span);
+  check_grouped_rows(a);
   const int t = blockIdx.x;
   const int q4 = blockIdx.y * 256 + (int)threadIdx.x;   // float4 column
   if (q4 < (a.H >> 2)) {

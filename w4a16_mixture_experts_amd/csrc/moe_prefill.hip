@@ -401,6 +401,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
           }
         }
       }
+    // exactness counter: the first row tile of each token tile counts the tile's rows
+    if (a.rows_ctr && rt == 0 && tid == 0) atomicAdd(a.rows_ctr + pt.e, min(kPfBN, pt.cnt - pt.tok0));
   }
   span_end(a.span);
 }

@@ -44,6 +44,27 @@ hipError_t table_upload(int32_t* dst, const int32_t* host, int n, hipStream_t s)
   return hipGetLastError();
 }
 
+// Every expert with rows must have been in one of the waves (mask bit set); otherwise its
+// rows were never computed and the output of its tokens is undefined: flag it.
+struct WaveMaskArg {
+  uint32_t m[kMaxExperts / 32];
+};
+
+__global__ __launch_bounds__(kMaxExperts) void wave_union_kernel(const int32_t* __restrict__ offsets, int E, WaveMaskArg mk,
+                                                                 uint32_t* __restrict__ debug) {
+  const int e = threadIdx.x;
+  if (e < E && offsets[e + 1] > offsets[e] && !((mk.m[e >> 5] >> (e & 31)) & 1u))
+    atomicOr(debug, (uint32_t)EXMOE_FLAG_EXPERT_WITHOUT_SLOT);
+}
+
+hipError_t check_wave_union(const int32_t* offsets, int E, const uint32_t mask[kMaxExperts / 32], uint32_t* debug,
+                            hipStream_t s) {
+  WaveMaskArg mk;
+  for (int i = 0; i < kMaxExperts / 32; i++) mk.m[i] = mask[i];
+  hipLaunchKernelGGL(wave_union_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, E, mk, debug);
+  return hipGetLastError();
+}
+
 }  // namespace exmoe
 
 using namespace exmoe;
