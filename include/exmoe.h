@@ -237,6 +237,23 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
                     int32_t* flat_to_sorted, exmoe_bf16* y, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
+/* exmoe_moe_layer for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same call without a
+ * workspace argument. It allocates nothing: its workspace is a fixed 64 MiB array in the
+ * library's device code (one copy per GPU, held until the process ends), which serves
+ * every call whose exmoe_moe_layer_workspace_bytes(T, H, I, E, k, flags) is at most 64 MiB
+ * (e.g. OLMoE-shaped layers up to about 700 tokens); a larger call fails with
+ * EXMOE_ERR_UNSUPPORTED before anything is enqueued. EXMOE_FLAG_DEBUG_COUNTERS is
+ * EXMOE_ERR_UNSUPPORTED (no workspace to read the counters from). Results are those of
+ * exmoe_moe_layer, bit for bit. The caller still passes every input and output buffer.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU
+ * (different streams, or host threads) race and must not be issued. */
+int exmoe_moe_layer_noalloc(const exmoe_bf16* x, const exmoe_bf16* w_router, const float* logit_bias,
+                            const exmoe_expert_bank* bank, int T, int H, int I, int E, int k,
+                            int renormalize, int flags, exmoe_bf16* logits, int32_t* topk_ids,
+                            float* topk_weights, int32_t* expert_offsets, int32_t* sorted_flat,
+                            int32_t* flat_to_sorted, exmoe_bf16* y, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Slot cache (host policy + asynchronous host-to-device copies). Abstract, Fig. 1, Fig. 2
  * and Tab. 1: a pinned host pool keeps every packed expert; a GPU cache of a configurable

@@ -83,6 +83,8 @@ _SIGS = {
     "exmoe_moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "exmoe_moe_layer": (_i, [_vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i, _i,
                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "exmoe_moe_layer_noalloc": (_i, [_vp, _vp, _vp, ctypes.POINTER(ExpertBankC), _i, _i, _i, _i, _i, _i, _i,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "exmoe_slot_cache_create": (_i, [_i, _i, _i, _sz, _i, ctypes.POINTER(_vp)]),
     "exmoe_slot_cache_host_slot": (_i, [_vp, _i, _i, ctypes.POINTER(_vp)]),
     "exmoe_slot_cache_preload": (_i, [_vp, _vp]),
@@ -349,6 +351,21 @@ def moe_layer(x, w_router, bank: ExpertBank, I: int, k: int, bias=None, renormal
                                 int(renormalize), flags, _ptr(b.logits), _ptr(b.ids), _ptr(b.weights), _ptr(b.offsets),
                                 _ptr(b.sorted_flat), _ptr(b.flat_to_sorted), _ptr(b.y), _ptr(b.workspace),
                                 b.workspace.numel(), _stream() if stream is None else stream))
+    return b
+
+
+def moe_layer_noalloc(x, w_router, bank: ExpertBank, I: int, k: int, buffers: LayerBuffers, bias=None,
+                      renormalize: bool = True, flags: int = PATH_AUTO):
+    """moe_layer without a workspace (the library's fixed per-GPU array serves as one):
+    every output goes to the preallocated `buffers` (its workspace is not used)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    b = buffers
+    bc = bank.c()
+    _check(_lib.exmoe_moe_layer_noalloc(_ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(bc), T, H, I, E, k,
+                                        int(renormalize), flags, _ptr(b.logits), _ptr(b.ids), _ptr(b.weights),
+                                        _ptr(b.offsets), _ptr(b.sorted_flat), _ptr(b.flat_to_sorted), _ptr(b.y),
+                                        _stream()))
     return b
 
 
