@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Summaries of rocprofv3 output for the library's kernels (standard library only).
 
-    python3 w4a16_mixture_experts_amd/profiling.py stats  DIR --cmd "..." --out FILE
-    python3 w4a16_mixture_experts_amd/profiling.py traffic --kernel decode_gateup_kernel \\
+    python3 rocprof_summary.py stats  DIR --cmd "..." --out FILE
+    python3 rocprof_summary.py traffic --kernel decode_fused_kernel \\
         --fetch DIR --write DIR --copy-bytes N --cmd "..." --out FILE
+    python3 rocprof_summary.py counters DIR --counter NAME ... --cmd "..." --out FILE
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` run into a per-kernel table (calls,
 average, median, min, max and total duration). `traffic` turns two `rocprofv3 --pmc`
@@ -12,7 +13,10 @@ launch of one kernel. Each counter is scaled by the ratio between the known traf
 `exmoe::copy_kernel` (N bytes read and N bytes written per dispatch, N larger than the
 on-package caches) and what the same counter reads for that copy in the same run. The
 traffic file records a hash of the kernel's sources; `read_traffic` returns nothing once
-the sources have changed since the counters were taken.
+the sources have changed since the counters were taken. `stats` files record the same
+hash for the kernels named in KERNEL_SOURCES, and `read_kernel_avg` returns a kernel's
+average launch duration from such a file under the same rule. Measurement tooling only:
+nothing in the library imports it; bench.py reads the committed summaries through it.
 """
 from __future__ import annotations
 
@@ -25,12 +29,13 @@ import sqlite3
 import statistics
 import sys
 
-CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4a16_mixture_experts_amd", "csrc")
 
 # Sources each profiled kernel is compiled from.
 KERNEL_SOURCES = {
     "decode_expert_kernel": ["moe_decode.hip", "device.h", "common.h"],
     "decode_fused_kernel": ["moe_decode.hip", "device.h", "common.h"],
+    "decode_narrow_kernel": ["moe_decode.hip", "device.h", "common.h"],
     "prefill_kernel": ["moe_prefill.hip", "device.h", "common.h"],
 }
 
@@ -108,7 +113,8 @@ def _ours(name: str) -> bool:
                                   "decode_fused_kernel", "combine_parts_kernel", "combine_parts_tok_kernel", "route_sel_kernel",
                                   "route_logits_mfma_kernel",
                                   "decode_narrow_kernel", "bf16_decode_kernel", "group_count_kernel",
-                                  "group_scan_kernel", "group_scatter_kernel", "table_fill_kernel", "span_fill_kernel")
+                                  "group_scan_kernel", "group_scatter_kernel", "table_fill_kernel", "span_fill_kernel",
+                                  "wave_union_kernel")
 
 
 def _match(values: dict[str, list[float]], kernel: str) -> list[float]:
@@ -124,7 +130,8 @@ def cmd_stats(args):
     durs = kernel_durations(args.dir)
     lines = [f"# rocprofv3 kernel-trace summary: {args.title}", f"# command: {args.cmd}",
              "# one row per (kernel, launch grid in workgroups x workgroup size); durations in",
-             "# microseconds per launch; library kernels first, then the rest", "",
+             "# microseconds per launch; library kernels first, then the rest",
+             "# sources: " + " ".join(f"{k}={source_hash(k)}" for k in sorted(KERNEL_SOURCES)), "",
              f"{'kernel':44s} {'grid':>16s} {'calls':>7s} {'avg':>9s} {'median':>9s} {'min':>9s} {'max':>9s} "
              f"{'total_ms':>9s}"]
     order = sorted(durs.items(), key=lambda kv: (not _ours(kv[0][0]), -sum(kv[1])))
@@ -193,6 +200,30 @@ def read_traffic(path: str, kernel: str):
         return None
     return {"bytes": float(kv["traffic_bytes_per_launch"]), "fetch_factor": float(kv["fetch_factor"]),
             "write_factor": float(kv["write_factor"]), "source_sha256": kv["source_sha256"]}
+
+
+def read_kernel_avg(path: str, kernel: str, grid: str):
+    """(average, median, calls) in microseconds of one (kernel, grid) row of a `stats` file,
+    or None when the file is missing, has no such row, or the kernel's sources changed
+    since the trace was taken. kernel is the row's name up to its template arguments' end,
+    e.g. 'decode_fused_kernel<2, true, 16>'; grid e.g. '257x1x1 wg1024'."""
+    if not os.path.exists(path):
+        return None
+    base = kernel.split("<")[0]
+    with open(path) as fh:
+        lines = fh.read().splitlines()
+    src = [ln for ln in lines if ln.startswith("# sources:")]
+    if base in KERNEL_SOURCES:
+        want = f"{base}={source_hash(base)}"
+        if not src or want not in src[0].split():
+            return None
+    for ln in lines:
+        if ln.startswith("#") or not ln.startswith(kernel):
+            continue
+        rest = ln[len(kernel):].split()
+        if len(rest) >= 6 and f"{rest[0]} {rest[1]}" == grid:
+            return float(rest[3]), float(rest[4]), int(rest[2])
+    return None
 
 
 def _emit(text: str, out: str | None):

@@ -132,6 +132,29 @@ __device__ __forceinline__ void dec_prestage_x(const MoeArgs& a, DecLDS& L) {
   for (int m = 0; m < SQ; m++) *reinterpret_cast<uint4*>(L.xs + dst[m]) = v[m];
 }
 
+// The same staging straight from memory into LDS (global_load_lds, 16 bytes per lane): no
+// registers are held, so the first weight ring can be issued behind these loads at once.
+// Wave w copies staging rows w, w + NW, ... (kDecTok rows); a wave-wide copy moves 512
+// consecutive activations. The count is fixed (kDecTok / NW rows x kDecKC / 512 copies per
+// wave), with no branch: rows past T copy token T - 1 and columns past H copy the row's
+// last 8 values, into staging positions nothing reads. The caller waits for completion
+// (the copies count in vmcnt, in issue order) and synchronizes the workgroup before
+// reading the rows.
+template <int NW>
+__device__ __forceinline__ void dec_dma_x(const MoeArgs& a, DecLDS& L, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kDecTok / NW; i++) {
+    const int r = wave + i * NW;
+    const uint16_t* src = a.x + (size_t)(r < a.T ? r : a.T - 1) * a.H;
+#pragma unroll
+    for (int c0 = 0; c0 < kDecKC; c0 += 512) {
+      const int c = c0 + 8 * lane < a.H ? c0 + 8 * lane : a.H - 8;
+      __builtin_amdgcn_global_load_lds(src + c, (__attribute__((address_space(3))) void*)(L.xs + r * kDecXS + c0), 16,
+                                       0, 0);
+    }
+  }
+}
+
 // Publisher of a table-routed launch (the grid's last workgroup): stable grouping of the
 // ids the routing kernel wrote, into the caller's offsets / sorted_flat / flat_to_sorted.
 template <int NT>
@@ -645,7 +668,11 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     dec_publish<NT>(a, L, pub);
     return;
   }
-  if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  // every token row of x straight into LDS; with every expert launched the first weight
+  // ring goes out right behind those copies
+  if (kSelAll) dec_dma_x<NW>(a, L, wave, lane);
+  else if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  __builtin_amdgcn_sched_barrier(0);
   WSlot2 W[kDecRing];
   __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
   if (ALL) {
@@ -654,6 +681,14 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
                                              slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
+  }
+  if (kSelAll) {
+    // the activation copies are older than the 4 x 4 ring loads: vmcnt(16) is their
+    // completion (expcnt and lgkmcnt left at their maxima); the barrier below (token list)
+    // publishes every wave's rows
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x4F70);
+    static_assert(kDecRing * 4 == 16, "the wait above counts 16 ring loads");
   }
   DecExpert ex;
   if (kSelAll) {
