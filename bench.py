@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16", "batched"],
                     default=None,
                     help="run a single workload (for profiling)")
+    ap.add_argument("--prefill-tokens", type=int, nargs="+", default=[128, 512, 2048],
+                    help="token counts of the Zipf-biased OLMoE-shaped prefill lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (traffic-counter calibration)")
     return ap.parse_args()
@@ -807,7 +809,7 @@ def main():
 
     if not args.no_secondary and args.only in (None, "prefill"):
         bias = olmoe_syn.zipf_bias()
-        for T in (128, 512, 2048):
+        for T in args.prefill_tokens:
             secondary[f"olmoe_prefill_zipf_T{T}"] = run_prefill(f"olmoe_prefill_zipf_T{T}", OLMOE, olmoe_syn,
                                                                 banks[:2], wr, T, bias, 20, 3)
     if banks is not None:

@@ -354,3 +354,49 @@ def test_ungrouped_rows_flagged(exm, tiny_bf16, path):
     exm.moe_forward(x, ids, w, off, sf, fs, lay.bank, lay.shape.I, flags=path | exm.DEBUG_COUNTERS, workspace=ws)
     assert exm.workspace_flags(ws) == exm.FLAG_ROWS_UNGROUPED
     assert np.array_equal(exm.workspace_rows(ws, E), ref_counts)
+
+
+# ------------------------------------------------------------------ whole-layer call against the separate calls
+@pytest.mark.parametrize("T", [4, 5, 16])
+def test_table_routed_layer_equals_separate_calls(exm, olmoe_packed, T):
+    """The whole-layer call at decode sizes routes through the routing kernel's expert table
+    (its fused expert kernel stages every token row, the 16-token case by direct copies
+    into LDS); the same routing through the separate calls groups first and runs the
+    fused kernel on the given grouping. Both outputs are equal bit for bit, and a second
+    whole-layer call on the same workspace repeats them."""
+    import torch
+    lay = olmoe_packed
+    s = lay.shape
+    x_bits = lay.syn.x(T, stream=300 + T)
+    x = to_dev_bf16(x_bits)
+    out = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k)
+    y_sep = exm.moe_forward(x, out.ids, out.weights, out.offsets, out.sorted_flat, out.flat_to_sorted, lay.bank, s.I)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(out.y), bf16_dev_to_bits(y_sep))
+    again = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k, buffers=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(again.y), bf16_dev_to_bits(y_sep)), "second call on the same workspace differs"
+
+
+def test_slotless_expert_leaves_workspace_clean(exm, olmoe_packed):
+    """A routed expert without a slot in a whole-layer call: flagged, its tokens' outputs
+    are undefined, and the workspace's persistent state (arrival counters, flag word once
+    read) is left clean: the next call on the same workspace equals a call on a fresh one
+    bit for bit."""
+    import torch
+    lay = olmoe_packed
+    s = lay.shape
+    x = to_dev_bf16(lay.syn.x(16, stream=400))
+    ref = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k)
+    torch.cuda.synchronize()
+    gone = int(ref.ids[3, 0])
+    table = torch.arange(s.E, dtype=torch.int32, device="cuda")
+    table[gone] = -1
+    holed = exm.ExpertBank(base=lay.bank.base, stride=lay.bank.stride, expert_to_slot=table)
+    b = exm.LayerBuffers(16, s.H, s.I, s.E, s.k)
+    exm.moe_layer(x, lay.wr, holed, s.I, s.k, buffers=b)
+    assert exm.workspace_flags(b.workspace) == exm.FLAG_EXPERT_WITHOUT_SLOT
+    exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k, buffers=b)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(b.y), bf16_dev_to_bits(ref.y))
+    assert exm.workspace_flags(b.workspace) == 0

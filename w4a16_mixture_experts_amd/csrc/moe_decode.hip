@@ -1111,6 +1111,7 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
 // ones of combine_parts_kernel.
 template <int NP>
 __global__ __launch_bounds__(256) void combine_parts_tok_kernel(MoeArgs a) {
+#pragma clang fp contract(off)   // the slot sum times the weight is rounded before it is added
   span_begin(a.span);
   check_grouped_rows(a);
   const int t = blockIdx.x;
@@ -1137,8 +1138,8 @@ __global__ __launch_bounds__(256) void combine_parts_tok_kernel(MoeArgs a) {
             sj.x += v[u][q].x; sj.y += v[u][q].y; sj.z += v[u][q].z; sj.w += v[u][q].w;
           }
           const float wt = a.w[t * a.k + j0 + u];
-          acc.x += __fmul_rn(sj.x, wt); acc.y += __fmul_rn(sj.y, wt);
-          acc.z += __fmul_rn(sj.z, wt); acc.w += __fmul_rn(sj.w, wt);
+          acc.x += sj.x * wt; acc.y += sj.y * wt;
+          acc.z += sj.z * wt; acc.w += sj.w * wt;
         }
     }
     uint2 pk;

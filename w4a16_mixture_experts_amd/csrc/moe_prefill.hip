@@ -42,8 +42,9 @@ struct PfTile {
 };
 
 __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTile& t,
-                           int* s_scan) {
-  // s_scan: LDS int[kMaxExperts + 1] of exclusive token-tile prefix sums
+                           int* s_scan, int* s_off) {
+  // s_scan: LDS int[kMaxExperts + 1] of exclusive token-tile prefix sums; s_off: LDS
+  // int[kMaxExperts + 1], the segment offsets (loaded once, all at a time)
   const int tid = threadIdx.x;
   if (fixed_expert >= 0) {
     t.e = fixed_expert;
@@ -53,13 +54,21 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
     return t.tok0 < t.cnt;
   }
   if (tid < 64) {
+    int o[5];
+#pragma unroll
+    for (int q = 0; q < 5; q++) {   // offsets 4 tid .. 4 tid + 4, clamped: every load at once
+      const int e = tid * 4 + q;
+      o[q] = a.offsets[e <= a.E ? e : a.E];
+    }
     int v[4], run = 0;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      int e = tid * 4 + q;
-      v[q] = e < a.E ? (a.offsets[e + 1] - a.offsets[e] + kPfBN - 1) / kPfBN : 0;
+      const int e = tid * 4 + q;
+      v[q] = e < a.E ? (o[q + 1] - o[q] + kPfBN - 1) / kPfBN : 0;
       run += v[q];
+      s_off[e] = o[q];
     }
+    if (tid == 63) s_off[kMaxExperts] = o[4];
     int incl = run;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -85,8 +94,8 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
   }
   const int e = lo;
   t.e = e;
-  t.seg0 = a.offsets[e];
-  t.cnt = a.offsets[e + 1] - t.seg0;
+  t.seg0 = s_off[e];
+  t.cnt = s_off[e + 1] - t.seg0;
   t.tok0 = (tt_lin - s_scan[e]) * kPfBN;
   return t.tok0 < t.cnt;
 }
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   // for the copies into the other
   __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
   __shared__ __attribute__((aligned(16))) float s_seed0[kPfBN], s_seed1[kPfBN];
-  __shared__ int s_scan[kMaxExperts + 1];
+  __shared__ int s_scan[kMaxExperts + 1], s_off[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) float s_gsum[NW][kPfBN];
 
   span_begin(a.span);
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   const int rt = blockIdx.x % n_row_tiles;
   const int tt_lin = blockIdx.x / n_row_tiles;
   PfTile pt;
-  if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_scan)) return;
+  if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_scan, s_off)) return;
   const int slot = a.e2s ? a.e2s[pt.e] : pt.e;
   if (slot < 0) {
     if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
@@ -161,15 +170,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   // pieces of 4 rows x 256 bytes per group. Chunk c (16 bytes) of row r lands at position
   // c ^ (r mod 16) of the row, so that the 16 rows of a fragment read hit distinct banks.
   // Rows past the segment read the zero row.
+  // (the gathered row indices are loaded at clamped positions, all at once, and the rows
+  // past the segment are then pointed at the zero row)
   constexpr int kDmaPerWave = kPfBN / 4 / NW;
   const uint16_t* drow[kDmaPerWave];
+  int grow[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; i++) {
+    const int r = (wave * kDmaPerWave + i) * 4 + (lane >> 4);
+    const int rr = pt.tok0 + r < pt.cnt ? pt.tok0 + r : pt.cnt - 1;
+    grow[i] = GATEUP ? a.sorted_flat[pt.seg0 + rr] : 0;
+  }
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; i++) {
     const int r = (wave * kDmaPerWave + i) * 4 + (lane >> 4);
     const uint16_t* src = g_zero_row_pf;
     if (pt.tok0 + r < pt.cnt) {
       if (GATEUP)
-        src = a.x + (size_t)(a.sorted_flat[pt.seg0 + pt.tok0 + r] / a.k) * a.H;
+        src = a.x + (size_t)(grow[i] / a.k) * a.H;
       else
         src = a.h + (size_t)(pt.seg0 + pt.tok0 + r) * a.I;
     }
@@ -385,19 +403,34 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     }
     }
   } else {
+    // y_perm rows are in flat (token, slot) order: every row index and routing weight of the
+    // lane's 32 tokens is loaded first (rows past the segment read row 0, unused) and waited
+    // for once, instead of one round trip per row between stores (which also count in vmcnt)
+    int fr[8][4];
+    float wr[8][4];
+#pragma unroll
+    for (int bj = 0; bj < 8; bj++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = pt.tok0 + bj * 16 + tl0 + i;
+        fr[bj][i] = a.sorted_flat[pt.seg0 + (r < pt.cnt ? r : 0)];
+      }
+#pragma unroll
+    for (int bj = 0; bj < 8; bj++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) wr[bj][i] = a.w[fr[bj][i]];
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int bj = 0; bj < 8; bj++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = pt.tok0 + bj * 16 + tl0 + i;
         if (r < pt.cnt) {
-          const int f = a.sorted_flat[pt.seg0 + r];     // y_perm rows are in flat (token, slot) order
-          const float wgt = a.w[f];
 #pragma unroll
           for (int ai = 0; ai < NA; ai++) {
             if (!rvalid[ai]) continue;
             const int col = (rt * 16 + NA * wave + ai) * 16 + (lane & 15);
-            a.y_perm[(size_t)f * a.H + col] = acc[ai][bj][i] * wgt;
+            a.y_perm[(size_t)fr[bj][i] * a.H + col] = acc[ai][bj][i] * wr[bj][i];
           }
         }
       }
