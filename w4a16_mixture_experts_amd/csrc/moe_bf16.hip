@@ -27,6 +27,7 @@ constexpr int kBfKC = 2048;                // reduction columns staged in LDS at
 constexpr int kBfXS = kBfKC + 8;           // LDS row stride (bf16): 16-byte skew per row
 constexpr int kBfRing = 4;                 // K steps (32 columns, two tiles) in flight per wave
 constexpr int kBfTileBytes = 1024;         // 16 rows x 32 columns x 2 bytes
+constexpr int kBfCpol = 2;                 // weight loads non-temporal (nt), as in the int4 decode kernels
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(MoeArgs a, int per) {
@@ -75,8 +76,8 @@ __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(MoeArgs a, int 
   auto issue = [&](int s, int j) {
     const __amdgpu_buffer_rsrc_t& rs = s < total ? rsrc : rsrc_none;
     const uint32_t kk = (uint32_t)(s % KS);
-    R0[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (int)((t0 + kk) * kBfTileBytes), 0));
-    R1[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (int)((t1 + kk) * kBfTileBytes), 0));
+    R0[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (int)((t0 + kk) * kBfTileBytes), kBfCpol));
+    R1[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (int)((t1 + kk) * kBfTileBytes), kBfCpol));
   };
   // the weight stream starts first; the activation rows are staged while it is in flight
 #pragma unroll
