@@ -30,8 +30,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "MoE-layer tokens/s on 1 MI355X; % HBM BW (decode) / % bf16 MFMA (prefill)"
 # The expert kernel each OLMoE-shaped decode size launches (kernel-trace name and grid).
-DECODE_KERNEL = {1: ("decode_narrow_kernel<2>", "257x1x1 wg1024"),
-                 4: ("decode_fused_kernel<2, false, 8>", "257x1x1 wg512"),
+DECODE_KERNEL = {1: ("decode_narrow_kernel<3>", "257x1x1 wg1024"),
+                 4: ("decode_fused_kernel<3, false, 8>", "257x1x1 wg512"),
                  16: ("decode_fused_kernel<2, true, 16>", "257x1x1 wg1024")}
 
 

@@ -77,7 +77,12 @@ struct DecExpert {
 // kDecKC): the routing kernel's table sel[e][t] = slot + 1 when token t selected expert
 // e, else 0; every token row of x is staged before the weight stream starts, and a
 // publisher workgroup (the grid's last) groups the ids for the caller's outputs.
-constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2;
+// kSrcSelW: the table with E <= 64 in a launch of the active experts only. Every wave
+// reads all E table rows (lane e: row e) and finds the workgroup's expert and its tokens
+// by ballots, with no LDS pass and no barrier, so that the weight loads go out one memory
+// latency after the kernel starts.
+constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2, kSrcSelW = 3;
+__host__ __device__ constexpr bool is_sel(int src) { return src == kSrcSel || src == kSrcSelW; }
 struct DecPublish {
   const uint8_t* sel;        // [E][kSelStride] bytes
   int32_t* offsets;
@@ -136,27 +141,82 @@ __device__ __forceinline__ void dec_prestage_x(const MoeArgs& a, DecLDS& L) {
   for (int m = 0; m < SQ; m++) *reinterpret_cast<uint4*>(L.xs + dst[m]) = v[m];
 }
 
-// The same staging straight from memory into LDS (global_load_lds, 16 bytes per lane): no
-// registers are held, so the first weight ring can be issued behind these loads at once.
-// Wave w copies staging rows w, w + NW, ... (kDecTok rows); a wave-wide copy moves 512
-// consecutive activations. The count is fixed (kDecTok / NW rows x kDecKC / 512 copies per
-// wave), with no branch: rows past T copy token T - 1 and columns past H copy the row's
-// last 8 values, into staging positions nothing reads. The caller waits for completion
-// (the copies count in vmcnt, in issue order) and synchronizes the workgroup before
-// reading the rows.
+// The same staging straight from memory into LDS (buffer loads to LDS, 16 bytes per
+// lane): no registers are held, so the first weight ring can be issued behind these loads
+// at once. Wave w copies staging rows w, w + NW, ... (kDecTok rows); a wave-wide copy
+// moves 512 consecutive activations. The count is fixed (kDecTok / NW rows x kDecKC / 512
+// copies per wave), with no branch: rows past T copy token T - 1 and columns past H copy
+// the row's last 8 values, into staging positions nothing reads. The caller waits for
+// completion (the copies count in vmcnt and complete in issue order with the other vector
+// loads) and synchronizes the workgroup before reading the rows. (The buffer form, unlike
+// the global one, lets the compiler count the loads issued before the copies exactly.)
 template <int NW>
 __device__ __forceinline__ void dec_dma_x(const MoeArgs& a, DecLDS& L, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, a.T * a.H * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < kDecTok / NW; i++) {
     const int r = wave + i * NW;
-    const uint16_t* src = a.x + (size_t)(r < a.T ? r : a.T - 1) * a.H;
+    const int src = (r < a.T ? r : a.T - 1) * a.H;
 #pragma unroll
     for (int c0 = 0; c0 < kDecKC; c0 += 512) {
       const int c = c0 + 8 * lane < a.H ? c0 + 8 * lane : a.H - 8;
-      __builtin_amdgcn_global_load_lds(src + c, (__attribute__((address_space(3))) void*)(L.xs + r * kDecXS + c0), 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(L.xs + r * kDecXS + c0), 16,
+                                               2 * (src + c), 0, 0, 0);
     }
   }
+}
+
+// kSrcSelW: table row of expert `lane` (clamped) and that expert's slot, one vector load
+// each (the slot table through a zero-length resource when there is none).
+struct DecSelRow {
+  uint4 row;
+  int slot;
+};
+__device__ __forceinline__ DecSelRow dec_sel_load(const MoeArgs& a, const DecPublish& pub, int lane) {
+  const int e = lane < a.E ? lane : a.E - 1;
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.sel, (short)0, a.E * kSelStride, 0x00020000);
+  const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
+  DecSelRow r;
+  r.row = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, e * kSelStride, 0, 0));
+  r.slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * e, 0, 0);
+  return r;
+}
+
+// kSrcSelW: the workgroup's expert is the ai-th active one in ascending id order (active:
+// at least one of the T tokens selected it). Its tokens, ascending, are L.srows: lane t <
+// T of wave 0 holds in `tok` its position in that list and its flat index when token t
+// selected the expert (else -1); the caller writes them once the activation copies have
+// landed (an LDS store before that would wait for them) and its barrier publishes them.
+// Returns false when there is no ai-th active expert. Every wave computes the same
+// uniform values from the same rows.
+struct DecSelTok {
+  int pos, flat;
+};
+__device__ __forceinline__ bool dec_sel_pick(const MoeArgs& a, const DecSelRow& r, int ai, int lane, DecExpert& ex,
+                                             int& slot, DecSelTok& tok) {
+  const uint32_t w4[4] = {r.row.x, r.row.y, r.row.z, r.row.w};
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < kDecTok; q++) c += (q < a.T && ((w4[q >> 2] >> (8 * (q & 3))) & 0xFFu)) ? 1 : 0;
+  const bool on = lane < a.E && c > 0;
+  const uint64_t m = __ballot(on);
+  if (ai >= __popcll(m)) return false;
+  const uint64_t pick = __ballot(on && __popcll(m & ((1ull << lane) - 1ull)) == ai);
+  const int e = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(pick));
+  ex.e = e;
+  ex.cnt = __builtin_amdgcn_readlane(c, e);
+  ex.seg0 = 0;
+  ex.row0 = 0;
+  slot = a.e2s ? __builtin_amdgcn_readlane(r.slot, e) : e;
+  const uint32_t rw[4] = {(uint32_t)__builtin_amdgcn_readlane((int)r.row.x, e), (uint32_t)__builtin_amdgcn_readlane((int)r.row.y, e),
+                          (uint32_t)__builtin_amdgcn_readlane((int)r.row.z, e), (uint32_t)__builtin_amdgcn_readlane((int)r.row.w, e)};
+  const int tq = lane & 15;
+  const uint32_t wd = tq < 4 ? rw[0] : tq < 8 ? rw[1] : tq < 12 ? rw[2] : rw[3];
+  const int sb = lane < a.T ? (int)((wd >> (8 * (lane & 3))) & 0xFFu) : 0;
+  const uint64_t mt = __ballot(sb > 0);
+  tok.pos = sb > 0 ? __popcll(mt & ((1ull << lane) - 1ull)) : -1;
+  tok.flat = lane * a.k + sb - 1;
+  return true;
 }
 
 // Publisher of a table-routed launch (the grid's last workgroup): stable grouping of the
@@ -660,21 +720,27 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   // table routing with every expert launched: this expert's 16-byte table row in every
   // lane (a vector load, like the slot's)
   constexpr bool kSelAll = SRC == kSrcSel && ALL;
+  constexpr bool kSelW = SRC == kSrcSelW;
+  static_assert(!(kSelW && ALL), "the wave-local pick serves launches of the active experts");
   uint4 selrow = make_uint4(0u, 0u, 0u, 0u);
   DecPre pre;
+  DecSelRow srow;
+  DecSelTok stok;
   if (kSelAll) {
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.sel, (short)0, a.E * kSelStride, 0x00020000);
     selrow = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, (aidx < a.E ? aidx : a.E - 1) * kSelStride, 0, 0));
+  } else if (kSelW) {
+    srow = dec_sel_load(a, pub, lane);
   } else {
     pre = dec_preload<SRC, NT>(a, pub);
   }
-  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+  if (is_sel(SRC) && blockIdx.x == gridDim.x - 1) {
     dec_publish<NT>(a, L, pub);
     return;
   }
-  // every token row of x straight into LDS; with every expert launched the first weight
-  // ring goes out right behind those copies
-  if (kSelAll) dec_dma_x<NW>(a, L, wave, lane);
+  // every token row of x straight into LDS; the first weight ring goes out right behind
+  // those copies (with every expert launched, or once the table names the expert)
+  if (kSelAll || kSelW) dec_dma_x<NW>(a, L, wave, lane);
   else if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
   __builtin_amdgcn_sched_barrier(0);
   WSlot2 W[kDecRing];
@@ -713,6 +779,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
+  } else if (kSelW) {
+    // (a workgroup that leaves first lets its activation copies land)
+    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
+    if (slot < 0) {
+      if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
+    ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
+    ex.scales = nullptr;
   } else if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex, pp != 0)) {
     return;
   }
@@ -721,6 +800,14 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
+  if (kSelW) {
+    // as above: vmcnt(16) is the completion of the activation copies; the barrier
+    // publishes every wave's rows and wave 0's token list
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x4F70);
+    if (wave == 0 && stok.pos >= 0) L.srows[stok.pos] = stok.flat;
+    __syncthreads();
+  }
   const __amdgpu_buffer_rsrc_t rsrc_none = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, 0, 0x00020000);
 
   const int npass = (ex.cnt + kDecTok - 1) / kDecTok;
@@ -728,7 +815,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     const int nrow = ex.cnt - p * kDecTok < kDecTok ? ex.cnt - p * kDecTok : kDecTok;
     if (tid < kDecTok) {
       const int r = p * kDecTok + tid;
-      L.pf[tid] = r < ex.cnt ? (SRC == kSrcSel ? L.srows[r] : SRC == kSrcIds ? L.rows[ex.row0 + r]
+      L.pf[tid] = r < ex.cnt ? (is_sel(SRC) ? L.srows[r] : SRC == kSrcIds ? L.rows[ex.row0 + r]
                                                                           : a.sorted_flat[ex.seg0 + ex.row0 + r])
                              : -1;
     }
@@ -745,7 +832,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
       const int kcw = a.H - kc0 < kDecKC ? a.H - kc0 : kDecKC;
       const int ngc = kcw / kGroup;
       __syncthreads();   // previous chunk consumed; pass row list visible
-      if (SRC != kSrcSel) {   // table routing: every token row is already staged
+      if (!is_sel(SRC)) {   // table routing: every token row is already staged
         const int cw8 = kcw / 8;
         for (int q = tid; q < nrow * cw8; q += NT) {
           const int r = q / cw8, c8 = q - r * cw8;
@@ -754,7 +841,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
         }
       }
       __syncthreads();
-      const int myrow = (lane & 15) < nrow ? (SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
+      const int myrow = (lane & 15) < nrow ? (is_sel(SRC) ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
       const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
 #pragma unroll
       for (int i0 = 0; i0 < kDecKG; i0 += kDecRing) {
@@ -882,7 +969,14 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   span_begin(a.span);
   const int nslice = a.I / kNarRows;
-  const int aidx = blockIdx.x / nslice, cs = blockIdx.x % nslice;
+  // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8), and the four
+  // slices 4j .. 4j + 3 of an expert read the same down tiles (a word each). The logical
+  // order is therefore transposed so that each XCD takes a contiguous run of workgroups:
+  // the slices of one expert share that XCD's L2.
+  const int nwk = gridDim.x - (is_sel(SRC) ? 1 : 0);
+  int b = blockIdx.x;
+  if (b < nwk && (nwk & 7) == 0) b = (b & 7) * (nwk >> 3) + (b >> 3);
+  const int aidx = b / nslice, cs = b % nslice;
   const int G = a.H / kGroup, GQ = (G + kNarQ - 1) / kNarQ;
   const int nrbd = a.H / kTileRows, Gd = a.I / kGroup;
   const int tr = wave & 3, q = wave >> 2;               // tile row (row block 2c + tr / 2, gate / up), quarter
@@ -896,14 +990,36 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
 
   for (int i = tid; i < kDecXS / 8; i += NT)
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
-  const DecPre pre = dec_preload<SRC, NT>(a, pub);
-  if (SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
+  constexpr bool kSelW = SRC == kSrcSelW;
+  DecPre pre;
+  DecSelRow srow;
+  if (kSelW) srow = dec_sel_load(a, pub, lane);
+  else pre = dec_preload<SRC, NT>(a, pub);
+  if (is_sel(SRC) && blockIdx.x == gridDim.x - 1) {
     dec_publish<NT>(a, L, pub);
     return;
   }
-  if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  if (kSelW) dec_dma_x<NW>(a, L, wave, lane);   // token rows straight into LDS
+  else if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
+  __builtin_amdgcn_sched_barrier(0);
   DecExpert ex;
-  if (!dec_setup<SRC, false, NT>(a, L, pub, pre, -1, aidx, cs == 0, 0, ex)) return;
+  DecSelTok stok;
+  if (kSelW) {
+    int slot = 0;
+    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) {
+      __builtin_amdgcn_s_waitcnt(0);   // let the activation copies land before leaving
+      return;
+    }
+    if (slot < 0) {
+      if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
+    ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
+    ex.scales = nullptr;
+  } else if (!dec_setup<SRC, false, NT>(a, L, pub, pre, -1, aidx, cs == 0, 0, ex)) {
+    return;
+  }
 
   // every weight load at once (positions past the data load through a zero-length resource)
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ex.tiles, (short)0, nbytes, 0x00020000);
@@ -925,17 +1041,26 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     const int r = wave * kNarD + i;
     const bool on = r < nrbd;
     const uint32_t t = dbase + (uint32_t)(on ? r : 0) * Gd + (uint32_t)(cs >> 2);
-    w2[i] = __builtin_amdgcn_raw_buffer_load_b32(on ? rsrc : rnone, lo_w, (int)(t * kTileBytes), kWeightCpol);
-    s2[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), kWeightCpol));
+    // (default cache policy: the four slices of a word group read these lines)
+    w2[i] = __builtin_amdgcn_raw_buffer_load_b32(on ? rsrc : rnone, lo_w, (int)(t * kTileBytes), 0);
+    s2[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), 0));
+  }
+  if (kSelW) {
+    // the activation copies are older than the 24 weight loads: vmcnt(24) is their
+    // completion; the barrier below publishes the rows and wave 0's token list
+    static_assert(2 * kNarG + 2 * kNarD == 24, "the wait counts 24 weight loads");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x4F78);
+    if (wave == 0 && stok.pos >= 0) L.srows[stok.pos] = stok.flat;
   }
 
   // the expert's rows (at most T <= kDecTok: one pass)
   const int nrow = ex.cnt;
   if (tid < kDecTok)
-    L.pf[tid] = tid < nrow ? (SRC == kSrcSel ? L.srows[tid] : SRC == kSrcIds ? L.rows[tid] : a.sorted_flat[ex.seg0 + tid])
+    L.pf[tid] = tid < nrow ? (is_sel(SRC) ? L.srows[tid] : SRC == kSrcIds ? L.rows[tid] : a.sorted_flat[ex.seg0 + tid])
                            : -1;
   __syncthreads();
-  if (SRC != kSrcSel) {   // table routing: every token row is already staged
+  if (!is_sel(SRC)) {   // table routing: every token row is already staged
     const int cw8 = a.H / 8;
     for (int i = tid; i < nrow * cw8; i += NT) {
       const int r = i / cw8, c8 = i - r * cw8;
@@ -945,7 +1070,7 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     __syncthreads();
   }
   // ---- phase 1: this wave's tile row over its quarter of the input groups
-  const int myrow = (lane & 15) < nrow ? (SRC == kSrcSel ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
+  const int myrow = (lane & 15) < nrow ? (is_sel(SRC) ? L.pf[lane & 15] / a.k : (lane & 15)) : kDecTok;
   const uint16_t* xrow = L.xs + myrow * kDecXS + 8 * (lane >> 4);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1057,10 +1182,14 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 }
 
 // combine of the fused decode: y[t] = bf16(sum over slots j in order of w[t k + j] times
-// (sum over I-slices q in order of part[q][t k + j])). Workgroup = (token, 128 columns); thread = (4
-// columns, slot j) adds the slices of its slot, then the slots are added through LDS.
-constexpr int kCombCols = 128;
+// (sum over I-slices q in order of part[q][t k + j])). Workgroup = (token, CC columns);
+// thread = (4 columns, slot j) adds the slices of its slot, then the slots are added
+// through LDS. CC shrinks for few tokens so that the partial sums (slices x slots x H
+// floats per token) are read by enough workgroups: a compute unit streams only a few tens
+// of GB/s.
+template <int CC>
 __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
+  constexpr int kCombCols = CC;
   __shared__ float4 red[kMaxK][kCombCols / 4];
   span_begin(a.span);
   check_grouped_rows(a);
@@ -1214,6 +1343,29 @@ int decode_fused_waves(int T, int H, int I, int E, int k) {
   return 0;
 }
 
+// One fused launch: grid (pass-parallel units, every expert, or the active ones) x slices,
+// plus the publisher of a table-routed launch.
+template <int SRC>
+static void launch_fused(ProfScope& prof, const MoeArgs& as, const DecPublish& P, int fixed_expert, int ny, int units,
+                         bool pp, bool all, hipStream_t s) {
+  const int nw = as.I / (kTileRows * as.nparts);   // the workspace layout chose the width
+  const int extra = is_sel(SRC) ? 1 : 0;           // the publisher workgroup
+  const dim3 grid((pp ? units : all ? as.E : ny) * as.nparts + extra);
+  if (nw == kNarRows / kTileRows) {
+    EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * as.nparts + extra), dim3(1024), 0, s, as, P);
+    return;
+  }
+  if constexpr (SRC != kSrcSelW) {
+    if (all) {
+      if (nw == 16) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, 0);
+      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, 0);
+      return;
+    }
+  }
+  if (nw == 16) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, pp);
+  else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, pp);
+}
+
 static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub, int fixed_expert, int ny,
                                         hipStream_t s) {
   if (a.nparts > 0 && fixed_expert < 0) {
@@ -1221,28 +1373,12 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
     const bool pp = a.T > kDecTok && !(pub && pub->sel);   // pass-parallel: one workgroup per 16-row pass
     const bool all = !pp && (long long)a.T * a.k >= 2LL * a.E;
     const int units = (int)fused_units(a.T, a.E, a.k);
-    const int nw = a.I / (kTileRows * a.nparts);   // the workspace layout chose the width
-    const int extra = pub && pub->sel ? 1 : 0;     // the publisher workgroup
-    const DecPublish none{};
     MoeArgs as = a;
     as.span = prof.span();
-#define EXMOE_FUSED(SRC, P)                                                                                      \
-  do {                                                                                                          \
-    const dim3 grid((pp ? units : all ? a.E : ny) * a.nparts + extra);                                          \
-    if (nw == kNarRows / kTileRows) {                                                                           \
-      EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * a.nparts + extra), dim3(1024), 0, s, as, P);       \
-    } else if (nw == 16) {                                                                                      \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, 0); \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, pp); \
-    } else {                                                                                                    \
-      if (all) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, 0);  \
-      else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, false, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, pp); \
-    }                                                                                                           \
-  } while (0)
-    if (!pub) EXMOE_FUSED(kSrcGiven, none);
-    else if (pub->sel) EXMOE_FUSED(kSrcSel, *pub);
-    else EXMOE_FUSED(kSrcIds, *pub);
-#undef EXMOE_FUSED
+    if (!pub) launch_fused<kSrcGiven>(prof, as, DecPublish{}, fixed_expert, ny, units, pp, all, s);
+    else if (pub->sel && !all && a.E <= 64) launch_fused<kSrcSelW>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
+    else if (pub->sel) launch_fused<kSrcSel>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
+    else launch_fused<kSrcIds>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
     return hipGetLastError();
   }
   {
@@ -1304,8 +1440,17 @@ hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
       EXMOE_LAUNCH(prof, combine_parts_tok_kernel<4>, tok_grid, dim3(256), 0, s, as);
     else if (a.T > kDecTok && a.nparts == 8)
       EXMOE_LAUNCH(prof, combine_parts_tok_kernel<8>, tok_grid, dim3(256), 0, s, as);
-    else
-      EXMOE_LAUNCH(prof, combine_parts_kernel, dim3((a.H + kCombCols - 1) / kCombCols, a.T), dim3(256), 0, s, as);
+    else {
+      // widest column block that still gives 128 workgroups; threads: k slots x CC / 4
+      int cc = 128;
+      while (cc > 16 && (long long)a.T * ((a.H + cc - 1) / cc) < 128) cc /= 2;
+      const int nth = a.k * (cc / 4) < 256 ? (a.k * (cc / 4) + 63) / 64 * 64 : 256;
+      const dim3 grid((a.H + cc - 1) / cc, a.T);
+      if (cc == 128) EXMOE_LAUNCH(prof, combine_parts_kernel<128>, grid, dim3(nth), 0, s, as);
+      else if (cc == 64) EXMOE_LAUNCH(prof, combine_parts_kernel<64>, grid, dim3(nth), 0, s, as);
+      else if (cc == 32) EXMOE_LAUNCH(prof, combine_parts_kernel<32>, grid, dim3(nth), 0, s, as);
+      else EXMOE_LAUNCH(prof, combine_parts_kernel<16>, grid, dim3(nth), 0, s, as);
+    }
     return hipGetLastError();
   }
   const int nv = a.H / 4;
