@@ -1185,40 +1185,45 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 // (sum over I-slices q in order of part[q][t k + j])). Workgroup = (token, CC columns);
 // thread = (4 columns, slot j) adds the slices of its slot, then the slots are added
 // through LDS. CC shrinks for few tokens so that the partial sums (slices x slots x H
-// floats per token) are read by enough workgroups: a compute unit streams only a few tens
-// of GB/s.
-template <int CC>
+// floats per token) are read by enough workgroups. Every load of a thread (QB slices at a
+// time, at clamped positions, and the routing weight) is issued unconditionally before the
+// first add, so that they share one memory latency; a position past the last slice adds
+// +0.0, which leaves the sum's bits unchanged (the sum starts at +0.0 and never becomes
+// -0.0).
+template <int CC, int QB>
 __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
   constexpr int kCombCols = CC;
   __shared__ float4 red[kMaxK][kCombCols / 4];
   span_begin(a.span);
-  check_grouped_rows(a);
   const int t = blockIdx.y;
   const int col0 = blockIdx.x * kCombCols;
   const size_t slice = (size_t)a.T * a.k * a.H;
+  const int nq = a.nparts;
   for (int i = threadIdx.x; i < a.k * (kCombCols / 4); i += blockDim.x) {
     const int j = i / (kCombCols / 4), cq = i % (kCombCols / 4);
     const int c = col0 + 4 * cq;
+    const bool cin = c < a.H;
+    const float* src = a.part + ((size_t)t * a.k + j) * a.H + (cin ? c : 0);
+    const float wt = a.w[t * a.k + j];
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < a.H) {
-      const float* src = a.part + ((size_t)t * a.k + j) * a.H + c;
-      // sixteen slices in flight at a time, added in slice order
-      for (int q0 = 0; q0 < a.nparts; q0 += 16) {
-        float4 v[16];
+    for (int q0 = 0; q0 < nq; q0 += QB) {
+      float4 v[QB];
 #pragma unroll
-        for (int u = 0; u < 16; u++)
-          v[u] = q0 + u < a.nparts ? *reinterpret_cast<const float4*>(src + (q0 + u) * slice)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < 16; u++)
-          if (q0 + u < a.nparts) {
-            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
-          }
+      for (int u = 0; u < QB; u++) {
+        const int q = q0 + u < nq ? q0 + u : nq - 1;
+        v[u] = *reinterpret_cast<const float4*>(src + (size_t)q * slice);
       }
-      const float wt = a.w[t * a.k + j];
-      s.x *= wt; s.y *= wt; s.z *= wt; s.w *= wt;
+#pragma unroll
+      for (int u = 0; u < QB; u++) {
+        const bool on = q0 + u < nq;
+        s.x += on ? v[u].x : 0.f;
+        s.y += on ? v[u].y : 0.f;
+        s.z += on ? v[u].z : 0.f;
+        s.w += on ? v[u].w : 0.f;
+      }
     }
-    red[j][cq] = s;
+    s.x *= wt; s.y *= wt; s.z *= wt; s.w *= wt;
+    red[j][cq] = cin ? s : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
   if (threadIdx.x < kCombCols / 4) {
@@ -1235,6 +1240,7 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(MoeArgs a) {
       *reinterpret_cast<uint2*>(a.y + (size_t)t * a.H + c) = pk;
     }
   }
+  check_grouped_rows(a);   // (after the sums: its load does not delay them)
   span_end(a.span);
 }
 
@@ -1446,10 +1452,20 @@ hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
       while (cc > 16 && (long long)a.T * ((a.H + cc - 1) / cc) < 128) cc /= 2;
       const int nth = a.k * (cc / 4) < 256 ? (a.k * (cc / 4) + 63) / 64 * 64 : 256;
       const dim3 grid((a.H + cc - 1) / cc, a.T);
-      if (cc == 128) EXMOE_LAUNCH(prof, combine_parts_kernel<128>, grid, dim3(nth), 0, s, as);
-      else if (cc == 64) EXMOE_LAUNCH(prof, combine_parts_kernel<64>, grid, dim3(nth), 0, s, as);
-      else if (cc == 32) EXMOE_LAUNCH(prof, combine_parts_kernel<32>, grid, dim3(nth), 0, s, as);
-      else EXMOE_LAUNCH(prof, combine_parts_kernel<16>, grid, dim3(nth), 0, s, as);
+      // slices in flight per thread: the slice count rounded up to 4, 8, 16 or 32
+      const int qb = a.nparts <= 4 ? 4 : a.nparts <= 8 ? 8 : a.nparts <= 16 ? 16 : 32;
+#define EXMOE_COMB(CC)                                                                            \
+  do {                                                                                            \
+    if (qb == 4) EXMOE_LAUNCH(prof, (combine_parts_kernel<CC, 4>), grid, dim3(nth), 0, s, as);    \
+    else if (qb == 8) EXMOE_LAUNCH(prof, (combine_parts_kernel<CC, 8>), grid, dim3(nth), 0, s, as); \
+    else if (qb == 16) EXMOE_LAUNCH(prof, (combine_parts_kernel<CC, 16>), grid, dim3(nth), 0, s, as); \
+    else EXMOE_LAUNCH(prof, (combine_parts_kernel<CC, 32>), grid, dim3(nth), 0, s, as);           \
+  } while (0)
+      if (cc == 128) EXMOE_COMB(128);
+      else if (cc == 64) EXMOE_COMB(64);
+      else if (cc == 32) EXMOE_COMB(32);
+      else EXMOE_COMB(16);
+#undef EXMOE_COMB
     }
     return hipGetLastError();
   }
