@@ -257,7 +257,7 @@ hipError_t launch_route_sel(const uint16_t* x, const uint16_t* wr, const float* 
                             int renormalize, uint16_t* logits, int32_t* ids, float* w, uint8_t* sel,
                             uint32_t* counters, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T > kRouteSelMaxTok || k > 64) return hipErrorInvalidValue;
+  if (T > kRouteSelMaxTok || H > kRouteSelMaxH || k > 64) return hipErrorInvalidValue;
   ProfScope prof("route_sel", s);
   const int blocks = ((T + kRouteSelTB - 1) / kRouteSelTB) * ((E + kRouteSelEB - 1) / kRouteSelEB);
   EXMOE_LAUNCH(prof, route_sel_kernel, dim3(blocks), dim3(64 * kRouteSelTB), 0, s, x, wr, bias, T, H, E, k, renormalize, logits, ids,

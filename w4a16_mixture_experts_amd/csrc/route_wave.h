@@ -21,8 +21,9 @@ namespace exmoe {
 // (many waves) for a few tokens; many tokens go to the fp64 matrix-core kernel.
 // ---------------------------------------------------------------------------------
 // WT: write-through (agent-scope atomic) stores of the logits, read back by another
-// workgroup in the same launch.
-template <int TB, int EB, int LANES, int MC, bool WT>
+// workgroup in the same launch. ONE: the caller guarantees H <= 8 LANES MC (one pass of
+// loads, all issued before any arithmetic).
+template <int TB, int EB, int LANES, int MC, bool WT, bool ONE = false>
 __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                   const float* __restrict__ bias, int T, int H, int E,
                                                   uint16_t* __restrict__ logits, int blk) {
@@ -39,7 +40,7 @@ __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x
   if (t0 < T) {
     const int chunks = H / 8;
     // MC chunks per lane are loaded before any arithmetic: one memory latency per piece
-    for (int c0 = 0; c0 < chunks; c0 += LANES * MC) {
+    for (int c0 = 0; ONE ? c0 == 0 : c0 < chunks; c0 += LANES * MC) {
       uint4 xu[TB][MC], wu[EB][MC];
 #pragma unroll
       for (int m = 0; m < MC; m++) {
@@ -56,9 +57,21 @@ __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x
           wu[j][m] = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c];
         }
       }
+      if (ONE) {
+        // chunks past H become zeros (a product 0 * 0 added to a sum that starts at +0.0
+        // leaves its bits unchanged), so that no load sits under a per-lane branch
+#pragma unroll
+        for (int m = 0; m < MC; m++) {
+          const bool on = c0 + li + LANES * m < chunks;
+#pragma unroll
+          for (int i = 0; i < TB; i++) xu[i][m] = on ? xu[i][m] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+          for (int j = 0; j < EB; j++) wu[j][m] = on ? wu[j][m] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
 #pragma unroll
       for (int m = 0; m < MC; m++) {
-        if (c0 + li + LANES * m < chunks) {
+        if (ONE || c0 + li + LANES * m < chunks) {
           double xv[TB][8], wv[EB][8];
 #pragma unroll
           for (int i = 0; i < TB; i++) {
@@ -114,22 +127,24 @@ __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------------
-// Selection part of a table-routed launch (T <= kRouteSelMaxTok). Workgroup `blk` of NW
+// Selection part of a table-routed launch (T <= kRouteSelMaxTok, H <= kRouteSelMaxH: the
+// logits of a wave take one pass of loads). Workgroup `blk` of NW
 // waves takes one block of 4 tokens (wave w: token w % 4) and NW / 4 blocks of 2 experts
 // (wave w: block w / 4 of the workgroup's), and computes those logits. The last workgroup
 // of the token block to arrive (one arrival counter per token block) then selects each
 // token's experts from the bf16 logits of all workgroups, one wave per token, writes ids
 // and weights, and fills word tb of every expert's 16-byte table row: byte t % 4 of it is
-// slot + 1 when token t selected the expert, else 0. It clears the counter last, so the
+// slot + 1 when token t selected the expert, else 0. It clears the counter, so the
 // counters are zero between launches (and must be zero before the first one). Returns
-// true in that last arriver, once its table words and ids have completed.
-// Ordering: the logits, ids and table words are written through to the device-coherent
-// level (agent-scope atomic stores) and each wave waits for their completion before its
-// workgroup counts; readers use agent-scope atomic loads after their count (or a counter
-// they watch) has returned. With every shared location accessed by such atomics, no
-// cache write-back or invalidate is needed (those order plain loads and stores).
+// true in that last arriver. The ids, weights and table are read by later launches.
+// Ordering: the logits are written through to the device-coherent level (agent-scope
+// atomic stores) and each wave waits for their completion before its workgroup counts;
+// the last arriver reads them with agent-scope atomic loads after its count has returned.
+// With every shared location accessed by such atomics, no cache write-back or invalidate
+// is needed (those order plain loads and stores).
 // ---------------------------------------------------------------------------------
 constexpr int kRouteSelTB = 4, kRouteSelEB = 2;
+constexpr int kRouteSelMaxH = 8 * 64 * 4;   // 16-byte chunks x lanes x chunks per lane
 static_assert(kRouteSelMaxTok <= kRouteSelTB * kRouteSelCounters, "one counter per token block");
 
 struct RouteSelShared {
@@ -160,7 +175,7 @@ __device__ bool route_sel_part(const uint16_t* __restrict__ x, const uint16_t* _
   const int t = tb * kRouteSelTB + (wave % kRouteSelTB);   // this wave's token
   const int eb = wb * PAIRS + wave / kRouteSelTB;          // this wave's expert block
   if (t < T && eb < nEB)
-    route_logits_wave<1, kRouteSelEB, 64, 4, true>(x, wr, bias, T, H, E, logits, t * nEB + eb);
+    route_logits_wave<1, kRouteSelEB, 64, 4, true, true>(x, wr, bias, T, H, E, logits, t * nEB + eb);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's logits stores have completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -197,10 +212,9 @@ __device__ bool route_sel_part(const uint16_t* __restrict__ x, const uint16_t* _
     __hip_atomic_store(reinterpret_cast<uint32_t*>(sel) + (size_t)e * (kSelRowBytes / 4) + tb, v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);   // ids and table words have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
+  // Every workgroup of the token block has counted, so the counter can be cleared at once:
+  // it is read again only by the next launch, which starts after every store of this one
+  // has completed (no wait here for the ids and table words).
   if (threadIdx.x == 0)
     __hip_atomic_store(counters + tb * kRouteCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
