@@ -463,10 +463,10 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   // all-experts launch: the expert's slot, loaded first so that its latency overlaps the
   // activation loads (the publisher's index is clamped; it returns before using it)
   // (a vector load: a scalar one would be waited for with the kernel arguments)
-  int slot = 0;
-  if (ALL) {
-    const __amdgpu_buffer_rsrc_t er =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
+  // (a resident bank has no slot table: the slot is the expert, and nothing waits for it)
+  int slot = aidx;
+  if (ALL && a.e2s) {
+    const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, 4 * a.E, 0x00020000);
     slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * (aidx < a.E ? aidx : a.E - 1), 0, 0);
     __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
   }
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   WSlot2 W[kDecRing];
   __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
   if (ALL) {
-    slot = a.e2s ? __builtin_amdgcn_readfirstlane(slot) : aidx;
+    if (a.e2s) slot = __builtin_amdgcn_readfirstlane(slot);
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
                                              slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
@@ -710,10 +710,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   // all-experts launch: the expert's slot, loaded first so that its latency overlaps the
   // activation loads (the publisher's index is clamped; it returns before using it)
   // (a vector load: a scalar one would be waited for with the kernel arguments)
-  int slot = 0;
-  if (ALL) {
-    const __amdgpu_buffer_rsrc_t er =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
+  // (a resident bank has no slot table: the slot is the expert, and nothing waits for it)
+  int slot = aidx;
+  if (ALL && a.e2s) {
+    const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, 4 * a.E, 0x00020000);
     slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * (aidx < a.E ? aidx : a.E - 1), 0, 0);
     __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
   }
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   WSlot2 W[kDecRing];
   __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.base, (short)0, 0, 0x00020000);
   if (ALL) {
-    slot = a.e2s ? __builtin_amdgcn_readfirstlane(slot) : aidx;
+    if (a.e2s) slot = __builtin_amdgcn_readfirstlane(slot);
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.base + a.stride * (size_t)(slot >= 0 ? slot : 0)), (short)0,
                                              slot >= 0 ? nbytes : 0, 0x00020000);
 #pragma unroll
