@@ -42,9 +42,11 @@ constexpr int kDecKG = kDecKC / kGroup;      // 128-input groups per staged chun
 constexpr int kDecXS = kDecKC + 8;           // LDS row stride (bf16): 16-byte skew per row
 constexpr int kDecRing = 4;                  // weight groups in flight per wave
 constexpr int kSelStride = kSelRowBytes;     // bytes per expert row of the routing table (T <= 16)
-// Cache policy of the weight and scale loads: non-temporal (the nt bit of gfx950 buffer
-// loads). Every byte of the packed experts is read once per launch; streaming ~190 MB
-// with nt loads measured about 10% faster than with default-policy loads on MI355X.
+// Cache policy of the weight and scale loads of table-routed launches (T <= 16):
+// non-temporal (the nt bit of gfx950 buffer loads). There every byte of the packed
+// experts is read once per launch; streaming ~190 MB with nt loads measured about 10%
+// faster than with default-policy loads on MI355X. Launches whose passes re-read an
+// expert (more than 16 rows) keep the default policy, so that the re-reads hit in L2.
 constexpr int kWeightCpol = 2;
 
 
@@ -83,6 +85,7 @@ struct DecExpert {
 // latency after the kernel starts.
 constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2, kSrcSelW = 3;
 __host__ __device__ constexpr bool is_sel(int src) { return src == kSrcSel || src == kSrcSelW; }
+__host__ __device__ constexpr int weight_cpol(int src) { return is_sel(src) ? kWeightCpol : 0; }
 struct DecPublish {
   const uint8_t* sel;        // [E][kSelStride] bytes
   int32_t* offsets;
@@ -450,10 +453,10 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   };
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int s, WSlot2& w) {
     const uint32_t g = (uint32_t)gof(s);
-    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t0b + g * kTileBytes), kWeightCpol));
-    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t1b + g * kTileBytes), kWeightCpol));
-    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s0b + g * kScaleBytes), kWeightCpol));
-    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s1b + g * kScaleBytes), kWeightCpol));
+    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t0b + g * kTileBytes), weight_cpol(SRC)));
+    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(t1b + g * kTileBytes), weight_cpol(SRC)));
+    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s0b + g * kScaleBytes), weight_cpol(SRC)));
+    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(s1b + g * kScaleBytes), weight_cpol(SRC)));
   };
 
   for (int i = tid; i < kDecXS / 8; i += kDecThreads)
@@ -698,10 +701,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int s, WSlot2& w) {
     uint32_t ta, tb;
     tiles_of(s, ta, tb);
-    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(ta * kTileBytes), kWeightCpol));
-    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(tb * kTileBytes), kWeightCpol));
-    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + ta * kScaleBytes), kWeightCpol));
-    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + tb * kScaleBytes), kWeightCpol));
+    w.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(ta * kTileBytes), weight_cpol(SRC)));
+    w.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo_t, (int)(tb * kTileBytes), weight_cpol(SRC)));
+    w.s[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + ta * kScaleBytes), weight_cpol(SRC)));
+    w.s[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lo_s, (int)(sc_base + tb * kScaleBytes), weight_cpol(SRC)));
   };
 
   for (int i = tid; i < kDecXS / 8; i += NT)
@@ -1033,8 +1036,8 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     const int g = q * GQ + i;
     const bool on = i < GQ && g < G;
     const uint32_t t = tbase + (uint32_t)(on ? g : 0);
-    w1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(on ? rsrc : rnone, lo_t, (int)(t * kTileBytes), kWeightCpol));
-    s1[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), kWeightCpol));
+    w1[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(on ? rsrc : rnone, lo_t, (int)(t * kTileBytes), weight_cpol(SRC)));
+    s1[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), weight_cpol(SRC)));
   }
 #pragma unroll
   for (int i = 0; i < kNarD; i++) {
