@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other decode sizes and the prefill lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16", "batched"],
+    ap.add_argument("--only", choices=["decode", "prefill", "large", "cache", "prefill_cache", "bf16", "batched", "blas"],
                     default=None,
                     help="run a single workload (for profiling)")
     ap.add_argument("--prefill-tokens", type=int, nargs="+", default=[128, 512, 2048],
@@ -278,6 +279,39 @@ def cpu_baseline(lay_syn, shape, T, seconds, n_batches=64, extra=True):
             "sample": f"expert 0: dequantization {tdeq:.2f}s, 8 routed rows {8 * trow:.2f}s; layer = 8 experts' "
                       f"dequantization + {rows} rows"}
     out["per_config"] = per
+    return out
+
+
+def run_blas_reference(torch, reps=20):
+    """Context for the MFMA fractions: the installed BLAS (torch.matmul on bf16, i.e.
+    hipBLASLt) on dense bf16 GEMMs of the per-expert shapes of the large-expert prefill
+    layer (1024 tokens per expert: gate and up together, then down) and of a large square
+    GEMM. Not part of the layer: it shows what a dense bf16 GEMM reaches on this GPU."""
+    from synthetic import LARGE
+    shapes = {"large_expert_gateup_1024x28672x4096": (1024, 2 * LARGE.I, LARGE.H),
+              "large_expert_down_1024x4096x14336": (1024, LARGE.H, LARGE.I),
+              "square_8192x8192x8192": (8192, 8192, 8192)}
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (M, N, K) in shapes.items():
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            torch.matmul(a, b)
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e-3)
+        t = statistics.median(ts)
+        tf = 2.0 * M * N * K / t / 1e12
+        out[name] = {"us": t * 1e6, "tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS}
+        log(f"blas dense bf16 {name}: {t * 1e6:.1f} us, {tf:.0f} TFLOP/s ({100 * tf / BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA)")
+        del a, b
     return out
 
 
@@ -826,6 +860,9 @@ def main():
         log(f"built large-expert layer ({bank.base.numel() / 1e6:.0f} MB) in {time.time() - t0:.1f}s")
         secondary["large_prefill_T4096"] = run_prefill("large_prefill_T4096", LARGE, syn, [bank],
                                                        to_dev_bf16(syn.router()), 4096, None, 10, 2, replays=12)
+
+    if not args.no_secondary and args.only in (None, "large", "blas"):
+        secondary["blas_dense_bf16_reference"] = run_blas_reference(torch)
 
     if "head" not in result:
         print(json.dumps({"secondary": secondary}))

@@ -4,7 +4,8 @@
     python3 rocprof_summary.py stats  DIR --cmd "..." --out FILE
     python3 rocprof_summary.py traffic --kernel decode_fused_kernel \\
         --fetch DIR --write DIR --copy-bytes N --cmd "..." --out FILE
-    python3 rocprof_summary.py counters DIR --counter NAME ... --cmd "..." --out FILE
+    python3 rocprof_summary.py counters DIR [DIR ...] [--kernel PREFIX] [--copy-bytes N] \\
+        --cmd "..." [--cmd "..."] --out FILE
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` run into a per-kernel table (calls,
 average, median, min, max and total duration). `traffic` turns two `rocprofv3 --pmc`
@@ -176,12 +177,50 @@ def cmd_traffic(args):
 
 
 def cmd_counters(args):
-    lines = [f"# rocprofv3 --pmc per-dispatch means: {args.title}", f"# command: {args.cmd}", ""]
-    for c in args.counter:
-        vals = dispatch_counters(args.dir, c)
-        for name, v in sorted(vals.items()):
-            if _ours(name):
+    """Per-dispatch means of counters over one or more --pmc runs (one run per counter
+    pass, e.g. two passes of 8 SQ counters), for the library's kernels (or those whose
+    name starts with --kernel), then derived figures for each kernel whose counters are
+    all present: MFMA-busy share of the CU-busy cycles (4 SIMDs), VALU (non-MFMA)
+    instructions per MFMA, LDS instructions per MFMA, VALU co-issued with MFMA, LDS-index
+    activity; and with --copy-bytes, FETCH_SIZE / WRITE_SIZE scaled to bytes by
+    exmoe::copy_kernel's readings in the same run."""
+    cmds = args.cmd
+    lines = [f"# rocprofv3 --pmc per-dispatch means: {args.title}"] + [f"# command: {c}" for c in cmds] + [""]
+    means: dict[str, dict[str, float]] = {}
+    copy: dict[str, float] = {}
+    for d in args.dirs:
+        names = args.counter or sorted({r["Counter_Name"] for r in _csv_rows(d, "counter_collection.csv")})
+        for c in names:
+            vals = dispatch_counters(d, c)
+            for name, v in sorted(vals.items()):
+                if name.split("<")[0] == "copy_kernel":
+                    copy[c] = statistics.median(v)
+                if not _ours(name) or (args.kernel and not name.startswith(args.kernel)):
+                    continue
+                means.setdefault(name, {})[c] = statistics.mean(v)
                 lines.append(f"{name[:44]:44s} {c:28s} dispatches={len(v):5d} mean={statistics.mean(v):.6g}")
+    lines.append("")
+    for name, m in sorted(means.items()):
+        d = []
+        if all(k in m for k in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")):
+            d.append(f"MFMA busy / (4 x SQ_BUSY_CU_CYCLES) = {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * m['SQ_BUSY_CU_CYCLES']):.3f}")
+        if all(k in m for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA")) and m["SQ_INSTS_MFMA"]:
+            d.append(f"(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA = "
+                     f"{(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_INSTS_MFMA']:.2f}")
+        if all(k in m for k in ("SQ_INSTS_LDS", "SQ_INSTS_MFMA")) and m["SQ_INSTS_MFMA"]:
+            d.append(f"SQ_INSTS_LDS / SQ_INSTS_MFMA = {m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f}")
+        if all(k in m for k in ("SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES")) and m["SQ_VALU_MFMA_BUSY_CYCLES"]:
+            d.append(f"VALU co-issued with MFMA / MFMA busy = "
+                     f"{m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        if all(k in m for k in ("SQ_LDS_IDX_ACTIVE", "SQ_BUSY_CU_CYCLES")):
+            d.append(f"SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES = {m['SQ_LDS_IDX_ACTIVE'] / m['SQ_BUSY_CU_CYCLES']:.3f}")
+        if args.copy_bytes:
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                if c in m and copy.get(c):
+                    fac = args.copy_bytes / 1024.0 / copy[c]
+                    d.append(f"{c} x {fac:.4f} = {m[c] * fac * 1024.0 / 1e6:.1f} MB per dispatch")
+        for x in d:
+            lines.append(f"derived {name[:44]:44s} {x}")
     _emit("\n".join(lines) + "\n", args.out)
 
 
@@ -253,9 +292,11 @@ def main():
     b.add_argument("--title", default="")
     b.add_argument("--out")
     c = sub.add_parser("counters")
-    c.add_argument("dir")
-    c.add_argument("--counter", action="append", required=True)
-    c.add_argument("--cmd", required=True)
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--counter", action="append", default=[])
+    c.add_argument("--kernel", default="")
+    c.add_argument("--copy-bytes", type=int, default=0)
+    c.add_argument("--cmd", action="append", required=True)
     c.add_argument("--title", default="")
     c.add_argument("--out")
     args = ap.parse_args()
