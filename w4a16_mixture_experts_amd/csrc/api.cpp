@@ -720,15 +720,21 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
   if (!(flags & EXMOE_WEIGHTS_BF16) && choose_path(T, H, I, E, k, flags) == EXMOE_PATH_DECODE &&
       (long long)T * k <= kDecMaxRows) {
     // Decode sizes: the expert kernel groups the rows itself and publishes the grouping;
-    // for a few tokens it also makes the top-k selection from the logits, otherwise one
-    // workgroup per token routes it first.
+    // for a few tokens and E <= 64 it also makes the top-k selection from the logits (for
+    // larger E the routing kernel makes it and writes a per-expert token table), otherwise
+    // one workgroup per token routes it first.
     MoeArgs a{};
     a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
     a.flat_to_sorted = flat_to_sorted; a.base = static_cast<const uint8_t*>(bank->base); a.stride = bank->stride;
     a.e2s = bank->expert_to_slot; a.T = T; a.H = H; a.I = I; a.E = E; a.k = k; a.y = y;
     moe_workspace_layout(T, H, I, E, k, EXMOE_PATH_DECODE, &a, workspace);
     set_row_counters(a, workspace, flags);
-    if (decode_table_routing_ok(T, H, E, k)) {
+    if (decode_logit_routing_ok(T, H, I, E, k)) {
+      // the logits only; every expert workgroup makes the top-k selection from them
+      EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
+      EXMOE_HIP(launch_moe_decode_logit_routed(a, logits, renormalize, topk_ids, topk_weights, expert_offsets,
+                                               sorted_flat, flat_to_sorted, stream));
+    } else if (decode_table_routing_ok(T, H, E, k)) {
       EXMOE_HIP(launch_route_sel(x, w_router, logit_bias, T, H, E, k, renormalize, logits, topk_ids, topk_weights,
                                  a.sel, a.counters, stream));
       EXMOE_HIP(launch_moe_decode_routed(a, a.sel, expert_offsets, sorted_flat, flat_to_sorted, stream));

@@ -156,6 +156,14 @@ hipError_t launch_route_sel(const uint16_t* x, const uint16_t* wr, const float* 
 bool decode_table_routing_ok(int T, int H, int E, int k);
 hipError_t launch_moe_decode_routed(const MoeArgs& a, const uint8_t* sel, int32_t* offsets, int32_t* sorted_flat,
                                     int32_t* flat_to_sorted, hipStream_t s);
+// Decode path that makes the top-k selection itself from the bf16 logits of
+// launch_route_logits (when decode_logit_routing_ok: table routing with E <= 64 and the
+// fused expert kernels): every workgroup ranks the experts of each token, and the
+// publisher workgroup also writes ids and routing weights (a.ids / a.w alias them).
+bool decode_logit_routing_ok(int T, int H, int I, int E, int k);
+hipError_t launch_moe_decode_logit_routed(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
+                                          float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
+                                          hipStream_t s);
 hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
 // The same paths in parts (a forward in waves runs the expert kernels once per wave and
 // the correction sums and the combine once): decode experts; prefill sums, experts.

@@ -79,18 +79,23 @@ struct DecExpert {
 // kDecKC): the routing kernel's table sel[e][t] = slot + 1 when token t selected expert
 // e, else 0; every token row of x is staged before the weight stream starts, and a
 // publisher workgroup (the grid's last) groups the ids for the caller's outputs.
-// kSrcSelW: the table with E <= 64 in a launch of the active experts only. Every wave
-// reads all E table rows (lane e: row e) and finds the workgroup's expert and its tokens
-// by ballots, with no LDS pass and no barrier, so that the weight loads go out one memory
-// latency after the kernel starts.
-constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2, kSrcSelW = 3;
-__host__ __device__ constexpr bool is_sel(int src) { return src == kSrcSel || src == kSrcSelW; }
+// kSrcLgt (T <= 16, H <= kDecKC, E <= 64): the routing kernel wrote only the bf16 logits.
+// Every workgroup makes the top-k selection itself (one wave per token, ranks by readlane
+// compares: the selection of topk_rank_token), exchanges the table columns in LDS and
+// finds its expert and tokens by ballots; the publisher workgroup also writes the ids and
+// routing weights. This removes the routing kernel's arrival count and read-back.
+constexpr int kSrcGiven = 0, kSrcIds = 1, kSrcSel = 2, kSrcLgt = 3;
+__host__ __device__ constexpr bool is_sel(int src) { return src == kSrcSel || src == kSrcLgt; }
 __host__ __device__ constexpr int weight_cpol(int src) { return is_sel(src) ? kWeightCpol : 0; }
 struct DecPublish {
-  const uint8_t* sel;        // [E][kSelStride] bytes
+  const uint8_t* sel;        // [E][kSelStride] bytes (kSrcSel)
   int32_t* offsets;
   int32_t* sorted_flat;
   int32_t* flat_to_sorted;
+  const uint16_t* logits;    // bf16 [T][E] (kSrcLgt)
+  int32_t* ids;              // [T][k], written by the publisher (kSrcLgt)
+  float* w;                  // [T][k], written by the publisher (kSrcLgt)
+  int renormalize;
 };
 
 // The routing inputs of the set-up (ids, offsets or the table), loaded into registers as
@@ -169,23 +174,54 @@ __device__ __forceinline__ void dec_dma_x(const MoeArgs& a, DecLDS& L, int wave,
   }
 }
 
-// kSrcSelW: table row of expert `lane` (clamped) and that expert's slot, one vector load
-// each (the slot table through a zero-length resource when there is none).
-struct DecSelRow {
-  uint4 row;
+// kSrcLgt: the logits of the tokens a wave ranks (tokens w, w + NW, ...; lane e: expert
+// e, clamped) and the slot of expert `lane`, loaded as the kernel's first loads (through
+// zero-length resources where there is nothing to read).
+template <int NW>
+struct DecLgt {
+  uint16_t lg[(kDecTok + NW - 1) / NW];
   int slot;
 };
-__device__ __forceinline__ DecSelRow dec_sel_load(const MoeArgs& a, const DecPublish& pub, int lane) {
+template <int NW>
+__device__ __forceinline__ DecLgt<NW> dec_lgt_load(const MoeArgs& a, const DecPublish& pub, int wave, int lane) {
   const int e = lane < a.E ? lane : a.E - 1;
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.sel, (short)0, a.E * kSelStride, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.logits, (short)0, a.T * a.E * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)a.e2s, (short)0, a.e2s ? 4 * a.E : 0, 0x00020000);
-  DecSelRow r;
-  r.row = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, e * kSelStride, 0, 0));
+  DecLgt<NW> r;
+#pragma unroll
+  for (int i = 0; i < (kDecTok + NW - 1) / NW; i++) {
+    const int t = wave + i * NW < a.T ? wave + i * NW : a.T - 1;
+    r.lg[i] = __builtin_amdgcn_raw_buffer_load_b16(lr, 2 * (t * a.E + e), 0, 0);
+  }
   r.slot = __builtin_amdgcn_raw_buffer_load_b32(er, 4 * e, 0, 0);
   return r;
 }
 
-// kSrcSelW: the workgroup's expert is the ai-th active one in ascending id order (active:
+// kSrcLgt: byte t of expert e's table row for each token t < T the wave ranks: rank + 1
+// when expert e is among token t's top k (its rank in (logit descending, id ascending)
+// order is its slot), else 0 — the selection of topk_rank_token. Lane e computes expert
+// e's byte and hands it to put(slot i of the wave's tokens, token, byte).
+template <int NW, class Put>
+__device__ __forceinline__ void dec_lgt_ranks(const MoeArgs& a, const DecLgt<NW>& r, int wave, int lane, Put put) {
+#pragma unroll
+  for (int i = 0; i < (kDecTok + NW - 1) / NW; i++) {
+    const int t = wave + i * NW;
+    if (t >= a.T) break;   // uniform
+    const uint32_t key = lane < a.E ? order_key(r.lg[i], lane) : 0u;
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; j++) rank += (uint32_t)__builtin_amdgcn_readlane((int)key, j) > key ? 1 : 0;
+    put(i, t, lane < a.E && rank < a.k ? rank + 1 : 0);
+  }
+}
+
+// The table row of expert `lane` and that expert's slot.
+struct DecSelRow {
+  uint4 row;
+  int slot;
+};
+
+// kSrcLgt: the workgroup's expert is the ai-th active one in ascending id order (active:
 // at least one of the T tokens selected it). Its tokens, ascending, are L.srows: lane t <
 // T of wave 0 holds in `tok` its position in that list and its flat index when token t
 // selected the expert (else -1); the caller writes them once the activation copies have
@@ -223,14 +259,30 @@ __device__ __forceinline__ bool dec_sel_pick(const MoeArgs& a, const DecSelRow& 
 }
 
 // Publisher of a table-routed launch (the grid's last workgroup): stable grouping of the
-// ids the routing kernel wrote, into the caller's offsets / sorted_flat / flat_to_sorted.
-template <int NT>
+// ids, into the caller's offsets / sorted_flat / flat_to_sorted. kSrcSel: the ids the
+// routing kernel wrote; kSrcLgt: the top-k selection and weights of every token made here
+// from the logits (one wave per token), also written to the caller's ids and weights.
+template <int SRC, int NT>
 __device__ void dec_publish(const MoeArgs& a, DecLDS& L, const DecPublish& pub) {
   int32_t* ids_l = reinterpret_cast<int32_t*>(L.xs);
   auto& gs = *reinterpret_cast<GroupSharedT<NT>*>(L.xs + 2 * kDecMaxRows);
   static_assert(2 * kDecMaxRows * 2 + sizeof(GroupSharedT<NT>) <= sizeof(L.xs), "publisher scratch exceeds the staging rows");
   const int TK = a.T * a.k;
-  for (int f = threadIdx.x; f < TK; f += NT) ids_l[f] = a.ids[f];
+  if (SRC == kSrcLgt) {
+    const int lane = (int)lane_id(), wave = threadIdx.x >> 6;
+    for (int t = wave; t < a.T; t += NT / 64) {
+      int id;
+      float wt;
+      topk_rank_token(pub.logits + (size_t)t * a.E, a.E, a.k, pub.renormalize, id, wt);
+      if (lane < a.k) {
+        ids_l[t * a.k + lane] = id;
+        pub.ids[t * a.k + lane] = id;
+        pub.w[t * a.k + lane] = wt;
+      }
+    }
+  } else {
+    for (int f = threadIdx.x; f < TK; f += NT) ids_l[f] = a.ids[f];
+  }
   __syncthreads();
   group_block<NT>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
 }
@@ -475,7 +527,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_expert_kernel(MoeArgs a
   }
   const DecPre pre = dec_preload<SRC, kDecThreads>(a, pub);
   if (GATEUP && SRC == kSrcSel && blockIdx.x == gridDim.x - 1) {
-    dec_publish<kDecThreads>(a, L, pub);
+    dec_publish<SRC, kDecThreads>(a, L, pub);
     return;
   }
   if (GATEUP && SRC == kSrcSel) dec_prestage_x<kDecThreads>(a, L);
@@ -721,29 +773,32 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     __builtin_amdgcn_sched_barrier(0);   // keep the load here, ahead of the others
   }
   // table routing with every expert launched: this expert's 16-byte table row in every
-  // lane (a vector load, like the slot's)
+  // lane (a vector load, like the slot's), or (logit routing) the logits of the wave's
+  // tokens, from which that row is made here
   constexpr bool kSelAll = SRC == kSrcSel && ALL;
-  constexpr bool kSelW = SRC == kSrcSelW;
-  static_assert(!(kSelW && ALL), "the wave-local pick serves launches of the active experts");
+  constexpr bool kLgt = SRC == kSrcLgt;
+  constexpr bool kTabAll = (SRC == kSrcSel || kLgt) && ALL;   // the token list from one table row
+  constexpr int TPW = (kDecTok + NW - 1) / NW;                // tokens ranked per wave
+  __shared__ __attribute__((aligned(16))) uint8_t s_tab[64 * kDecTok];   // logit routing: table rows
   uint4 selrow = make_uint4(0u, 0u, 0u, 0u);
   DecPre pre;
-  DecSelRow srow;
+  DecLgt<NW> lgt;
   DecSelTok stok;
   if (kSelAll) {
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)pub.sel, (short)0, a.E * kSelStride, 0x00020000);
     selrow = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, (aidx < a.E ? aidx : a.E - 1) * kSelStride, 0, 0));
-  } else if (kSelW) {
-    srow = dec_sel_load(a, pub, lane);
+  } else if (kLgt) {
+    lgt = dec_lgt_load<NW>(a, pub, wave, lane);
   } else {
     pre = dec_preload<SRC, NT>(a, pub);
   }
   if (is_sel(SRC) && blockIdx.x == gridDim.x - 1) {
-    dec_publish<NT>(a, L, pub);
+    dec_publish<SRC, NT>(a, L, pub);
     return;
   }
-  // every token row of x straight into LDS; the first weight ring goes out right behind
-  // those copies (with every expert launched, or once the table names the expert)
-  if (kSelAll || kSelW) dec_dma_x<NW>(a, L, wave, lane);
+  // every token row of x straight into LDS; with every expert launched the first weight
+  // ring goes out right behind those copies
+  if (kTabAll) dec_dma_x<NW>(a, L, wave, lane);
   else if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
   __builtin_amdgcn_sched_barrier(0);
   WSlot2 W[kDecRing];
@@ -755,16 +810,38 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
-  if (kSelAll) {
+  if (kTabAll) {
+    // logit routing: this expert's byte of each of the wave's tokens (uniform), while the
+    // copies and the ring are in flight
+    // (one expert's rank per token: the number of experts whose key is above its own, by one
+    // ballot; the same order as the full ranks)
+    uint8_t tb[TPW];
+    if (kLgt) {
+#pragma unroll
+      for (int i = 0; i < TPW; i++) {
+        const uint32_t key = lane < a.E ? order_key(lgt.lg[i], lane) : 0u;
+        const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)key, aidx < a.E ? aidx : 0);
+        const int rank = __popcll(__ballot(key > mine));
+        tb[i] = (uint8_t)(rank < a.k ? rank + 1 : 0);
+      }
+    }
     // the activation copies are older than the 4 x 4 ring loads: vmcnt(16) is their
     // completion (expcnt and lgkmcnt left at their maxima); the barrier below (token list)
     // publishes every wave's rows
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x4F70);
     static_assert(kDecRing * 4 == 16, "the wait above counts 16 ring loads");
+    if (kLgt) {
+      // (stored after that wait: an LDS store before it would wait for the copies)
+#pragma unroll
+      for (int i = 0; i < TPW; i++)
+        if (lane == 0 && wave + i * NW < a.T) s_tab[wave + i * NW] = tb[i];
+      __syncthreads();
+      selrow = *reinterpret_cast<const uint4*>(s_tab);
+    }
   }
   DecExpert ex;
-  if (kSelAll) {
+  if (kTabAll) {
     // the expert's tokens, ascending, straight from its table row: no grouping needed
     const uint32_t wd = (lane & 15) < 4 ? selrow.x : (lane & 15) < 8 ? selrow.y : (lane & 15) < 12 ? selrow.z : selrow.w;
     const int sb = lane < a.T ? (int)((wd >> (8 * (lane & 3))) & 0xFFu) : 0;
@@ -782,19 +859,20 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
-  } else if (kSelW) {
-    // (a workgroup that leaves first lets its activation copies land)
-    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) {
-      __builtin_amdgcn_s_waitcnt(0);
-      return;
-    }
+  } else if (kLgt) {
+    // every token's table column into LDS (wave w: tokens w, w + NW, ...; lane e: row e),
+    // then every wave reads the rows and picks the workgroup's expert by ballots
+    dec_lgt_ranks<NW>(a, lgt, wave, lane, [&](int, int t, int b) { s_tab[lane * kDecTok + t] = (uint8_t)b; });
+    __syncthreads();
+    const DecSelRow srow{*reinterpret_cast<const uint4*>(&s_tab[lane * kDecTok]), lgt.slot};
+    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) return;
     if (slot < 0) {
       if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
-      __builtin_amdgcn_s_waitcnt(0);
       return;
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
+    dec_dma_x<NW>(a, L, wave, lane);   // the token rows straight into LDS, then the weights
   } else if (!dec_setup<SRC, ALL, NT>(a, L, pub, pre, fixed_expert, aidx, cs == 0, slot, ex, pp != 0)) {
     return;
   }
@@ -803,7 +881,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
 #pragma unroll
     for (int j = 0; j < kDecRing; j++) issue(rsrc, j, W[j]);
   }
-  if (kSelW) {
+  if (kLgt && !ALL) {
     // as above: vmcnt(16) is the completion of the activation copies; the barrier
     // publishes every wave's rows and wave 0's token list
     __builtin_amdgcn_sched_barrier(0);
@@ -993,33 +1071,35 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
 
   for (int i = tid; i < kDecXS / 8; i += NT)
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
-  constexpr bool kSelW = SRC == kSrcSelW;
+  constexpr bool kLgt = SRC == kSrcLgt;
+  __shared__ __attribute__((aligned(16))) uint8_t s_tab[64 * kDecTok];   // logit routing: table rows
   DecPre pre;
-  DecSelRow srow;
-  if (kSelW) srow = dec_sel_load(a, pub, lane);
+  DecLgt<NW> lgt;
+  if (kLgt) lgt = dec_lgt_load<NW>(a, pub, wave, lane);
   else pre = dec_preload<SRC, NT>(a, pub);
   if (is_sel(SRC) && blockIdx.x == gridDim.x - 1) {
-    dec_publish<NT>(a, L, pub);
+    dec_publish<SRC, NT>(a, L, pub);
     return;
   }
-  if (kSelW) dec_dma_x<NW>(a, L, wave, lane);   // token rows straight into LDS
-  else if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
-  __builtin_amdgcn_sched_barrier(0);
+  if (SRC == kSrcSel) dec_prestage_x<NT>(a, L);
   DecExpert ex;
   DecSelTok stok;
-  if (kSelW) {
+  if (kLgt) {
+    // every token's table column into LDS (wave w: token w; lane e: row e), then every
+    // wave reads the rows and picks the workgroup's expert by ballots
+    dec_lgt_ranks<NW>(a, lgt, wave, lane, [&](int, int t, int b) { s_tab[lane * kDecTok + t] = (uint8_t)b; });
+    __syncthreads();
+    const DecSelRow srow{*reinterpret_cast<const uint4*>(&s_tab[lane * kDecTok]), lgt.slot};
     int slot = 0;
-    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) {
-      __builtin_amdgcn_s_waitcnt(0);   // let the activation copies land before leaving
-      return;
-    }
+    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) return;
     if (slot < 0) {
       if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
-      __builtin_amdgcn_s_waitcnt(0);
       return;
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
+    dec_dma_x<NW>(a, L, wave, lane);   // the token rows straight into LDS, then the weights
+    __builtin_amdgcn_sched_barrier(0);
   } else if (!dec_setup<SRC, false, NT>(a, L, pub, pre, -1, aidx, cs == 0, 0, ex)) {
     return;
   }
@@ -1048,7 +1128,7 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     w2[i] = __builtin_amdgcn_raw_buffer_load_b32(on ? rsrc : rnone, lo_w, (int)(t * kTileBytes), 0);
     s2[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(on ? rsrc : rnone, lo_s, (int)(sc_base + t * kScaleBytes), 0));
   }
-  if (kSelW) {
+  if (kLgt) {
     // the activation copies are older than the 24 weight loads: vmcnt(24) is their
     // completion; the barrier below publishes the rows and wave 0's token list
     static_assert(2 * kNarG + 2 * kNarD == 24, "the wait counts 24 weight loads");
@@ -1364,7 +1444,7 @@ static void launch_fused(ProfScope& prof, const MoeArgs& as, const DecPublish& P
     EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * as.nparts + extra), dim3(1024), 0, s, as, P);
     return;
   }
-  if constexpr (SRC != kSrcSelW) {
+  {
     if (all) {
       if (nw == 16) EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 16>), grid, dim3(1024), 0, s, as, P, fixed_expert, 0);
       else EXMOE_LAUNCH(prof, (decode_fused_kernel<SRC, true, 8>), grid, dim3(512), 0, s, as, P, fixed_expert, 0);
@@ -1379,13 +1459,13 @@ static hipError_t launch_decode_experts(const MoeArgs& a, const DecPublish* pub,
                                         hipStream_t s) {
   if (a.nparts > 0 && fixed_expert < 0) {
     ProfScope prof("decode_fused", s);
-    const bool pp = a.T > kDecTok && !(pub && pub->sel);   // pass-parallel: one workgroup per 16-row pass
+    const bool pp = a.T > kDecTok && !(pub && (pub->sel || pub->logits));   // pass-parallel: one workgroup per 16-row pass
     const bool all = !pp && (long long)a.T * a.k >= 2LL * a.E;
     const int units = (int)fused_units(a.T, a.E, a.k);
     MoeArgs as = a;
     as.span = prof.span();
     if (!pub) launch_fused<kSrcGiven>(prof, as, DecPublish{}, fixed_expert, ny, units, pp, all, s);
-    else if (pub->sel && !all && a.E <= 64) launch_fused<kSrcSelW>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
+    else if (pub->logits) launch_fused<kSrcLgt>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
     else if (pub->sel) launch_fused<kSrcSel>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
     else launch_fused<kSrcIds>(prof, as, *pub, fixed_expert, ny, units, pp, all, s);
     return hipGetLastError();
@@ -1428,6 +1508,21 @@ hipError_t launch_moe_decode_routed(const MoeArgs& a, const uint8_t* sel, int32_
                                     int32_t* flat_to_sorted, hipStream_t s) {
   const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
   const DecPublish pub{sel, offsets, sorted_flat, flat_to_sorted};
+  hipError_t e = launch_decode_experts(a, &pub, -1, ny, s);
+  if (e != hipSuccess) return e;
+  return launch_combine(a, s);
+}
+
+bool decode_logit_routing_ok(int T, int H, int I, int E, int k) {
+  return decode_table_routing_ok(T, H, E, k) && E <= 64 && decode_fused_waves(T, H, I, E, k) != 0;
+}
+
+hipError_t launch_moe_decode_logit_routed(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
+                                          float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
+                                          hipStream_t s) {
+  if (a.nparts <= 0 || a.E > 64) return hipErrorInvalidValue;
+  const int ny = a.E < a.T * a.k ? a.E : a.T * a.k;
+  const DecPublish pub{nullptr, offsets, sorted_flat, flat_to_sorted, logits, ids, w, renormalize};
   hipError_t e = launch_decode_experts(a, &pub, -1, ny, s);
   if (e != hipSuccess) return e;
   return launch_combine(a, s);

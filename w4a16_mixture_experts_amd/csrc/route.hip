@@ -12,14 +12,15 @@
 
 namespace exmoe {
 
-template <int TB, int EB, int LANES, int MC>
+// ONE: H <= 8 LANES MC, one pass of loads per wave.
+template <int TB, int EB, int LANES, int MC, bool ONE>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias, int T,
                                                           int H, int E,
                                                           uint16_t* __restrict__ logits) {
-  route_logits_wave<TB, EB, LANES, MC, false>(x, wr, bias, T, H, E, logits,
-                                             blockIdx.x * (64 / LANES) + (int)lane_id() / LANES);
+  route_logits_wave<TB, EB, LANES, MC, false, ONE>(x, wr, bias, T, H, E, logits,
+                                                  blockIdx.x * (64 / LANES) + (int)lane_id() / LANES);
 }
 
 // ---------------------------------------------------------------------------------
@@ -272,7 +273,12 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (T <= 128) {
     // one wave per 2 tokens x 2 experts, the whole wave on H: a row in one round trip
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
-    EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E, logits);
+    if (H <= kRouteSelMaxH)
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, true>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E,
+                   logits);
+    else
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, false>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E,
+                   logits);
   } else {
     // 16 x 16 tiles on the fp64 matrix cores (H is a multiple of 128), H split over 8
     // waves. Measured against four 4 x 4 blocks of vector FMAs per wave: 2048 tokens and
