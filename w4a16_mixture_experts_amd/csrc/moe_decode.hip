@@ -201,18 +201,42 @@ __device__ __forceinline__ DecLgt<NW> dec_lgt_load(const MoeArgs& a, const DecPu
 // when expert e is among token t's top k (its rank in (logit descending, id ascending)
 // order is its slot), else 0 — the selection of topk_rank_token. Lane e computes expert
 // e's byte and hands it to put(slot i of the wave's tokens, token, byte).
+// The 64 keys go through the wave's own LDS row (skeys: 64 words per wave), where every
+// lane reads all of them with broadcast 16-byte reads: no scalar round trip per key. (A
+// wave's LDS operations complete in order, so no barrier is needed.)
+__device__ __forceinline__ int dec_lgt_byte(const MoeArgs& a, uint16_t lg, int lane, uint32_t* row) {
+  const uint32_t key = lane < a.E ? order_key(lg, lane) : 0u;
+  row[lane] = key;
+  int rank = 0;
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + 4 * q);
+    rank += (v.x > key ? 1 : 0) + (v.y > key ? 1 : 0) + (v.z > key ? 1 : 0) + (v.w > key ? 1 : 0);
+  }
+  return lane < a.E && rank < a.k ? rank + 1 : 0;
+}
 template <int NW, class Put>
-__device__ __forceinline__ void dec_lgt_ranks(const MoeArgs& a, const DecLgt<NW>& r, int wave, int lane, Put put) {
+__device__ __forceinline__ void dec_lgt_ranks(const MoeArgs& a, const DecLgt<NW>& r, int wave, int lane,
+                                              uint32_t* skeys, Put put) {
 #pragma unroll
   for (int i = 0; i < (kDecTok + NW - 1) / NW; i++) {
     const int t = wave + i * NW;
     if (t >= a.T) break;   // uniform
-    const uint32_t key = lane < a.E ? order_key(r.lg[i], lane) : 0u;
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < 64; j++) rank += (uint32_t)__builtin_amdgcn_readlane((int)key, j) > key ? 1 : 0;
-    put(i, t, lane < a.E && rank < a.k ? rank + 1 : 0);
+    put(i, t, dec_lgt_byte(a, r.lg[i], lane, skeys + wave * 64));
   }
+}
+
+// kSrcLgt, launches of the active experts: the table row of expert `lane`. With one token
+// every wave ranks it itself (its logits are what every wave loaded); otherwise wave w
+// ranks tokens w, w + NW, ..., the columns meet in LDS (stab: 64 rows of kDecTok bytes)
+// and every wave reads the rows after a barrier.
+template <int NW>
+__device__ __forceinline__ uint4 dec_lgt_rows(const MoeArgs& a, const DecLgt<NW>& r, int wave, int lane,
+                                              uint32_t* skeys, uint8_t* stab) {
+  if (a.T == 1) return make_uint4((uint32_t)dec_lgt_byte(a, r.lg[0], lane, skeys + wave * 64), 0u, 0u, 0u);
+  dec_lgt_ranks<NW>(a, r, wave, lane, skeys, [&](int, int t, int b) { stab[lane * kDecTok + t] = (uint8_t)b; });
+  __syncthreads();
+  return *reinterpret_cast<const uint4*>(&stab[lane * kDecTok]);
 }
 
 // The table row of expert `lane` and that expert's slot.
@@ -780,6 +804,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
   constexpr bool kTabAll = (SRC == kSrcSel || kLgt) && ALL;   // the token list from one table row
   constexpr int TPW = (kDecTok + NW - 1) / NW;                // tokens ranked per wave
   __shared__ __attribute__((aligned(16))) uint8_t s_tab[64 * kDecTok];   // logit routing: table rows
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kLgt && !ALL ? NW * 64 : 4];   // logit routing: keys
   uint4 selrow = make_uint4(0u, 0u, 0u, 0u);
   DecPre pre;
   DecLgt<NW> lgt;
@@ -860,11 +885,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(MoeArgs a, DecPub
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
     ex.scales = nullptr;
   } else if (kLgt) {
-    // every token's table column into LDS (wave w: tokens w, w + NW, ...; lane e: row e),
-    // then every wave reads the rows and picks the workgroup's expert by ballots
-    dec_lgt_ranks<NW>(a, lgt, wave, lane, [&](int, int t, int b) { s_tab[lane * kDecTok + t] = (uint8_t)b; });
-    __syncthreads();
-    const DecSelRow srow{*reinterpret_cast<const uint4*>(&s_tab[lane * kDecTok]), lgt.slot};
+    // the table rows (lane e: row e), then the workgroup's expert by ballots
+    const DecSelRow srow{dec_lgt_rows<NW>(a, lgt, wave, lane, s_keys, s_tab), lgt.slot};
     if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) return;
     if (slot < 0) {
       if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
@@ -1073,6 +1095,7 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     *reinterpret_cast<uint4*>(L.xs + kDecTok * kDecXS + i * 8) = make_uint4(0u, 0u, 0u, 0u);
   constexpr bool kLgt = SRC == kSrcLgt;
   __shared__ __attribute__((aligned(16))) uint8_t s_tab[64 * kDecTok];   // logit routing: table rows
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kLgt ? NW * 64 : 4];   // logit routing: keys
   DecPre pre;
   DecLgt<NW> lgt;
   if (kLgt) lgt = dec_lgt_load<NW>(a, pub, wave, lane);
@@ -1085,11 +1108,8 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
   DecExpert ex;
   DecSelTok stok;
   if (kLgt) {
-    // every token's table column into LDS (wave w: token w; lane e: row e), then every
-    // wave reads the rows and picks the workgroup's expert by ballots
-    dec_lgt_ranks<NW>(a, lgt, wave, lane, [&](int, int t, int b) { s_tab[lane * kDecTok + t] = (uint8_t)b; });
-    __syncthreads();
-    const DecSelRow srow{*reinterpret_cast<const uint4*>(&s_tab[lane * kDecTok]), lgt.slot};
+    // the table rows (lane e: row e), then the workgroup's expert by ballots
+    const DecSelRow srow{dec_lgt_rows<NW>(a, lgt, wave, lane, s_keys, s_tab), lgt.slot};
     int slot = 0;
     if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) return;
     if (slot < 0) {
