@@ -283,6 +283,28 @@ def test_olmoe_decode(exm, olmoe, T):
         check_y(got["y"], ref["y"], f"decode T={T} path={path}")
 
 
+@pytest.mark.parametrize("T,k,renormalize,biased", [(1, 8, True, False), (2, 8, False, True), (5, 1, True, False),
+                                                    (7, 16, True, False), (9, 8, True, False), (16, 4, True, True),
+                                                    (16, 8, False, True), (3, 64, True, False)])
+def test_olmoe_logit_routed_decode(exm, olmoe, T, k, renormalize, biased):
+    """Decode with E <= 64 and table-sized batches: the routing kernel writes only the
+    logits and every expert workgroup makes the top-k selection itself (the narrow kernel,
+    the 8-wave launch of the active experts with one or two tokens per wave, and the
+    16-wave launch of every expert); the publisher writes ids and weights. Other k than the
+    layer's own (1 to E), full-softmax weights and a logit bias; the same experts."""
+    import copy
+    import dataclasses
+    lay = copy.copy(olmoe)
+    lay.shape = dataclasses.replace(OLMOE, k=k)
+    x = olmoe.syn.x(T, stream=70 + T)
+    bias = olmoe.syn.zipf_bias() if biased else None
+    log(f"olmoe logit-routed decode T={T} k={k} renormalize={renormalize} bias={biased}")
+    ref = oracle_layer(lay, x, bias=bias, renormalize=renormalize)
+    got = run_layer(exm, lay, x, bias=bias, renormalize=renormalize)
+    check_routing(got, ref, f"T={T} k={k}")
+    check_y(got["y"], ref["y"], f"T={T} k={k}")
+
+
 @pytest.mark.parametrize("T", [128, 512, 2048])
 def test_olmoe_prefill_zipf(exm, olmoe, T):
     log(f"olmoe prefill T={T} (Zipf-biased routing)")
