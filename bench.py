@@ -33,7 +33,7 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; % HBM BW (decode) / % bf16 MFMA (prefi
 # The expert kernel each OLMoE-shaped decode size launches (kernel-trace name and grid).
 DECODE_KERNEL = {1: ("decode_narrow_kernel<3>", "257x1x1 wg1024"),
                  4: ("decode_fused_kernel<3, false, 8>", "257x1x1 wg512"),
-                 16: ("decode_fused_kernel<2, true, 16>", "257x1x1 wg1024")}
+                 16: ("decode_fused_kernel<3, true, 16>", "257x1x1 wg1024")}
 
 
 def log(msg):
