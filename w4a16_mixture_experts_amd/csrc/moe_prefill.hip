@@ -36,15 +36,20 @@ constexpr int kLdsStride = kGroup;         // bf16 elements per LDS row (256 B; 
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row_pf[kMaxDim];
 
 // Which expert / token tile / row tile this workgroup owns. Token tiles are counted per
-// expert (ceil(count / 128)); a single wave scans the counts (E <= 256).
+// expert (ceil(count / 128)); the full tiles of every expert come first (in expert
+// order), then the ragged last tiles: workgroups are dispatched in index order, so the
+// long ones start first and the short ones fill in behind them (under skewed routing
+// the full tiles of the popular experts would otherwise end the launch alone). A single
+// wave scans the counts (E <= 256).
 struct PfTile {
   int e, seg0, cnt, tok0;
 };
 
 __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTile& t,
-                           int* s_scan, int* s_off) {
-  // s_scan: LDS int[kMaxExperts + 1] of exclusive token-tile prefix sums; s_off: LDS
-  // int[kMaxExperts + 1], the segment offsets (loaded once, all at a time)
+                           int* s_full, int* s_part, int* s_off) {
+  // s_full / s_part: LDS int[kMaxExperts + 1] of exclusive prefix sums of the full tiles
+  // and of the ragged tiles (0 or 1) per expert; s_off: LDS int[kMaxExperts + 1], the
+  // segment offsets (loaded once, all at a time)
   const int tid = threadIdx.x;
   if (fixed_expert >= 0) {
     t.e = fixed_expert;
@@ -60,43 +65,58 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
       const int e = tid * 4 + q;
       o[q] = a.offsets[e <= a.E ? e : a.E];
     }
-    int v[4], run = 0;
+    int vf[4], vp[4], run_f = 0, run_p = 0;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int e = tid * 4 + q;
-      v[q] = e < a.E ? (o[q + 1] - o[q] + kPfBN - 1) / kPfBN : 0;
-      run += v[q];
+      const int c = e < a.E ? o[q + 1] - o[q] : 0;
+      vf[q] = c / kPfBN;
+      vp[q] = c % kPfBN != 0 ? 1 : 0;
+      run_f += vf[q];
+      run_p += vp[q];
       s_off[e] = o[q];
     }
     if (tid == 63) s_off[kMaxExperts] = o[4];
-    int incl = run;
+    int incl_f = run_f, incl_p = run_p;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += o;
+      const int uf = __shfl_up(incl_f, off, 64), up = __shfl_up(incl_p, off, 64);
+      if (tid >= off) {
+        incl_f += uf;
+        incl_p += up;
+      }
     }
-    int excl = incl - run;
+    int ef = incl_f - run_f, ep = incl_p - run_p;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      s_scan[tid * 4 + q] = excl;
-      excl += v[q];
+      s_full[tid * 4 + q] = ef;
+      s_part[tid * 4 + q] = ep;
+      ef += vf[q];
+      ep += vp[q];
     }
-    if (tid == 63) s_scan[kMaxExperts] = incl;
+    if (tid == 63) {
+      s_full[kMaxExperts] = incl_f;
+      s_part[kMaxExperts] = incl_p;
+    }
   }
   __syncthreads();
-  if (tt_lin >= s_scan[kMaxExperts]) return false;
-  // The owner is the largest e with s_scan[e] <= tt_lin: an empty expert shares its
-  // prefix value with the next one, so the largest such e always has tiles.
+  const int nfull = s_full[kMaxExperts];
+  const bool full = tt_lin < nfull;
+  const int idx = full ? tt_lin : tt_lin - nfull;
+  const int* scan = full ? s_full : s_part;
+  if (!full && idx >= s_part[kMaxExperts]) return false;
+  // The owner is the largest e with scan[e] <= idx: an expert without such tiles shares
+  // its prefix value with the next one, so the largest such e always has one.
   int lo = 0, hi = a.E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (s_scan[mid] <= tt_lin) lo = mid; else hi = mid - 1;
+    if (scan[mid] <= idx) lo = mid; else hi = mid - 1;
   }
   const int e = lo;
   t.e = e;
   t.seg0 = s_off[e];
   t.cnt = s_off[e + 1] - t.seg0;
-  t.tok0 = (tt_lin - s_scan[e]) * kPfBN;
+  t.tok0 = full ? (idx - s_full[e]) * kPfBN : t.cnt / kPfBN * kPfBN;
   return t.tok0 < t.cnt;
 }
 
@@ -125,7 +145,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   // for the copies into the other
   __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
   __shared__ __attribute__((aligned(16))) float s_seed0[kPfBN], s_seed1[kPfBN];
-  __shared__ int s_scan[kMaxExperts + 1], s_off[kMaxExperts + 1];
+  __shared__ int s_full[kMaxExperts + 1], s_part[kMaxExperts + 1], s_off[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) float s_gsum[NW][kPfBN];
 
   span_begin(a.span);
@@ -134,7 +154,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   const int rt = blockIdx.x % n_row_tiles;
   const int tt_lin = blockIdx.x / n_row_tiles;
   PfTile pt;
-  if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_scan, s_off)) return;
+  if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_full, s_part, s_off)) return;
   const int slot = a.e2s ? a.e2s[pt.e] : pt.e;
   if (slot < 0) {
     if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
