@@ -175,7 +175,7 @@ typedef struct exmoe_expert_bank {
 enum {
   EXMOE_PATH_AUTO = 0,       /* choose by rows per active expert */
   EXMOE_PATH_DECODE = 1,     /* split-K GEMV-style kernels, 16-token MFMA tiles */
-  EXMOE_PATH_PREFILL = 2,    /* grouped GEMM kernels, large token tiles */
+  EXMOE_PATH_PREFILL = 2,    /* grouped GEMM kernels, 64- or 128-token tiles */
   EXMOE_PATH_SEQUENTIAL = 3, /* per-expert launches in ascending expert order (reference
                                 W4 path; synchronizes once to read the offsets) */
   EXMOE_PATH_MASK = 0xff,

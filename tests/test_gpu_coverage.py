@@ -256,10 +256,10 @@ def test_debug_counters_tiny_paths(exm, tiny_bf16, T, path, bf16):
     assert np.array_equal(rows, np.bincount(ids.reshape(-1), minlength=tiny_bf16.shape.E))
 
 
-@pytest.mark.parametrize("T,bias", [(1, False), (4, False), (16, False), (128, True), (512, True)])
+@pytest.mark.parametrize("T,bias", [(1, False), (4, False), (16, False), (64, True), (512, True)])
 def test_debug_counters_olmoe_paths(exm, olmoe_packed, T, bias):
     """The OLMoE-shaped layer on the paths its sizes choose: narrow kernel (1 token), fused
-    decode (4 and 16 tokens, table-routed), pass-parallel fused decode (128 tokens, Zipf
+    decode (4 and 16 tokens, table-routed), pass-parallel fused decode (64 tokens, Zipf
     skew) and the grouped GEMM (512 tokens, Zipf skew)."""
     x = olmoe_packed.syn.x(T, stream=900 + T)
     b = olmoe_packed.syn.zipf_bias() if bias else None

@@ -370,12 +370,12 @@ static int choose_path(int T, int H, int I, int E, int k, int flags) {
   const long long act = std::min<long long>(E, rows);
   if (T <= 16) return EXMOE_PATH_DECODE;
   // Routed rows per possibly-active expert at which the grouped GEMM catches up, measured
-  // on the OLMoE shape: about 30 with the pass-parallel fused decode kernel (uniform
-  // routing 256 tokens: 121 vs 135 us; under Zipf skew the two tie there), about 16 for
-  // the two-kernel decode path and for the bf16 comparator's decode kernels (one
+  // on the OLMoE shape: about 10 against the pass-parallel fused decode kernel (64 tokens:
+  // 62 vs 72 us; 96 tokens: 80 vs 76 us under Zipf skew, 88 vs 71 us uniform), about 16
+  // for the two-kernel decode path and for the bf16 comparator's decode kernels (one
   // workgroup walks its expert's passes).
   const bool fused = !(flags & EXMOE_WEIGHTS_BF16) && decode_fused_waves(T, H, I, E, k) != 0;
-  if (rows <= (fused ? 30 : 16) * act) return EXMOE_PATH_DECODE;
+  if (rows <= (fused ? 10 : 16) * act) return EXMOE_PATH_DECODE;
   return EXMOE_PATH_PREFILL;
 }
 

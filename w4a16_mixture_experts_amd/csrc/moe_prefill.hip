@@ -26,7 +26,7 @@
 
 namespace exmoe {
 
-constexpr int kPfBN = 128;                 // tokens per workgroup tile
+constexpr int kPfBN = 128;                 // tokens per token tile of long segments (and the down seeds' row padding)
 constexpr int kPfWaves = 8;                // waves per workgroup (2 row subtiles each)
 constexpr int kPfRows = 256;               // output rows per workgroup tile
 constexpr int kLdsStride = kGroup;         // bf16 elements per LDS row (256 B; 16-byte chunks swizzled)
@@ -45,6 +45,7 @@ struct PfTile {
   int e, seg0, cnt, tok0;
 };
 
+template <int BN>
 __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTile& t,
                            int* s_full, int* s_part, int* s_off) {
   // s_full / s_part: LDS int[kMaxExperts + 1] of exclusive prefix sums of the full tiles
@@ -55,7 +56,7 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
     t.e = fixed_expert;
     t.seg0 = a.offsets[t.e];
     t.cnt = a.offsets[t.e + 1] - t.seg0;
-    t.tok0 = tt_lin * kPfBN;
+    t.tok0 = tt_lin * BN;
     return t.tok0 < t.cnt;
   }
   if (tid < 64) {
@@ -70,8 +71,8 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
     for (int q = 0; q < 4; q++) {
       const int e = tid * 4 + q;
       const int c = e < a.E ? o[q + 1] - o[q] : 0;
-      vf[q] = c / kPfBN;
-      vp[q] = c % kPfBN != 0 ? 1 : 0;
+      vf[q] = c / BN;
+      vp[q] = c % BN != 0 ? 1 : 0;
       run_f += vf[q];
       run_p += vp[q];
       s_off[e] = o[q];
@@ -116,7 +117,7 @@ __device__ bool pf_resolve(const MoeArgs& a, int fixed_expert, int tt_lin, PfTil
   t.e = e;
   t.seg0 = s_off[e];
   t.cnt = s_off[e + 1] - t.seg0;
-  t.tok0 = full ? (idx - s_full[e]) * kPfBN : t.cnt / kPfBN * kPfBN;
+  t.tok0 = full ? (idx - s_full[e]) * BN : t.cnt / BN * BN;
   return t.tok0 < t.cnt;
 }
 
@@ -135,18 +136,21 @@ __device__ __forceinline__ void dma4(const void* src, void* dst) {
 // scale) and 4 consecutive tokens (one float4 of correction seeds).
 // Q4 = false: the bank holds dense bf16 experts (the comparator), 1 KiB tiles of 16 rows x
 // 32 columns in operand order, four per 128-column group; no scales and no seeds.
-template <bool GATEUP, int NW, bool Q4>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixed_expert,
-                                                           int n_row_tiles) {
+template <bool GATEUP, int NW, int BN, bool Q4>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int fixed_expert,
+                                                                int n_row_tiles) {
   constexpr int NT = NW * 64;            // threads
   constexpr int NA = 16 / NW;            // row subtiles per wave
   constexpr int NL = Q4 ? 1 : 4;         // 16-byte weight loads per lane, row subtile and group
+  constexpr int NB = BN / 16;            // token subtiles per wave (all of the tile's tokens)
+  constexpr int NP = NB / 2;             // token subtile pairs
+  constexpr int kSeedWaves = BN / 64;    // waves that stage the correction seeds (64 each)
   // two buffers as separate arrays: the compiler then sees that reading one does not wait
   // for the copies into the other
-  __shared__ __attribute__((aligned(16))) uint16_t s_act0[kPfBN * kLdsStride], s_act1[kPfBN * kLdsStride];
-  __shared__ __attribute__((aligned(16))) float s_seed0[kPfBN], s_seed1[kPfBN];
+  __shared__ __attribute__((aligned(16))) uint16_t s_act0[BN * kLdsStride], s_act1[BN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) float s_seed0[BN], s_seed1[BN];
   __shared__ int s_full[kMaxExperts + 1], s_part[kMaxExperts + 1], s_off[kMaxExperts + 1];
-  __shared__ __attribute__((aligned(16))) float s_gsum[NW][kPfBN];
+  __shared__ __attribute__((aligned(16))) float s_gsum[NW][BN];
 
   span_begin(a.span);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   const int rt = blockIdx.x % n_row_tiles;
   const int tt_lin = blockIdx.x / n_row_tiles;
   PfTile pt;
-  if (!pf_resolve(a, fixed_expert, tt_lin, pt, s_full, s_part, s_off)) return;
+  if (!pf_resolve<BN>(a, fixed_expert, tt_lin, pt, s_full, s_part, s_off)) return;
   const int slot = a.e2s ? a.e2s[pt.e] : pt.e;
   if (slot < 0) {
     if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   // Rows past the segment read the zero row.
   // (the gathered row indices are loaded at clamped positions, all at once, and the rows
   // past the segment are then pointed at the zero row)
-  constexpr int kDmaPerWave = kPfBN / 4 / NW;
+  constexpr int kDmaPerWave = BN / 4 / NW;
   const uint16_t* drow[kDmaPerWave];
   int grow[kDmaPerWave];
 #pragma unroll
@@ -219,25 +223,25 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   const float* seed_src;
   size_t seed_stride;
   if (GATEUP) {
-    const int r = pt.tok0 + (wave & 1) * 64 + lane;
+    const int r = pt.tok0 + (wave % kSeedWaves) * 64 + lane;
     seed_src = a.xsum + (r < pt.cnt ? a.sorted_flat[pt.seg0 + r] / a.k : 0);
     seed_stride = (size_t)a.T;
   } else {
-    seed_src = a.gsum + pt.seg0 + pt.tok0 + (wave & 1) * 64 + lane;
+    seed_src = a.gsum + pt.seg0 + pt.tok0 + (wave % kSeedWaves) * 64 + lane;
     seed_stride = (size_t)rows_pad;
   }
 #define EXMOE_STAGE(g_, ACT, SEED)                                                                      \
   do {                                                                                                  \
     _Pragma("unroll") for (int i = 0; i < kDmaPerWave; i++)                                             \
         dma16(drow[i] + (g_) * kGroup, &ACT[(wave * kDmaPerWave + i) * 4 * kLdsStride]);                \
-    if (Q4 && wave < 2) dma4(seed_src + (size_t)(g_) * seed_stride, &SEED[wave * 64]);                  \
+    if (Q4 && wave < kSeedWaves) dma4(seed_src + (size_t)(g_) * seed_stride, &SEED[wave * 64]);         \
   } while (0)
 
-  f32x4 acc[NA][8];
+  f32x4 acc[NA][NB];
 #pragma unroll
   for (int ai = 0; ai < NA; ai++)
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bj = 0; bj < NB; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 wcur[NA][NL], wnext[NA][NL];
   uint32_t scur[NA], snext[NA];
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
 
   // Token subtile pairs (32 tokens) that hold rows of the segment: the last token tile of
   // an expert is often mostly padding, and its MFMAs on padding rows are skipped.
-  const int npairs = pt.cnt - pt.tok0 >= kPfBN ? 4 : (pt.cnt - pt.tok0 + 31) / 32;
+  const int npairs = pt.cnt - pt.tok0 >= BN ? NP : (pt.cnt - pt.tok0 + 31) / 32;
 
   // One group: compute it from (cact, cseed) while the next one lands in (nact, nseed).
   // full: every pair holds rows (no skip tests in the MFMA stream).
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     for (int ai = 0; ai < NA; ai++) sc[ai] = Q4 ? __uint_as_float(scur[ai] << 16) : 1.0f;
     // token subtiles in pairs: activation fragments of both for all 4 K steps
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
+    for (int p = 0; p < NP; p++) {
       if constexpr (!decltype(full)::value) {
         if (p >= npairs) break;
       }
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
       scur[ai] = snext[ai];
     }
   };
-  if (npairs == 4) {
+  if (npairs == NP) {
     for (int g = 0; g < G; g += 2) {
       group(std::true_type{}, g, s_act0, s_seed0, s_act1, s_seed1);
       if (g + 1 < G) group(std::true_type{}, g + 1, s_act1, s_seed1, s_act0, s_seed0);
@@ -361,9 +365,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
   // bj*16 + 4(l/16) + i of each token subtile
   const int tl0 = 4 * (lane >> 4);
   if (GATEUP) {
-    float gpart[8][4];
+    float gpart[NB][4];
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++)
+    for (int bj = 0; bj < NB; bj++)
 #pragma unroll
       for (int i = 0; i < 4; i++) gpart[bj][i] = 0.f;
 #pragma unroll
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
       const int nv = pt.cnt - pt.tok0 - tl0;
       auto store = [&](auto full) {
 #pragma unroll
-        for (int bj = 0; bj < 8; bj++) {
+        for (int bj = 0; bj < NB; bj++) {
           const f32x4 gv = acc[2 * rbl][bj], uv = acc[2 * rbl + 1][bj];
 #pragma unroll
           for (int i = 0; i < 4; i++) {
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
           }
         }
       };
-      if (pt.cnt - pt.tok0 >= kPfBN) store(std::true_type{});
+      if (pt.cnt - pt.tok0 >= BN) store(std::true_type{});
       else store(std::false_type{});
     }
     // per-token sum over this workgroup's 128 intermediate columns (one down group):
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     if (Q4) {
     auto rot_add = [&](auto ctrl) {
 #pragma unroll
-      for (int bj = 0; bj < 8; bj++)
+      for (int bj = 0; bj < NB; bj++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
           gpart[bj][i] += __uint_as_float(dpp_u32<decltype(ctrl)::value>(__float_as_uint(gpart[bj][i])));
@@ -407,12 +411,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     rot_add(std::integral_constant<int, 0x128>{});
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int bj = 0; bj < 8; bj++)
+      for (int bj = 0; bj < NB; bj++)
         *reinterpret_cast<float4*>(&s_gsum[wave][bj * 16 + tl0]) =
             make_float4(gpart[bj][0], gpart[bj][1], gpart[bj][2], gpart[bj][3]);
     }
     __syncthreads();
-    if (tid < kPfBN) {
+    if (tid < BN) {
       const int r = pt.tok0 + tid;
       if (r < pt.cnt) {
         float v = s_gsum[0][tid];
@@ -426,22 +430,22 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
     // y_perm rows are in flat (token, slot) order: every row index and routing weight of the
     // lane's 32 tokens is loaded first (rows past the segment read row 0, unused) and waited
     // for once, instead of one round trip per row between stores (which also count in vmcnt)
-    int fr[8][4];
-    float wr[8][4];
+    int fr[NB][4];
+    float wr[NB][4];
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++)
+    for (int bj = 0; bj < NB; bj++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = pt.tok0 + bj * 16 + tl0 + i;
         fr[bj][i] = a.sorted_flat[pt.seg0 + (r < pt.cnt ? r : 0)];
       }
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++)
+    for (int bj = 0; bj < NB; bj++)
 #pragma unroll
       for (int i = 0; i < 4; i++) wr[bj][i] = a.w[fr[bj][i]];
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int bj = 0; bj < 8; bj++)
+    for (int bj = 0; bj < NB; bj++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = pt.tok0 + bj * 16 + tl0 + i;
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(MoeArgs a, int fixe
         }
       }
     // exactness counter: the first row tile of each token tile counts the tile's rows
-    if (a.rows_ctr && rt == 0 && tid == 0) atomicAdd(a.rows_ctr + pt.e, min(kPfBN, pt.cnt - pt.tok0));
+    if (a.rows_ctr && rt == 0 && tid == 0) atomicAdd(a.rows_ctr + pt.e, min(BN, pt.cnt - pt.tok0));
   }
   span_end(a.span);
 }
@@ -487,17 +491,18 @@ hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool Q4>
-static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
+// NW waves per workgroup and BN tokens per token tile; the row tile is 256 rows either way.
+template <bool Q4, int NW, int BN>
+static hipError_t launch_prefill_tiles(const MoeArgs& a, hipStream_t s) {
   const int TK = a.T * a.k;
-  const int max_tt = TK / kPfBN + (a.E < TK ? a.E : TK);
+  const int max_tt = TK / BN + (a.E < TK ? a.E : TK);
   const int rt_gu = a.I / 128;
   {
     ProfScope prof(Q4 ? "prefill_gateup" : "bf16_prefill_gateup", s);
     MoeArgs as = a;
     as.span = prof.span();
-    EXMOE_LAUNCH(prof, (prefill_kernel<true, kPfWaves, Q4>), dim3(max_tt * rt_gu), dim3(kPfWaves * 64), 0, s, as,
-                 -1, rt_gu);
+    EXMOE_LAUNCH(prof, (prefill_kernel<true, NW, BN, Q4>), dim3(max_tt * rt_gu), dim3(NW * 64), 0, s, as, -1,
+                 rt_gu);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -506,10 +511,23 @@ static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
     ProfScope prof(Q4 ? "prefill_down" : "bf16_prefill_down", s);
     MoeArgs as = a;
     as.span = prof.span();
-    EXMOE_LAUNCH(prof, (prefill_kernel<false, kPfWaves, Q4>), dim3(max_tt * rt_d), dim3(kPfWaves * 64), 0, s, as,
-                 -1, rt_d);
+    EXMOE_LAUNCH(prof, (prefill_kernel<false, NW, BN, Q4>), dim3(max_tt * rt_d), dim3(NW * 64), 0, s, as, -1,
+                 rt_d);
   }
   return hipGetLastError();
+}
+
+// Short segments (at most 64 routed rows per expert on average) take 64-token tiles on
+// 4-wave workgroups, two per compute unit, so that one workgroup's memory round trips
+// overlap the other's MFMAs; longer ones take 128-token tiles on 8-wave workgroups. The
+// bf16 comparator keeps the 128-token tiles (its 4-wave form runs out of registers: four
+// 16-byte weight loads per row subtile and group).
+template <bool Q4>
+static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
+  if constexpr (Q4) {
+    if ((long)a.T * a.k <= 64L * a.E) return launch_prefill_tiles<Q4, 4, 64>(a, s);
+  }
+  return launch_prefill_tiles<Q4, kPfWaves, kPfBN>(a, s);
 }
 
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<true>(a, s); }
