@@ -331,8 +331,8 @@ def prefill_roofline(rec, read_kernel_avg):
            "gemm_pair_ms_events": rec.get("gemm_pair_ms"), "gemm_pair_frac_events": rec.get("gemm_pair_mfma_frac"),
            "gateup_frac_events": rec.get("gateup_mfma_frac"), "down_frac_events": rec.get("down_mfma_frac")}
     path = os.path.join(ROOT, "profiles", "kernel_trace_large_prefill_T4096.txt")
-    gu = read_kernel_avg(path, "prefill_kernel<true, 8, 128, true>", "8064x1x1 wg512")
-    dn = read_kernel_avg(path, "prefill_kernel<false, 8, 128, true>", "1152x1x1 wg512")
+    gu = read_kernel_avg(path, "prefill_kernel<true, 4, 64, true>", "15232x1x1 wg256")
+    dn = read_kernel_avg(path, "prefill_kernel<false, 4, 64, true>", "2176x1x1 wg256")
     if gu and dn:
         out["gemm_pair_ms_rocprof_median"] = (gu[1] + dn[1]) * 1e-3
         out["gemm_pair_frac_rocprof_median"] = flops / ((gu[1] + dn[1]) * 1e-6) / 1e12 / BF16_PEAK_TFLOPS

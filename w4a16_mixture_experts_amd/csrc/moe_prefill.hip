@@ -1,8 +1,10 @@
 // Prefill-sized expert layer (many tokens per expert): grouped GEMMs on bf16 MFMA, gfx950.
 //
 // Every selected expert runs over the tokens grouped to it (ExactMoE abstract; Fig. 1).
-// One workgroup (8 waves, two per SIMD) computes a 256-row x 128-token output tile of one
-// expert; each wave owns 32 rows (two 16-row subtiles) x all 128 tokens:
+// A workgroup computes a 256-row x BN-token output tile of one expert. int4 experts take
+// BN = 64 on 4 waves (one per SIMD, two workgroups per compute unit), each wave owning 64
+// rows (four 16-row subtiles) x all 64 tokens; the bf16 comparator takes BN = 128 on 8
+// waves (two per SIMD), each owning 32 rows x all 128 tokens. The rows:
 //   gate/up: rows = 128 gate rows + the matching 128 up rows (one 128-wide slice of the
 //            intermediate dimension), epilogue h = bf16(silu(g) * u) plus the fp32 sum of
 //            each token's 128 rounded h values (the down kernel's dequant correction);
@@ -15,9 +17,9 @@
 // wave-wide 128-bit load, prefetched a group ahead) and become exact bf16 operands 128 + u
 // in registers. Each group's MFMA chain starts from -136 * (group sum of the activations:
 // per token for gate/up, per routed row of h for down), so it ends at sum(x * q); the bf16
-// scale of the row is applied once per group in fp32. A wave dequantizes its 2 row
-// subtiles of a group once and reuses them across the 8 token subtiles (16 tokens each).
-// Q4 = false runs the same tiling on dense bf16 experts (the comparator): the weight
+// scale of the row is applied once per group in fp32. A wave dequantizes its row subtiles
+// of a group once and reuses them across all token subtiles of the tile (16 tokens each).
+// Q4 = false runs the same loop on dense bf16 experts (the comparator): the weight
 // fragments are loaded as they are, with no scales and no seeds.
 #include <type_traits>
 
@@ -26,8 +28,8 @@
 
 namespace exmoe {
 
-constexpr int kPfBN = 128;                 // tokens per token tile of long segments (and the down seeds' row padding)
-constexpr int kPfWaves = 8;                // waves per workgroup (2 row subtiles each)
+constexpr int kPfBN = 128;                 // tokens per token tile of the bf16 comparator (and the down seeds' row padding)
+constexpr int kPfWaves = 8;                // waves per workgroup of the bf16 comparator (2 row subtiles each)
 constexpr int kPfRows = 256;               // output rows per workgroup tile
 constexpr int kLdsStride = kGroup;         // bf16 elements per LDS row (256 B; 16-byte chunks swizzled)
 
@@ -131,9 +133,10 @@ __device__ __forceinline__ void dma4(const void* src, void* dst) {
 }
 
 // NW waves per workgroup; each wave owns NA = 16 / NW row subtiles (of 16 rows) and all
-// 8 token subtiles of the 256 x 128 tile. Tokens are the M operand of the MFMA and weight
-// rows the N operand, so a lane's 4 accumulator values belong to one weight row (one
-// scale) and 4 consecutive tokens (one float4 of correction seeds).
+// BN / 16 token subtiles of the 256 x BN tile. Tokens are the M operand of the MFMA and
+// weight rows the N operand, so a lane's 4 accumulator values belong to one weight row
+// (one scale) and 4 consecutive tokens (one float4 of correction seeds). 8 / NW waves per
+// SIMD: with NW = 4, two workgroups share a compute unit.
 // Q4 = false: the bank holds dense bf16 experts (the comparator), 1 KiB tiles of 16 rows x
 // 32 columns in operand order, four per 128-column group; no scales and no seeds.
 template <bool GATEUP, int NW, int BN, bool Q4>
@@ -517,17 +520,18 @@ static hipError_t launch_prefill_tiles(const MoeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Short segments (at most 64 routed rows per expert on average) take 64-token tiles on
-// 4-wave workgroups, two per compute unit, so that one workgroup's memory round trips
-// overlap the other's MFMAs; longer ones take 128-token tiles on 8-wave workgroups. The
-// bf16 comparator keeps the 128-token tiles (its 4-wave form runs out of registers: four
-// 16-byte weight loads per row subtile and group).
+// int4 experts: 64-token tiles on 4-wave workgroups, two per compute unit, so that the
+// waves sharing a SIMD belong to different workgroups and their barriers, memory round
+// trips, unpacking and MFMAs overlap (against 128-token tiles on 8-wave workgroups:
+// Zipf 512 tokens 0.164 -> 0.143 ms per layer, 2048 tokens 0.372 -> 0.342 ms, large layer
+// 2.86 -> 2.85 ms). The bf16 comparator keeps the 128-token tiles: its 4-wave form runs
+// out of registers (four 16-byte weight loads per row subtile and group).
 template <bool Q4>
 static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
-  if constexpr (Q4) {
-    if ((long)a.T * a.k <= 64L * a.E) return launch_prefill_tiles<Q4, 4, 64>(a, s);
-  }
-  return launch_prefill_tiles<Q4, kPfWaves, kPfBN>(a, s);
+  if constexpr (Q4)
+    return launch_prefill_tiles<Q4, 4, 64>(a, s);
+  else
+    return launch_prefill_tiles<Q4, kPfWaves, kPfBN>(a, s);
 }
 
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<true>(a, s); }
