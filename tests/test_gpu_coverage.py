@@ -25,14 +25,14 @@ def exm():
 
 
 # ------------------------------------------------------------------ large-expert prefill, every expert
-def _segment_rows(sf, off, e, k):
-    """Tokens of expert e's first row, of the first row of its last 128-row tile (the
+def _segment_rows(sf, off, e, k, tile=64):
+    """Tokens of expert e's first row, of the first row of its last `tile`-row tile (the
     ragged one the kernel masks), of the row before it and of its last row."""
     seg = sf[off[e]:off[e + 1]]
     n = len(seg)
     if n == 0:
         return set()
-    last_tile = (n - 1) // 128 * 128
+    last_tile = (n - 1) // tile * tile
     picks = {0, n - 1, last_tile, max(last_tile - 1, 0)}
     return {int(seg[i]) // k for i in picks}
 
@@ -376,6 +376,33 @@ def test_table_routed_layer_equals_separate_calls(exm, olmoe_packed, T):
     again = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k, buffers=out)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_dev_to_bits(again.y), bf16_dev_to_bits(y_sep)), "second call on the same workspace differs"
+
+
+@pytest.mark.parametrize("shape,T", [("olmoe", 100), ("olmoe", 300), ("wide", 100), ("wide", 200)])
+def test_prefill_layer_seeds_equal_separate_calls(exm, olmoe_packed, shape, T):
+    """At prefill sizes the whole-layer call takes the grouped GEMM's correction seeds from
+    the routing kernel (the vector kernel up to 128 tokens, in one pass of loads at hidden
+    2048 and in several at 4096; the fp64 matrix-core kernel above), the separate forward
+    call from a kernel of its own; both sum in one order, so the outputs are equal bit for
+    bit, and the layer call meets the oracle."""
+    import torch
+    if shape == "olmoe":
+        lay = olmoe_packed
+    else:
+        lay = Layer(LayerShape(H=4096, I=256, E=8, k=2), seed=31)
+    s = lay.shape
+    assert T * s.k > 10 * min(s.E, T * s.k), "a grouped-GEMM size"
+    x_bits = lay.syn.x(T, stream=400 + T)
+    x = to_dev_bf16(x_bits)
+    out = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k)
+    y_sep = exm.moe_forward(x, out.ids, out.weights, out.offsets, out.sorted_flat, out.flat_to_sorted, lay.bank, s.I)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(out.y), bf16_dev_to_bits(y_sep))
+    ids = oracle.topk_ids(oracle.router_logits(x_bits, lay.wr_bits), s.k)
+    assert np.array_equal(out.ids.cpu().numpy(), ids)
+    if shape == "wide":   # small enough for the oracle on every token
+        ref = oracle.moe_layer(x_bits, lay.wr_bits, lay.experts, s.k)
+        check_y(bf16_dev_to_f64(out.y), ref["y"], f"wide T={T}")
 
 
 def test_slotless_expert_leaves_workspace_clean(exm, olmoe_packed):

@@ -468,7 +468,7 @@ static void set_row_counters(MoeArgs& a, void* workspace, int flags) {
 static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const float* topk_weights,
                             const int32_t* expert_offsets, const int32_t* sorted_flat, const int32_t* flat_to_sorted,
                             const exmoe_expert_bank* bank, int T, int H, int I, int E, int k, int flags, exmoe_bf16* y,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+                            void* workspace, size_t ws_bytes, hipStream_t stream, bool xsum_ready = false) {
   const int path = choose_path(T, H, I, E, k, flags);
   MoeArgs a{};
   a.x = x; a.ids = topk_ids; a.w = topk_weights; a.offsets = expert_offsets; a.sorted_flat = sorted_flat;
@@ -485,7 +485,9 @@ static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const 
   } else if (path == EXMOE_PATH_DECODE) {
     EXMOE_HIP(launch_moe_decode(a, stream));
   } else if (path == EXMOE_PATH_PREFILL) {
-    EXMOE_HIP(launch_moe_prefill(a, stream));
+    if (!xsum_ready) EXMOE_HIP(launch_moe_prefill_xsum(a, stream));
+    EXMOE_HIP(launch_moe_prefill_experts(a, stream));
+    EXMOE_HIP(launch_combine(a, stream));
   } else {
     // Sequential W4 reference: experts one after another in ascending id, each with its
     // own launches over its gathered rows; one host read of the offsets drives the loop.
@@ -746,12 +748,15 @@ int exmoe_moe_layer(const exmoe_bf16* x, const exmoe_bf16* w_router, const float
     return EXMOE_OK;
   }
   MoeArgs ag{};
-  moe_workspace_layout(T, H, I, E, k, choose_path(T, H, I, E, k, flags), &ag, workspace);
-  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream));
+  const int path = choose_path(T, H, I, E, k, flags);
+  moe_workspace_layout(T, H, I, E, k, path, &ag, workspace);
+  // the grouped GEMM's correction seeds come with the logits (the routing kernel loads x)
+  const bool xs = path == EXMOE_PATH_PREFILL && !(flags & EXMOE_WEIGHTS_BF16) && H <= kLgtXsMaxH;
+  EXMOE_HIP(launch_route_logits(x, w_router, logit_bias, T, H, E, logits, stream, xs ? ag.xsum : nullptr));
   EXMOE_HIP(launch_topk_group(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_flat,
                               flat_to_sorted, ag.group_ws, stream));
   return moe_forward_impl(x, topk_ids, topk_weights, expert_offsets, sorted_flat, flat_to_sorted, bank, T, H, I, E,
-                          k, flags, y, workspace, ws_bytes, stream);
+                          k, flags, y, workspace, ws_bytes, stream, xs);
 }
 
 }  // extern "C"

@@ -85,8 +85,11 @@ hipError_t table_upload(int32_t* dst, const int32_t* host, int n, hipStream_t s)
 // non-empty segment whose bit is clear in mask (the union of the waves' experts).
 hipError_t check_wave_union(const int32_t* offsets, int E, const uint32_t mask[kMaxExperts / 32], uint32_t* debug,
                             hipStream_t s);
+// xsum (optional, fp32 [H/128][T], H <= kLgtXsMaxH): also the grouped GEMM's correction
+// seeds of x, the values launch_moe_prefill_xsum writes.
+constexpr int kLgtXsMaxH = 4096;
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
-                               int E, uint16_t* logits, hipStream_t s);
+                               int E, uint16_t* logits, hipStream_t s, float* xsum = nullptr);
 hipError_t launch_topk(const uint16_t* logits, const int32_t* given_ids, int T, int E, int k,
                        int renormalize, int32_t* ids, float* w, hipStream_t s);
 // group_ws: group_workspace_bytes(T * k, E) bytes (may be null when that is 0)
@@ -164,9 +167,8 @@ bool decode_logit_routing_ok(int T, int H, int I, int E, int k);
 hipError_t launch_moe_decode_logit_routed(const MoeArgs& a, const uint16_t* logits, int renormalize, int32_t* ids,
                                           float* w, int32_t* offsets, int32_t* sorted_flat, int32_t* flat_to_sorted,
                                           hipStream_t s);
-hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s);
-// The same paths in parts (a forward in waves runs the expert kernels once per wave and
-// the correction sums and the combine once): decode experts; prefill sums, experts.
+// The paths in parts (a forward in waves runs the expert kernels once per wave and the
+// correction sums and the combine once): decode experts; prefill sums, experts.
 hipError_t launch_moe_decode_experts(const MoeArgs& a, hipStream_t s);
 // Experts per layer, slots per layer, dry-run flag and bytes per expert of a slot cache.
 void slot_cache_shape(const exmoe_slot_cache* c, int* E, int* S, int* dry, size_t* expert_bytes);

@@ -125,6 +125,32 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// Group sums of the activations (the grouped GEMM's correction seeds) in one order for
+// every kernel that makes them, so that they agree bit for bit: the 8 bf16 of a 16-byte
+// chunk in element order, then the 16 chunk sums of a 128-input group in a balanced
+// pairwise tree in chunk order, ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) + ...
+__device__ __forceinline__ float chunk8_sum(uint4 v) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+  float s = __uint_as_float(q[0] << 16);
+  s += __uint_as_float(q[0] & 0xFFFF0000u);
+#pragma unroll
+  for (int i = 1; i < 4; i++) {
+    s += __uint_as_float(q[i] << 16);
+    s += __uint_as_float(q[i] & 0xFFFF0000u);
+  }
+  return s;
+}
+// The tree over the chunk sums held by the 16 lanes of a row (lane l of the row: chunk l),
+// in every lane of the row: partners at lane distance 1 and 2 (quad permutes), then the
+// other quad of the half row and the other half row (mirrors); each step adds two equal
+// subtrees, so every lane ends with the same bits.
+__device__ __forceinline__ float row16_tree_sum(float v) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));    // quad_perm [1, 0, 3, 2]
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));    // quad_perm [2, 3, 0, 1]
+  v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));   // row_half_mirror
+  v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));   // row_mirror
+  return v;
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   uint32_t o;
   o = dpp_u32<0x121>(v); v = o > v ? o : v;   // row_ror:1

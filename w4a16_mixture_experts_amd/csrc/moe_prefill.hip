@@ -468,7 +468,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
 }
 
 // Correction seeds of the gate/up kernel: xsum[g][t] = -136 * (sum over group g of the
-// activations of token t), fp32, one thread per (token, group).
+// activations of token t), fp32, one thread per (token, group), in the order of
+// chunk8_sum and row16_tree_sum (the routing kernels that also make these sums follow it).
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                    float* __restrict__ xsum) {
   const int G = H / kGroup;
@@ -476,15 +477,14 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
   if (i >= G * T) return;
   const int g = i / T, t = i % T;
   const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + g * kGroup);
-  float s = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < kGroup / 8; c++) {
-    const uint4 v = p[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float c[16];
 #pragma unroll
-    for (int q = 0; q < 4; q++) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
-  }
-  xsum[i] = -136.0f * s;
+  for (int j = 0; j < 16; j++) c[j] = chunk8_sum(p[j]);
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; j += 2 * w) c[j] += c[j + w];
+  xsum[i] = -136.0f * c[0];
 }
 
 hipError_t launch_moe_prefill_xsum(const MoeArgs& a, hipStream_t s) {
@@ -537,11 +537,5 @@ static hipError_t launch_prefill_experts(const MoeArgs& a, hipStream_t s) {
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<true>(a, s); }
 hipError_t launch_bf16_prefill_experts(const MoeArgs& a, hipStream_t s) { return launch_prefill_experts<false>(a, s); }
 
-hipError_t launch_moe_prefill(const MoeArgs& a, hipStream_t s) {
-  hipError_t e = launch_moe_prefill_xsum(a, s);
-  if (e == hipSuccess) e = launch_moe_prefill_experts(a, s);
-  if (e == hipSuccess) e = launch_combine(a, s);
-  return e;
-}
 
 }  // namespace exmoe

@@ -12,15 +12,16 @@
 
 namespace exmoe {
 
-// ONE: H <= 8 LANES MC, one pass of loads per wave.
-template <int TB, int EB, int LANES, int MC, bool ONE>
+// ONE: H <= 8 LANES MC, one pass of loads per wave. XS: also the grouped GEMM's
+// correction seeds (route_logits_wave).
+template <int TB, int EB, int LANES, int MC, bool ONE, bool XS>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias, int T,
                                                           int H, int E,
-                                                          uint16_t* __restrict__ logits) {
-  route_logits_wave<TB, EB, LANES, MC, false, ONE>(x, wr, bias, T, H, E, logits,
-                                                  blockIdx.x * (64 / LANES) + (int)lane_id() / LANES);
+                                                          uint16_t* __restrict__ logits, float* __restrict__ xsum) {
+  route_logits_wave<TB, EB, LANES, MC, false, ONE, XS>(x, wr, bias, T, H, E, logits,
+                                                      blockIdx.x * (64 / LANES) + (int)lane_id() / LANES, xsum);
 }
 
 // ---------------------------------------------------------------------------------
@@ -33,14 +34,22 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 // MFMA j are columns {8 g + j}. The products of bf16 values are exact in fp64 and the sum
 // is rounded to bf16 once, as in the vector form.
 // ---------------------------------------------------------------------------------
+// XS (H <= kLgtXsMaxH): the workgroups also write the grouped GEMM's correction seeds of
+// their 16 tokens, xsum[g][t] = -136 * (sum of group g of token t), from the activation
+// chunks they load (group g by the workgroup of expert block g mod the block count), in
+// the order of chunk8_sum and row16_tree_sum: each lane's 16-byte chunk sums go to LDS,
+// and after the loop one thread per (group, token) adds the group's 16 in that tree.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kLgtXsMaxG = kLgtXsMaxH / kGroup;
 
-template <int KW>
+template <int KW, bool XS>
 __global__ __launch_bounds__(64 * KW) void route_logits_mfma_kernel(const uint16_t* __restrict__ x,
                                                                     const uint16_t* __restrict__ wr,
                                                                     const float* __restrict__ bias, int T, int H,
-                                                                    int E, uint16_t* __restrict__ logits) {
+                                                                    int E, uint16_t* __restrict__ logits,
+                                                                    float* __restrict__ xsum) {
   __shared__ f64x4 red[KW][64];
+  __shared__ float s_x16[XS ? kLgtXsMaxG : 1][16][16];   // [group][16-byte chunk of it][token]
   const int lane = (int)lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nEB = (E + 15) / 16;
@@ -51,7 +60,9 @@ __global__ __launch_bounds__(64 * KW) void route_logits_mfma_kernel(const uint16
   const uint4* wrr = reinterpret_cast<const uint4*>(wr + (size_t)e * H) + g;
   const int nch = H / 32;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  auto chunk = [&](const uint4 xu, const uint4 wu) {
+  const int xeb = (int)blockIdx.x % nEB;
+  auto chunk = [&](const uint4 xu, const uint4 wu, int cc) {
+    if (XS && (cc >> 2) % nEB == xeb) s_x16[cc >> 2][4 * (cc & 3) + g][m] = chunk8_sum(xu);   // wave-uniform test
     const uint32_t xq[4] = {xu.x, xu.y, xu.z, xu.w}, wq[4] = {wu.x, wu.y, wu.z, wu.w};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -69,15 +80,30 @@ __global__ __launch_bounds__(64 * KW) void route_logits_mfma_kernel(const uint16
   for (; c < nch; c += 2 * KW) {
     const uint4 xc = xa, wc = wa;
     if (c + 2 * KW < nch) { xa = xr[4 * (c + 2 * KW)]; wa = wrr[4 * (c + 2 * KW)]; }
-    chunk(xc, wc);
+    chunk(xc, wc, c);
     if (c + KW < nch) {
       const uint4 xd = xb, wd = wb;
       if (c + 3 * KW < nch) { xb = xr[4 * (c + 3 * KW)]; wb = wrr[4 * (c + 3 * KW)]; }
-      chunk(xd, wd);
+      chunk(xd, wd, c + KW);
     }
   }
   red[wave][lane] = acc;
   __syncthreads();
+  if (XS) {
+    for (int i = (int)threadIdx.x; i < (H / kGroup) * 16; i += 64 * KW) {
+      const int gg = i / 16, mm = i % 16;
+      if (gg % nEB == xeb && t0 + mm < T) {
+        float c[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) c[j] = s_x16[gg][j][mm];
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+          for (int j = 0; j < 16; j += 2 * w) c[j] += c[j + w];
+        xsum[(size_t)gg * T + t0 + mm] = -136.0f * c[0];
+      }
+    }
+  }
   if (wave == 0) {
     f64x4 s = red[0][lane];
 #pragma unroll
@@ -267,24 +293,37 @@ hipError_t launch_route_sel(const uint16_t* x, const uint16_t* wr, const float* 
 }
 
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
-                               int E, uint16_t* logits, hipStream_t s) {
+                               int E, uint16_t* logits, hipStream_t s, float* xsum) {
   if (T == 0) return hipSuccess;
+  if (xsum && H > kLgtXsMaxH) return hipErrorInvalidValue;   // the seed sums' LDS rows
   ProfScope prof("route_logits", s);
   if (T <= 128) {
     // one wave per 2 tokens x 2 experts, the whole wave on H: a row in one round trip
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
-    if (H <= kRouteSelMaxH)
-      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, true>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E,
-                   logits);
+    const bool one = H <= kRouteSelMaxH;
+    if (one && xsum)
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, true, true>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T,
+                   H, E, logits, xsum);
+    else if (one)
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, true, false>), dim3(blocks), dim3(64), 0, s, x, wr, bias,
+                   T, H, E, logits, nullptr);
+    else if (xsum)
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, false, true>), dim3(blocks), dim3(64), 0, s, x, wr, bias,
+                   T, H, E, logits, xsum);
     else
-      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, false>), dim3(blocks), dim3(64), 0, s, x, wr, bias, T, H, E,
-                   logits);
+      EXMOE_LAUNCH(prof, (route_logits_kernel<2, 2, 64, 4, false, false>), dim3(blocks), dim3(64), 0, s, x, wr, bias,
+                   T, H, E, logits, nullptr);
   } else {
     // 16 x 16 tiles on the fp64 matrix cores (H is a multiple of 128), H split over 8
     // waves. Measured against four 4 x 4 blocks of vector FMAs per wave: 2048 tokens and
     // 64 experts 30.9 -> 15.5 us, 512 tokens 12.4 -> 8.8 us.
     const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
-    EXMOE_LAUNCH(prof, route_logits_mfma_kernel<8>, dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
+    if (xsum)
+      EXMOE_LAUNCH(prof, (route_logits_mfma_kernel<8, true>), dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E,
+                   logits, xsum);
+    else
+      EXMOE_LAUNCH(prof, (route_logits_mfma_kernel<8, false>), dim3(tiles), dim3(512), 0, s, x, wr, bias, T, H, E,
+                   logits, nullptr);
   }
   return hipGetLastError();
 }

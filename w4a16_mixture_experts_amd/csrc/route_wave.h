@@ -22,11 +22,16 @@ namespace exmoe {
 // ---------------------------------------------------------------------------------
 // WT: write-through (agent-scope atomic) stores of the logits, read back by another
 // workgroup in the same launch. ONE: the caller guarantees H <= 8 LANES MC (one pass of
-// loads, all issued before any arithmetic).
-template <int TB, int EB, int LANES, int MC, bool WT, bool ONE = false>
+// loads, all issued before any arithmetic). XS (LANES = 64): the lane groups also write
+// the grouped GEMM's correction seeds of their tokens from the activation chunks they
+// load, xsum[g][t] = -136 * (sum of group g of token t) in the order of chunk8_sum and
+// row16_tree_sum (a 16-lane row holds the 16 chunks of one group).
+template <int TB, int EB, int LANES, int MC, bool WT, bool ONE = false, bool XS = false>
 __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                   const float* __restrict__ bias, int T, int H, int E,
-                                                  uint16_t* __restrict__ logits, int blk) {
+                                                  uint16_t* __restrict__ logits, int blk,
+                                                  float* __restrict__ xsum = nullptr) {
+  static_assert(!XS || LANES == 64, "seed rows need 16-lane rows of consecutive chunks");
   const int lane = (int)lane_id();
   const int li = lane % LANES;
   const int nEB = (E + EB - 1) / EB;
@@ -67,6 +72,22 @@ __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x
           for (int i = 0; i < TB; i++) xu[i][m] = on ? xu[i][m] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
           for (int j = 0; j < EB; j++) wu[j][m] = on ? wu[j][m] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      if (XS) {
+        // row r of the wave holds chunks c0 + 64 m + 16 r + (0..15), i.e. group
+        // (c0 + 64 m) / 16 + r; group g is summed by the lane groups of expert block
+        // g mod the block count
+#pragma unroll
+        for (int m = 0; m < MC; m++) {
+          const int c = c0 + li + LANES * m, g0 = (c0 + LANES * m) / 16;
+          if ((eb - g0 % nEB + nEB) % nEB >= 4) continue;   // none of the wave's four groups (wave-uniform)
+          const bool mine = (c / 16) % nEB == eb && (li & 15) == 0 && c < chunks;
+#pragma unroll
+          for (int i = 0; i < TB; i++) {
+            const float v = row16_tree_sum(chunk8_sum(xu[i][m]));
+            if (mine && t0 + i < T) xsum[(size_t)(c / 16) * T + t0 + i] = -136.0f * v;
+          }
         }
       }
 #pragma unroll
