@@ -158,11 +158,11 @@ __device__ __forceinline__ void route_logits_wave(const uint16_t* __restrict__ x
 // slot + 1 when token t selected the expert, else 0. It clears the counter, so the
 // counters are zero between launches (and must be zero before the first one). Returns
 // true in that last arriver. The ids, weights and table are read by later launches.
-// Ordering: the logits are written through to the device-coherent level (agent-scope
-// atomic stores) and each wave waits for their completion before its workgroup counts;
-// the last arriver reads them with agent-scope atomic loads after its count has returned.
-// With every shared location accessed by such atomics, no cache write-back or invalidate
-// is needed (those order plain loads and stores).
+// Ordering: the logits are stored with agent-scope atomic stores, the workgroup barrier
+// puts every wave's stores before thread 0's count, and the count is an agent-scope
+// acquire-release read-modify-write: the releases of all workgroups of the token block
+// happen before the last arriver's acquire, which the barrier after it extends to all of
+// its waves; they then read the logits with agent-scope atomic loads.
 // ---------------------------------------------------------------------------------
 constexpr int kRouteSelTB = 4, kRouteSelEB = 2;
 constexpr int kRouteSelMaxH = 8 * 64 * 4;   // 16-byte chunks x lanes x chunks per lane
@@ -203,7 +203,7 @@ __device__ bool route_sel_part(const uint16_t* __restrict__ x, const uint16_t* _
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(counters + tb * kRouteCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counters + tb * kRouteCounterStride, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     sh.last = old == (uint32_t)(nWB - 1);
   }
   __syncthreads();
