@@ -33,10 +33,11 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4a16_mixture_experts_amd", "csrc")
 
 # Sources each profiled kernel is compiled from.
+_DECODE_SOURCES = ["moe_decode.hip", "device.h", "common.h", "group_block.h", "topk.h"]
 KERNEL_SOURCES = {
-    "decode_expert_kernel": ["moe_decode.hip", "device.h", "common.h"],
-    "decode_fused_kernel": ["moe_decode.hip", "device.h", "common.h"],
-    "decode_narrow_kernel": ["moe_decode.hip", "device.h", "common.h"],
+    "decode_expert_kernel": _DECODE_SOURCES,
+    "decode_fused_kernel": _DECODE_SOURCES,
+    "decode_narrow_kernel": _DECODE_SOURCES,
     "prefill_kernel": ["moe_prefill.hip", "device.h", "common.h"],
 }
 

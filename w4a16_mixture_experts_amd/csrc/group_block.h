@@ -103,8 +103,9 @@ __device__ __forceinline__ void group_block(const int32_t* ids, int n, int E, in
   }
   __syncthreads();
   // 3. stable scatter, chunk by chunk: the per-wave counts of the chunk become, per
-  // expert, exclusive prefixes over the waves (one thread per expert), which place each
-  // wave's rows after those of the earlier waves and chunks
+  // expert, exclusive prefixes over the waves (a 16-lane row per expert with 16 waves, else
+  // one thread per expert), which place each wave's rows after those of the earlier waves
+  // and chunks
 #pragma unroll
   for (int c = 0; c < kChunks; c++) {
     if (c * kThreads >= n) break;   // uniform
@@ -113,15 +114,35 @@ __device__ __forceinline__ void group_block(const int32_t* ids, int n, int E, in
     const int e = idr[c];
     if (nlead[c]) gs.wave[wave][e] = nlead[c];
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += kThreads) {
-      int run = gs.base[e2];
-#pragma unroll
-      for (int w = 0; w < kWaves; w++) {
-        const int v = gs.wave[w][e2];
-        gs.wave[w][e2] = run;
-        run += v;
+    if constexpr (kWaves == 16) {
+      // 16 lanes per expert (lane w of the row: wave w), an inclusive scan along the row by
+      // DPP row shifts (lanes without a source add 0), then base + exclusive prefix; the
+      // row's last lane moves the base on (its lanes read the base before, in program order)
+      for (int e0 = 0; e0 < E; e0 += kThreads / 16) {
+        const int e2 = e0 + (tid >> 4), w = tid & 15;
+        const int v = e2 < E ? gs.wave[w][e2] : 0;
+        int incl = v;
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);   // row_shr:1
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);   // row_shr:2
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);   // row_shr:4
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);   // row_shr:8
+        if (e2 < E) {
+          const int b = gs.base[e2];
+          gs.wave[w][e2] = b + incl - v;
+          if (w == 15) gs.base[e2] = b + incl;
+        }
       }
-      gs.base[e2] = run;
+    } else {
+      for (int e2 = tid; e2 < E; e2 += kThreads) {
+        int run = gs.base[e2];
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) {
+          const int v = gs.wave[w][e2];
+          gs.wave[w][e2] = run;
+          run += v;
+        }
+        gs.base[e2] = run;
+      }
     }
     __syncthreads();
     const int f = c * kThreads + tid;
