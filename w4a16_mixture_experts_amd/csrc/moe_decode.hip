@@ -311,6 +311,35 @@ __device__ void dec_publish(const MoeArgs& a, DecLDS& L, const DecPublish& pub) 
   group_block<NT>(ids_l, TK, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, gs);
 }
 
+// The publisher's work done by a workgroup that also runs an expert slice (logit routing,
+// E <= 64): wave t ranks token t from the logits it loaded first (lane e: expert e) through
+// an LDS row of its own, writes ids and weights, and the workgroup groups the ids. Called
+// once the slice's weight loads are in flight, so that it runs while they land.
+template <int NT>
+struct DecPubLDS {
+  uint16_t lg[kDecTok][64];
+  int32_t ids[kDecTok * 64];
+  GroupSharedT<NT> gs;
+};
+template <int NW, int NT>
+__device__ void dec_publish_lgt(const MoeArgs& a, const DecLgt<NW>& lgt, int wave, int lane, const DecPublish& pub,
+                                DecPubLDS<NT>& P) {
+  static_assert(NW * 64 == NT && (kDecTok + NW - 1) / NW == 1, "one token per wave");
+  if (wave < a.T) {
+    if (lane < a.E) P.lg[wave][lane] = lgt.lg[0];
+    int id;
+    float wt;
+    topk_rank_token(P.lg[wave], a.E, a.k, pub.renormalize, id, wt);
+    if (lane < a.k) {
+      P.ids[wave * a.k + lane] = id;
+      pub.ids[wave * a.k + lane] = id;
+      pub.w[wave * a.k + lane] = wt;
+    }
+  }
+  __syncthreads();
+  group_block<NT>(P.ids, a.T * a.k, a.E, pub.offsets, pub.sorted_flat, pub.flat_to_sorted, P.gs);
+}
+
 // pp (pass-parallel, not ALL): aidx counts 16-row passes over the active experts in
 // ascending order instead of the experts themselves, so that a hot expert's passes run in
 // workgroups of their own; ex.row0 / ex.cnt are then this pass's rows.
@@ -1076,7 +1105,11 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
   // slices 4j .. 4j + 3 of an expert read the same down tiles (a word each). The logical
   // order is therefore transposed so that each XCD takes a contiguous run of workgroups:
   // the slices of one expert share that XCD's L2.
-  const int nwk = gridDim.x - (is_sel(SRC) ? 1 : 0);
+  // With logit routing the grid's last workgroup is also the publisher (after its slice's
+  // weight loads); otherwise a workgroup of its own follows the slices.
+  constexpr bool kPubFold = SRC == kSrcLgt;
+  const bool pub_wg = kPubFold && blockIdx.x == gridDim.x - 1;
+  const int nwk = gridDim.x - (is_sel(SRC) && !kPubFold ? 1 : 0);
   int b = blockIdx.x;
   if (b < nwk && (nwk & 7) == 0) b = (b & 7) * (nwk >> 3) + (b >> 3);
   const int aidx = b / nslice, cs = b % nslice;
@@ -1096,11 +1129,12 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
   constexpr bool kLgt = SRC == kSrcLgt;
   __shared__ __attribute__((aligned(16))) uint8_t s_tab[64 * kDecTok];   // logit routing: table rows
   __shared__ __attribute__((aligned(16))) uint32_t s_keys[kLgt ? NW * 64 : 4];   // logit routing: keys
+  __shared__ DecPubLDS<kPubFold ? NT : 64> s_pub;                               // the folded publisher
   DecPre pre;
   DecLgt<NW> lgt;
   if (kLgt) lgt = dec_lgt_load<NW>(a, pub, wave, lane);
   else pre = dec_preload<SRC, NT>(a, pub);
-  if (is_sel(SRC) && blockIdx.x == gridDim.x - 1) {
+  if (is_sel(SRC) && !kPubFold && blockIdx.x == gridDim.x - 1) {
     dec_publish<SRC, NT>(a, L, pub);
     return;
   }
@@ -1111,9 +1145,12 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     // the table rows (lane e: row e), then the workgroup's expert by ballots
     const DecSelRow srow{dec_lgt_rows<NW>(a, lgt, wave, lane, s_keys, s_tab), lgt.slot};
     int slot = 0;
-    if (!dec_sel_pick(a, srow, aidx, lane, ex, slot, stok)) return;
-    if (slot < 0) {
-      if (tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
+    const bool has = dec_sel_pick(a, srow, aidx, lane, ex, slot, stok);
+    if (!has || slot < 0) {
+      if (has && tid == 0 && !a.skip_absent) atomicOr(a.debug, 1u);   // routed expert without a slot
+      if constexpr (kPubFold) {
+        if (pub_wg) dec_publish_lgt<NW, NT>(a, lgt, wave, lane, pub, s_pub);
+      }
       return;
     }
     ex.tiles = reinterpret_cast<const uint4*>(a.base + a.stride * (size_t)slot);
@@ -1155,6 +1192,9 @@ __global__ __launch_bounds__(1024) void decode_narrow_kernel(MoeArgs a, DecPubli
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x4F78);
     if (wave == 0 && stok.pos >= 0) L.srows[stok.pos] = stok.flat;
+    if constexpr (kPubFold) {
+      if (pub_wg) dec_publish_lgt<NW, NT>(a, lgt, wave, lane, pub, s_pub);   // while the weights land
+    }
   }
 
   // the expert's rows (at most T <= kDecTok: one pass)
@@ -1461,7 +1501,9 @@ static void launch_fused(ProfScope& prof, const MoeArgs& as, const DecPublish& P
   const int extra = is_sel(SRC) ? 1 : 0;           // the publisher workgroup
   const dim3 grid((pp ? units : all ? as.E : ny) * as.nparts + extra);
   if (nw == kNarRows / kTileRows) {
-    EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * as.nparts + extra), dim3(1024), 0, s, as, P);
+    // with logit routing the last slice's workgroup also publishes
+    EXMOE_LAUNCH(prof, decode_narrow_kernel<SRC>, dim3(ny * as.nparts + (SRC == kSrcLgt ? 0 : extra)), dim3(1024), 0, s,
+                 as, P);
     return;
   }
   {
