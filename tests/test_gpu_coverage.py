@@ -378,6 +378,46 @@ def test_table_routed_layer_equals_separate_calls(exm, olmoe_packed, T):
     assert np.array_equal(bf16_dev_to_bits(again.y), bf16_dev_to_bits(y_sep)), "second call on the same workspace differs"
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_narrow_publisher_outputs_with_slot_table(exm, olmoe_packed, T):
+    """A few tokens on the OLMoE shape (the narrow kernel, whose last slice workgroup also
+    publishes ids, weights and the grouping): through a permuting expert->slot table the
+    output equals the resident bank's bit for bit; with every expert unmapped (slot -1,
+    so every workgroup returns before its weights, the publisher included) the call is
+    flagged and the published routing and grouping still equal the oracle's."""
+    import torch
+    lay = olmoe_packed
+    s = lay.shape
+    x_bits = lay.syn.x(T, stream=500 + T)
+    x = to_dev_bf16(x_bits)
+    base = exm.moe_layer(x, lay.wr, lay.bank, s.I, s.k)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x_bits, lay.wr_bits)
+    ids = oracle.topk_ids(logits, s.k)
+    w = oracle.topk_weights(logits, ids)
+    off, sf, fs = oracle.group_tokens(ids, s.E)
+    perm = np.random.default_rng(5).permutation(s.E).astype(np.int32)   # expert e in slot perm[e]
+    blobs = [None] * s.E
+    for e in range(s.E):
+        blobs[perm[e]] = lay.blobs[e]
+    bank = exm.bank_from_blobs(blobs)
+    bank.expert_to_slot = torch.from_numpy(perm).cuda()
+    out = exm.moe_layer(x, lay.wr, bank, s.I, s.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(out.y), bf16_dev_to_bits(base.y))
+    assert exm.workspace_flags(out.workspace) == 0
+    bank.expert_to_slot = torch.full((s.E,), -1, dtype=torch.int32, device="cuda")
+    gone = exm.moe_layer(x, lay.wr, bank, s.I, s.k)
+    torch.cuda.synchronize()
+    assert exm.workspace_flags(gone.workspace) & exm.FLAG_EXPERT_WITHOUT_SLOT
+    for got in (out, gone):
+        assert np.array_equal(got.ids.cpu().numpy(), ids)
+        np.testing.assert_allclose(got.weights.cpu().numpy(), w, rtol=0, atol=1e-6)
+        assert np.array_equal(got.offsets.cpu().numpy(), off)
+        assert np.array_equal(got.sorted_flat.cpu().numpy()[:T * s.k], sf)
+        assert np.array_equal(got.flat_to_sorted.cpu().numpy()[:T * s.k], fs)
+
+
 @pytest.mark.parametrize("shape,T", [("olmoe", 100), ("olmoe", 300), ("wide", 100), ("wide", 200)])
 def test_prefill_layer_seeds_equal_separate_calls(exm, olmoe_packed, shape, T):
     """At prefill sizes the whole-layer call takes the grouped GEMM's correction seeds from
