@@ -200,21 +200,53 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
   // (the gathered row indices are loaded at clamped positions, all at once, and the rows
   // past the segment are then pointed at the zero row)
   constexpr int kDmaPerWave = BN / 4 / NW;
-  const uint16_t* drow[kDmaPerWave];
+  // Every index load of the set-up is issued at once, then the first group's weights
+  // behind them, so that waiting for the indices leaves the weight loads in flight:
+  //   gate/up: the gathered rows of the wave's copies and the token of the lane's seed row;
+  //   down: the flat (token, slot) index of each of the tile's rows (for the epilogue).
+  // (the clamped positions are hidden from the optimizer: where it can prove a position
+  // unclamped it issues a second load there, late and waited for on its own)
+  auto row_index = [&](int r) {
+    int rr = r < pt.cnt ? r : pt.cnt - 1;
+    asm volatile("" : "+v"(rr));
+    return a.sorted_flat[pt.seg0 + rr];
+  };
   int grow[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; i++) {
-    const int r = (wave * kDmaPerWave + i) * 4 + (lane >> 4);
-    const int rr = pt.tok0 + r < pt.cnt ? pt.tok0 + r : pt.cnt - 1;
-    grow[i] = GATEUP ? a.sorted_flat[pt.seg0 + rr] : 0;
+  for (int i = 0; i < kDmaPerWave; i++)
+    grow[i] = GATEUP ? row_index(pt.tok0 + (wave * kDmaPerWave + i) * 4 + (lane >> 4)) : 0;
+  const int seed_r = pt.tok0 + (wave % kSeedWaves) * 64 + lane;
+  int srow = 0;
+  if (GATEUP && Q4) srow = row_index(seed_r);
+  int fr_l = 0;
+  if (!GATEUP && wave < BN / 64) fr_l = row_index(pt.tok0 + tid);
+
+  uint4 wcur[NA][NL], wnext[NA][NL];
+  uint32_t scur[NA], snext[NA];
+#pragma unroll
+  for (int ai = 0; ai < NA; ai++) {
+    const size_t t = tbase[ai];
+#pragma unroll
+    for (int q = 0; q < NL; q++) wcur[ai][q] = tiles[(t * NL + q) * 64 + lane];
+    if (Q4) scur[ai] = scales[t * 16 + (lane & 15)];
   }
+
+  // flat (token, slot) index -> token: a high multiply by floor((2^32 - 1) / k) gives the
+  // quotient or one less (for any 32-bit index), and one compare corrects it
+  const uint32_t kmul = 0xFFFFFFFFu / (uint32_t)a.k;
+  auto tok_of = [&](int flat) {
+    uint32_t q = __umulhi((uint32_t)flat, kmul);
+    if ((uint32_t)flat - q * (uint32_t)a.k >= (uint32_t)a.k) q++;
+    return (int)q;
+  };
+  const uint16_t* drow[kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; i++) {
     const int r = (wave * kDmaPerWave + i) * 4 + (lane >> 4);
     const uint16_t* src = g_zero_row_pf;
     if (pt.tok0 + r < pt.cnt) {
       if (GATEUP)
-        src = a.x + (size_t)(grow[i] / a.k) * a.H;
+        src = a.x + (size_t)tok_of(grow[i]) * a.H;
       else
         src = a.h + (size_t)(pt.seg0 + pt.tok0 + r) * a.I;
     }
@@ -226,8 +258,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
   const float* seed_src;
   size_t seed_stride;
   if (GATEUP) {
-    const int r = pt.tok0 + (wave % kSeedWaves) * 64 + lane;
-    seed_src = a.xsum + (r < pt.cnt ? a.sorted_flat[pt.seg0 + r] / a.k : 0);
+    seed_src = a.xsum + (seed_r < pt.cnt ? tok_of(srow) : 0);
     seed_stride = (size_t)a.T;
   } else {
     seed_src = a.gsum + pt.seg0 + pt.tok0 + (wave % kSeedWaves) * 64 + lane;
@@ -246,18 +277,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
 #pragma unroll
     for (int bj = 0; bj < NB; bj++) acc[ai][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wcur[NA][NL], wnext[NA][NL];
-  uint32_t scur[NA], snext[NA];
-#pragma unroll
-  for (int ai = 0; ai < NA; ai++) {
-    const size_t t = tbase[ai];
-#pragma unroll
-    for (int q = 0; q < NL; q++) wcur[ai][q] = tiles[(t * NL + q) * 64 + lane];
-    if (Q4) scur[ai] = scales[t * 16 + (lane & 15)];
-  }
   EXMOE_STAGE(0, s_act0, s_seed0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // down: the tile's flat row indices and routing weights for the epilogue go to LDS (the
+  // gate/up kernel's group-sum rows); the weights' loads run behind the first group
+  int* const s_fr = reinterpret_cast<int*>(s_gsum[0]);
+  float* const s_wr = s_gsum[1];
+  float wr_l = 0.f;
+  if (!GATEUP && wave < BN / 64) {
+    s_fr[tid] = fr_l;
+    wr_l = a.w[fr_l];
+  }
 
   // Token subtile pairs (32 tokens) that hold rows of the segment: the last token tile of
   // an expert is often mostly padding, and its MFMAs on padding rows are skipped.
@@ -430,25 +461,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
     }
     }
   } else {
-    // y_perm rows are in flat (token, slot) order: every row index and routing weight of the
-    // lane's 32 tokens is loaded first (rows past the segment read row 0, unused) and waited
-    // for once, instead of one round trip per row between stores (which also count in vmcnt)
-    int fr[NB][4];
-    float wr[NB][4];
+    // y_perm rows are in flat (token, slot) order; the row indices and routing weights of
+    // the tile's rows were loaded during the set-up (rows past the segment hold the last
+    // row's, unused)
+    if (wave < BN / 64) s_wr[tid] = wr_l;
+    __syncthreads();
 #pragma unroll
-    for (int bj = 0; bj < NB; bj++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = pt.tok0 + bj * 16 + tl0 + i;
-        fr[bj][i] = a.sorted_flat[pt.seg0 + (r < pt.cnt ? r : 0)];
-      }
-#pragma unroll
-    for (int bj = 0; bj < NB; bj++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) wr[bj][i] = a.w[fr[bj][i]];
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int bj = 0; bj < NB; bj++)
+    for (int bj = 0; bj < NB; bj++) {
+      const int4 fr4 = *reinterpret_cast<const int4*>(&s_fr[bj * 16 + tl0]);
+      const f32x4 wr4 = *reinterpret_cast<const f32x4*>(&s_wr[bj * 16 + tl0]);
+      const int fr[4] = {fr4.x, fr4.y, fr4.z, fr4.w};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = pt.tok0 + bj * 16 + tl0 + i;
@@ -457,10 +479,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(MoeArgs a, int
           for (int ai = 0; ai < NA; ai++) {
             if (!rvalid[ai]) continue;
             const int col = (rt * 16 + NA * wave + ai) * 16 + (lane & 15);
-            a.y_perm[(size_t)fr[bj][i] * a.H + col] = acc[ai][bj][i] * wr[bj][i];
+            a.y_perm[(size_t)fr[i] * a.H + col] = acc[ai][bj][i] * wr4[i];
           }
         }
       }
+    }
     // exactness counter: the first row tile of each token tile counts the tile's rows
     if (a.rows_ctr && rt == 0 && tid == 0) atomicAdd(a.rows_ctr + pt.e, min(BN, pt.cnt - pt.tok0));
   }
