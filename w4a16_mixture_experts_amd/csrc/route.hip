@@ -25,6 +25,57 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------
+// Logits of a few tokens, one logit per workgroup, with H split over its KW waves: one
+// 16-byte chunk of the token row and of the router row per lane (H <= 512 KW), both
+// loaded before any arithmetic; the chunk's 8 products are added in fp64 in element
+// order, then the lanes of each 16-lane row (DPP rotations), the 4 rows of the wave (fixed
+// order) and the KW waves (wave order, through LDS); one thread rounds once to bf16.
+// ---------------------------------------------------------------------------------
+template <int KW>
+__global__ __launch_bounds__(64 * KW) void route_logits_split_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ wr,
+                                                                     const float* __restrict__ bias, int T, int H,
+                                                                     int E, uint16_t* __restrict__ logits) {
+  __shared__ double red[KW];
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int t = (int)blockIdx.x / E, e = (int)blockIdx.x % E;
+  const int chunks = H / 8;
+  const int c = wave * 64 + lane;
+  const bool on = c < chunks;
+  const int cc = on ? c : chunks - 1;   // clamped: no load under a per-lane branch
+  uint4 xu = reinterpret_cast<const uint4*>(x + (size_t)t * H)[cc];
+  uint4 wu = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[cc];
+  // chunks past H become zeros (0 * 0 added to +0.0 leaves the sum's bits unchanged)
+  xu = on ? xu : make_uint4(0u, 0u, 0u, 0u);
+  wu = on ? wu : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t xq[4] = {xu.x, xu.y, xu.z, xu.w}, wq[4] = {wu.x, wu.y, wu.z, wu.w};
+  double a = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    a = fma((double)__uint_as_float(xq[q] << 16), (double)__uint_as_float(wq[q] << 16), a);
+    a = fma((double)__uint_as_float(xq[q] & 0xFFFF0000u), (double)__uint_as_float(wq[q] & 0xFFFF0000u), a);
+  }
+  double sv = row16_sum_f64(a);
+  const long long b = __double_as_longlong(sv);
+  const int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+  double r[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    r[q] = __longlong_as_double(((long long)(unsigned)__builtin_amdgcn_readlane(lo, 16 * q)) |
+                                ((long long)__builtin_amdgcn_readlane(hi, 16 * q) << 32));
+  sv = ((r[0] + r[1]) + r[2]) + r[3];
+  if (lane == 0) red[wave] = sv;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double v = red[0];
+#pragma unroll
+    for (int w = 1; w < KW; w++) v += red[w];
+    logits[(size_t)t * E + e] = f64_to_bf16(bias ? v + (double)bias[e] : v);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Logits of many tokens on the fp64 matrix cores: a workgroup owns a tile of 16 tokens x
 // 16 experts, each of its KW waves a strided share of the 32-column chunks of H, and the
 // KW partial tiles are added in wave order through LDS. v_mfma_f64_16x16x4f64 takes A[m][k]
@@ -297,7 +348,17 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (T == 0) return hipSuccess;
   if (xsum && H > kLgtXsMaxH) return hipErrorInvalidValue;   // the seed sums' LDS rows
   ProfScope prof("route_logits", s);
-  if (T <= 128) {
+  if (T <= 16 && !xsum && H <= 4096) {
+    // one logit per workgroup, H split over its waves (16 tokens and 64 experts: layer
+    // 44.2 -> 43.5 us; one token 23.7 -> 22.7 us; against a wave per 2 tokens x 2 experts)
+    const int kw = (H + 511) / 512;
+    if (kw <= 2)
+      EXMOE_LAUNCH(prof, route_logits_split_kernel<2>, dim3(T * E), dim3(128), 0, s, x, wr, bias, T, H, E, logits);
+    else if (kw <= 4)
+      EXMOE_LAUNCH(prof, route_logits_split_kernel<4>, dim3(T * E), dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+    else
+      EXMOE_LAUNCH(prof, route_logits_split_kernel<8>, dim3(T * E), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
+  } else if (T <= 128) {
     // one wave per 2 tokens x 2 experts, the whole wave on H: a row in one round trip
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
     const bool one = H <= kRouteSelMaxH;
