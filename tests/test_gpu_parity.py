@@ -213,10 +213,13 @@ def test_expert_without_slot_is_flagged(exm, tiny, path):
     assert exm.workspace_flags(out.workspace) == 0          # cleared by the previous read
 
 
-@pytest.mark.parametrize("T,k,E", [(4096, 1, 8), (4097, 1, 64), (2049, 8, 64), (300, 64, 256), (5000, 2, 3)])
+@pytest.mark.parametrize("T,k,E", [(4096, 1, 8), (4097, 1, 64), (2049, 8, 64), (300, 64, 256), (5000, 2, 3),
+                                   (8192, 8, 256), (9000, 8, 64)])
 def test_grouping_many_rows_chunked(exm, T, k, E):
-    """The grouping of more than 4096 routed rows (chunk counts, one scan, chunk scatters)
-    against the oracle, bit for bit, including a ragged last chunk and empty experts."""
+    """The grouping of more than 4096 routed rows (chunk counts of 1024 rows, then up to 64
+    chunks scatters that scan the counts themselves, beyond that one scan launch and the
+    scatters) against the oracle, bit for bit, including a ragged last chunk, empty
+    experts, exactly 64 chunks (8192 x 8) and 71 chunks (9000 x 8)."""
     import torch
     rng = np.random.default_rng(T + E)
     if E >= k:
