@@ -172,6 +172,92 @@ __global__ __launch_bounds__(64 * KW) void route_logits_mfma_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------------
+// The same split for 2 tokens x 2 experts per workgroup (prefill sizes up to 128 tokens).
+// XS: the workgroups also write the grouped GEMM's correction seeds of their two tokens:
+// row r of wave w holds the 16 chunks of group 4 w + r, which the workgroups of expert
+// block g mod the block count sum (chunk8_sum, then row16_tree_sum over the row).
+// ---------------------------------------------------------------------------------
+template <int KW, bool XS>
+__global__ __launch_bounds__(64 * KW) void route_logits_split2_kernel(const uint16_t* __restrict__ x,
+                                                                      const uint16_t* __restrict__ wr,
+                                                                      const float* __restrict__ bias, int T, int H,
+                                                                      int E, uint16_t* __restrict__ logits,
+                                                                      float* __restrict__ xsum) {
+  __shared__ double red[KW][4];
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nEB = (E + 1) / 2;
+  const int eb = (int)blockIdx.x % nEB;
+  const int t0 = ((int)blockIdx.x / nEB) * 2, e0 = eb * 2;
+  const int chunks = H / 8;
+  const int c = wave * 64 + lane;
+  const bool on = c < chunks;
+  const int cc = on ? c : chunks - 1;   // clamped: no load under a per-lane branch
+  uint4 xu[2], wu[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int t = t0 + i < T ? t0 + i : T - 1;
+    xu[i] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[cc];
+    const int e = e0 + i < E ? e0 + i : E - 1;
+    wu[i] = reinterpret_cast<const uint4*>(wr + (size_t)e * H)[cc];
+  }
+  // chunks past H become zeros (0 * 0 added to +0.0 leaves the sum's bits unchanged)
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    xu[i] = on ? xu[i] : make_uint4(0u, 0u, 0u, 0u);
+    wu[i] = on ? wu[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (XS) {
+    const int g = c / 16;
+    const bool mine = g % nEB == eb && (lane & 15) == 0 && on;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const float v = row16_tree_sum(chunk8_sum(xu[i]));
+      if (mine && t0 + i < T) xsum[(size_t)g * T + t0 + i] = -136.0f * v;
+    }
+  }
+  double xv[2][8], wv[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const uint32_t xq[4] = {xu[i].x, xu[i].y, xu[i].z, xu[i].w}, wq[4] = {wu[i].x, wu[i].y, wu[i].z, wu[i].w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      xv[i][2 * q] = (double)__uint_as_float(xq[q] << 16);
+      xv[i][2 * q + 1] = (double)__uint_as_float(xq[q] & 0xFFFF0000u);
+      wv[i][2 * q] = (double)__uint_as_float(wq[q] << 16);
+      wv[i][2 * q + 1] = (double)__uint_as_float(wq[q] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      double a = 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; q++) a = fma(xv[i][q], wv[j][q], a);
+      double sv = row16_sum_f64(a);
+      const long long b = __double_as_longlong(sv);
+      const int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+      double r[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        r[q] = __longlong_as_double(((long long)(unsigned)__builtin_amdgcn_readlane(lo, 16 * q)) |
+                                    ((long long)__builtin_amdgcn_readlane(hi, 16 * q) << 32));
+      sv = ((r[0] + r[1]) + r[2]) + r[3];
+      if (lane == 0) red[wave][2 * i + j] = sv;
+    }
+  __syncthreads();
+  const int q = (int)threadIdx.x;
+  if (q < 4) {
+    const int t = t0 + q / 2, e = e0 + q % 2;
+    double v = red[0][q];
+#pragma unroll
+    for (int w = 1; w < KW; w++) v += red[w][q];
+    if (t < T && e < E) logits[(size_t)t * E + e] = f64_to_bf16(bias ? v + (double)bias[e] : v);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Logits, top-k and the expert table of a few tokens (T <= 16) in one launch: the
 // selection part (route_wave.h) with one wave per token of a 4-token block and one block
 // of 2 experts per workgroup.
@@ -358,6 +444,23 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
       EXMOE_LAUNCH(prof, route_logits_split_kernel<4>, dim3(T * E), dim3(256), 0, s, x, wr, bias, T, H, E, logits);
     else
       EXMOE_LAUNCH(prof, route_logits_split_kernel<8>, dim3(T * E), dim3(512), 0, s, x, wr, bias, T, H, E, logits);
+  } else if (T <= 128 && H <= 4096) {
+    // 2 tokens x 2 experts per workgroup, H split over its waves
+    const int kw = (H + 511) / 512;
+    const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
+#define EXMOE_SPLIT2(KW_)                                                                                        \
+  do {                                                                                                           \
+    if (xsum)                                                                                                    \
+      EXMOE_LAUNCH(prof, (route_logits_split2_kernel<KW_, true>), dim3(blocks), dim3(64 * KW_), 0, s, x, wr, bias, \
+                   T, H, E, logits, xsum);                                                                       \
+    else                                                                                                         \
+      EXMOE_LAUNCH(prof, (route_logits_split2_kernel<KW_, false>), dim3(blocks), dim3(64 * KW_), 0, s, x, wr,      \
+                   bias, T, H, E, logits, nullptr);                                                              \
+  } while (0)
+    if (kw <= 2) EXMOE_SPLIT2(2);
+    else if (kw <= 4) EXMOE_SPLIT2(4);
+    else EXMOE_SPLIT2(8);
+#undef EXMOE_SPLIT2
   } else if (T <= 128) {
     // one wave per 2 tokens x 2 experts, the whole wave on H: a row in one round trip
     const int blocks = ((T + 1) / 2) * ((E + 1) / 2);
