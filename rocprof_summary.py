@@ -116,7 +116,8 @@ def _ours(name: str) -> bool:
                                   "route_logits_mfma_kernel",
                                   "decode_narrow_kernel", "bf16_decode_kernel", "group_count_kernel",
                                   "group_scan_kernel", "group_scatter_kernel", "table_fill_kernel", "span_fill_kernel",
-                                  "wave_union_kernel")
+                                  "wave_union_kernel", "route_logits_split_kernel", "route_logits_split2_kernel",
+                                  "group_scan_scatter_kernel")
 
 
 def _match(values: dict[str, list[float]], kernel: str) -> list[float]:
