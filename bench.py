@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--tokens", type=int, default=16, help="tokens per decode call (1, 4 or 16)")
+    ap.add_argument("--tokens", type=int, default=16, choices=[1, 4, 16], help="tokens per decode call")
     ap.add_argument("--rotate", type=int, default=8, help="expert-bank copies rotated across calls")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
