@@ -446,7 +446,7 @@ def main():
     if args.only in (None, "decode"):
         head = run_decode(args.tokens, args.steps, args.warmup, True)
         result["head"] = head
-        if not args.no_secondary and args.only is None:
+        if not args.no_secondary:
             secondary["olmoe_decode_T16_fused_vs_sequential"] = run_sequential(16, 64, 8)
         if not args.no_secondary:
             for T in (1, 4, 16):

@@ -269,6 +269,22 @@ def test_debug_counters_olmoe_paths(exm, olmoe_packed, T, bias):
     assert np.array_equal(rows, np.diff(off))
 
 
+@pytest.mark.parametrize("T,bias", [(16, False), (128, True)])
+def test_debug_counters_olmoe_sequential(exm, olmoe_packed, T, bias):
+    """The sequential path on the OLMoE shape: experts with up to 16 rows run through the
+    launch pair whose reductions are split over workgroups, hotter experts (Zipf skew at
+    128 tokens) through the decode kernel pair; every routed row is counted once."""
+    x = olmoe_packed.syn.x(T, stream=950 + T)
+    b = olmoe_packed.syn.zipf_bias() if bias else None
+    rows, off = _forward_counted(exm, olmoe_packed, x, 3, bias=b)
+    ids = oracle.topk_ids(oracle.router_logits(x, olmoe_packed.wr_bits, b), olmoe_packed.shape.k)
+    counts = np.bincount(ids.reshape(-1), minlength=olmoe_packed.shape.E)
+    if bias:
+        assert counts.max() > 16 and 0 < counts[counts > 0].min() <= 16   # both launch pairs ran
+    assert np.array_equal(rows, counts)
+    assert np.array_equal(rows, np.diff(off))
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_debug_counters_cached_waves_and_missing_expert(exm, path):
     """A cached forward in several waves counts every routed row once; leaving a routed

@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 
-SOURCES = ["api.cpp", "slot_cache.cpp", "profile.cpp", "route.hip", "group.hip", "moe_decode.hip", "moe_prefill.hip", "moe_bf16.hip", "util.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "slot_cache.cpp", "profile.cpp", "route.hip", "group.hip", "moe_decode.hip", "moe_prefill.hip", "moe_bf16.hip", "moe_seq.hip", "util.hip", "noalloc.hip"]
 # Per-file flags. The grouped GEMM keeps MFMA results in VGPRs: they are scaled by VALU
 # FMAs right away, and AGPR results would cost one v_accvgpr_read per element.
 FILE_FLAGS = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -491,13 +491,17 @@ static int moe_forward_impl(const exmoe_bf16* x, const int32_t* topk_ids, const 
   } else {
     // Sequential W4 reference: experts one after another in ascending id, each with its
     // own launches over its gathered rows; one host read of the offsets drives the loop.
+    // Up to 16 rows, an expert runs on a launch pair built for a short latency chain;
+    // more rows go through the decode kernel pair, which walks them in passes of 16 inside
+    // one launch pair.
     int32_t off[kMaxExperts + 1];
     EXMOE_HIP(hipMemcpyAsync(off, expert_offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, stream));
     EXMOE_HIP(hipStreamSynchronize(stream));
     for (int e = 0; e < E; e++) {
       const int cnt = off[e + 1] - off[e];
       if (cnt <= 0) continue;
-      EXMOE_HIP(launch_moe_expert_range(a, e, cnt, stream));
+      if (cnt <= kSeqMaxRows) EXMOE_HIP(launch_seq_expert(a, e, off[e], cnt, stream));
+      else EXMOE_HIP(launch_moe_expert_range(a, e, cnt, stream));
     }
     EXMOE_HIP(launch_combine(a, stream));
   }
