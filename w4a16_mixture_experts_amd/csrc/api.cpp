@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "common.h"
+#include "moe_seq.h"
 #include "exmoe.h"
 
 namespace exmoe {

@@ -197,10 +197,6 @@ hipError_t launch_bf16_decode_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_bf16_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefill_experts(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_expert_range(const MoeArgs& a, int expert, int rows, hipStream_t s);  // sequential path
-// Sequential path, an expert with at most kSeqMaxRows rows: a gate/up and a down launch
-// with many waves on each row block and a short latency chain.
-constexpr int kSeqMaxRows = 16;
-hipError_t launch_seq_expert(const MoeArgs& a, int e, int seg0, int cnt, hipStream_t s);
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);
 
 }  // namespace exmoe

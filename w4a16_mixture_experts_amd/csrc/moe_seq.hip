@@ -14,6 +14,7 @@
 // (gate/up), or the routing weight times the row into y_perm (down). At most 16 rows per
 // launch (one MFMA column block).
 #include "device.h"
+#include "moe_seq.h"
 
 namespace exmoe {
 
