@@ -483,3 +483,56 @@ def test_slotless_expert_leaves_workspace_clean(exm, olmoe_packed):
     torch.cuda.synchronize()
     assert np.array_equal(bf16_dev_to_bits(b.y), bf16_dev_to_bits(ref.y))
     assert exm.workspace_flags(b.workspace) == 0
+
+
+def test_sequential_path_row_counts_at_the_crossover(exm):
+    """The sequential path on constructed routing whose segments sit at the boundary between
+    its two launch pairs: an expert with exactly 16 rows (the last size the short-chain
+    pair takes), one with 17 (the decode kernel pair), one with a single row and one with
+    none, on a shape whose short-chain launches put several waves on every row block
+    (H = 1024: 8 input groups for gate/up; I = 512: 4 for down). The output against the
+    oracle's per-token layer with the same ids and weights, the exactness counters against
+    the segment sizes, and a repeated call bit for bit."""
+    import torch
+    shape = LayerShape(H=1024, I=512, E=8, k=4)
+    lay = Layer(shape, seed=41)
+    T, k, E = 20, shape.k, shape.E
+    ids_np = np.zeros((T, k), np.int64)
+    fill = [3, 4, 5, 6]
+    for t in range(T):
+        row = []
+        if t < 16:
+            row.append(0)
+        if t < 17:
+            row.append(1)
+        if t == 19:
+            row.append(2)
+        j = t
+        while len(row) < k:
+            e = fill[j % len(fill)]
+            if e not in row:
+                row.append(e)
+            j += 1
+        ids_np[t] = row
+    counts = np.bincount(ids_np.reshape(-1), minlength=E)
+    assert counts[0] == 16 and counts[1] == 17 and counts[2] == 1 and counts[7] == 0
+    rng = np.random.default_rng(7)
+    w_np = rng.random((T, k)).astype(np.float32) + 0.1
+    w_np /= w_np.sum(axis=1, keepdims=True)
+    x_bits = lay.syn.x(T, stream=77)
+    x = to_dev_bf16(x_bits)
+    ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+    w = torch.from_numpy(w_np).cuda()
+    off, sf, fs = exm.group_tokens(ids, E)
+    ws = exm.alloc_workspace(exm.moe_workspace_bytes(T, shape.H, shape.I, E, k, 3))
+    y = exm.moe_forward(x, ids, w, off, sf, fs, lay.bank, shape.I, flags=3 | exm.DEBUG_COUNTERS, workspace=ws)
+    torch.cuda.synchronize()
+    y_bits = bf16_dev_to_bits(y)
+    assert np.array_equal(exm.workspace_rows(ws, E), counts)
+    assert exm.workspace_flags(ws) == 0
+    xf = bf16_bits_to_f64(x_bits)
+    y_ref = oracle.forward_per_token(xf, ids_np, w_np.astype(np.float64), lay.experts)
+    check_y(bf16_dev_to_f64(y), y_ref, "sequential at the 16/17-row crossover")
+    again = exm.moe_forward(x, ids, w, off, sf, fs, lay.bank, shape.I, flags=3, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(again), y_bits)
